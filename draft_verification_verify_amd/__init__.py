@@ -1,0 +1,231 @@
+"""Python binding of libspecverify (batched draft verification on MI355X).
+
+Argument marshalling only: every step of verification runs in the HIP
+kernels of ``libspecverify.so`` (built from ``csrc/specverify.hip`` by
+``build.py``).  torch supplies device memory and the stream; tensors must be
+contiguous and on the current GPU.  If the shared library is missing this
+module raises at import time -- there is no fallback path.
+
+Calls mirror the C ABI in ``include/specverify.h``:
+
+    verify_greedy(target, tokens, depth=None)            -> (out_tokens, num_accepted)
+    verify_sample(target, draft, tokens, temperature,
+                  u_accept, u_sample, depth=None)        -> (out_tokens, num_accepted, p_draft, q_draft)
+    draft_confidence(draft, max_depth=None)              -> conf
+    dcut_allocate(conf, budget, max_depth=None)          -> depth
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED", 3: "SV_ERR_WORKSPACE",
+          4: "SV_ERR_BUDGET", 5: "SV_ERR_BAD_INPUT", 6: "SV_ERR_HIP"}
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python draft_verification_verify_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.spec_verify_abi_version.restype = i32
+    L.spec_verify_abi_version.argtypes = []
+    L.spec_verify_status_string.restype = ctypes.c_char_p
+    L.spec_verify_status_string.argtypes = [ctypes.c_int]
+    L.spec_verify_workspace_size.restype = sz
+    L.spec_verify_workspace_size.argtypes = [i32, i32, i32]
+    L.spec_verify_greedy.restype = ctypes.c_int
+    L.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.spec_verify_sample.restype = ctypes.c_int
+    L.spec_verify_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32,
+                                     vp, vp, vp, vp, vp, sz, vp]
+    L.spec_draft_confidence.restype = ctypes.c_int
+    L.spec_draft_confidence.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, sz, vp]
+    L.dcut_allocate.restype = ctypes.c_int
+    L.dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    if L.spec_verify_abi_version() != 1:
+        raise ImportError("libspecverify ABI version mismatch")
+    return L
+
+
+lib = _load()
+
+EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify_workspace_size",
+            "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate")
+
+
+def workspace_size(B: int, K: int, V: int) -> int:
+    return int(lib.spec_verify_workspace_size(B, K, V))
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _ = torch
+
+
+class Workspace:
+    """A zero-filled device buffer reused across calls on one device.
+
+    The library leaves its counters at zero after every call, so the buffer
+    is zeroed only when it is (re)allocated.  Calls that share a workspace
+    must be ordered on one stream."""
+
+    def __init__(self):
+        self._buf = {}
+        self._lock = threading.Lock()
+
+    def get(self, device, nbytes: int):
+        torch = _torch()
+        key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+        with self._lock:
+            buf = self._buf.get(key)
+            if buf is None or buf.numel() < nbytes:
+                buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=torch.device("cuda", key))
+                self._buf[key] = buf
+            return buf
+
+
+_default_ws = Workspace()
+
+
+def _ws(device, B, K, V, workspace):
+    n = workspace_size(B, K, V)
+    if n == 0:
+        raise SpecVerifyError("spec_verify_workspace_size", 2)
+    if workspace is None:
+        return _default_ws.get(device, n), n
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _raise(fn, st):
+    if st != 0:
+        raise SpecVerifyError(fn, st)
+
+
+def verify_greedy(target, tokens, depth=None, *, out_tokens=None, num_accepted=None,
+                  workspace=None, stream=None):
+    """Greedy (T=0) verification.  target [B,K+1,V] bf16/fp32, tokens [B,K] int32."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check(target, "target")
+    _check(tokens, "tokens", torch.int32, (B, K))
+    _check(depth, "depth", torch.int32, (B,))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=target.device)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
+    ws, nbytes = _ws(target.device, B, K, V, workspace)
+    st = lib.spec_verify_greedy(_ptr(target), _dtype_code(target), _ptr(tokens), _ptr(depth), B, K, V,
+                                _ptr(out_tokens), _ptr(num_accepted), _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_verify_greedy", st)
+    return out_tokens, num_accepted
+
+
+def verify_sample(target, draft, tokens, temperature, u_accept, u_sample, depth=None, *,
+                  out_tokens=None, num_accepted=None, p_draft=None, q_draft=None,
+                  want_probs: bool = True, workspace=None, stream=None):
+    """Rejection-sampling verification.  Returns (out_tokens, num_accepted, p_draft, q_draft)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check(target, "target")
+    _check(draft, "draft", target.dtype, (B, K, V))
+    _check(tokens, "tokens", torch.int32, (B, K))
+    _check(temperature, "temperature", torch.float32, (B,))
+    _check(u_accept, "u_accept", torch.float32, (B, K))
+    _check(u_sample, "u_sample", torch.float32, (B,))
+    _check(depth, "depth", torch.int32, (B,))
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if want_probs and p_draft is None:
+        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if want_probs and q_draft is None:
+        q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    ws, nbytes = _ws(dev, B, K, V, workspace)
+    st = lib.spec_verify_sample(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens), _ptr(depth),
+                                _ptr(temperature), _ptr(u_accept), _ptr(u_sample), B, K, V,
+                                _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft),
+                                _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_verify_sample", st)
+    return out_tokens, num_accepted, p_draft, q_draft
+
+
+def draft_confidence(draft, max_depth=None, *, conf=None, workspace=None, stream=None):
+    """conf[b,k] = max softmax(draft[b,k]) at T=1 (0 beyond max_depth[b])."""
+    torch = _torch()
+    B, K, V = draft.shape
+    _check(draft, "draft")
+    _check(max_depth, "max_depth", torch.int32, (B,))
+    if conf is None:
+        conf = torch.empty((B, K), dtype=torch.float32, device=draft.device)
+    ws, nbytes = _ws(draft.device, B, K, V, workspace)
+    st = lib.spec_draft_confidence(_ptr(draft), _dtype_code(draft), _ptr(max_depth), B, K, V, _ptr(conf),
+                                   _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_draft_confidence", st)
+    return conf
+
+
+def dcut_allocate(conf, budget: int, max_depth=None, *, depth_out=None, stream=None):
+    """D-cut depth allocation (global top-k of fp32 prefix confidence)."""
+    torch = _torch()
+    B, K = conf.shape
+    _check(conf, "conf", torch.float32)
+    _check(max_depth, "max_depth", torch.int32, (B,))
+    if depth_out is None:
+        depth_out = torch.empty((B,), dtype=torch.int32, device=conf.device)
+    st = lib.dcut_allocate(_ptr(conf), _ptr(max_depth), B, K, int(budget), _ptr(depth_out), _stream(stream))
+    _raise("dcut_allocate", st)
+    return depth_out

@@ -1,0 +1,170 @@
+/*
+ * specverify.h -- C ABI of libspecverify: batched verification of drafted
+ * tokens in speculative decoding, and D-cut verification-depth allocation,
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as printed):
+ *   [Stack]    aimodeling.com, "Tencent Hunyuan Turns Speculative Decoding
+ *              Into a Full Open-Source Stack"
+ *   [Remio]    remio.ai, "Tencent rilascia AngelSpec in open source, sfidando
+ *              lo speculative decoding universale"
+ *   [Hamidun]  news.hamidun.com, "Tencent открыл AngelSpec - фреймворк для
+ *              ускорения инференса LLM через speculative decoding"
+ *   [AIbase]   test-news.aibase.com news item 30001 (AngelSpec release)
+ *
+ * Problem statement these calls follow: B requests, each with K drafted
+ * tokens over a vocabulary of V; the target model has produced logits for
+ * every drafted position plus one more ([B, K+1, V]); the target verifies
+ * the whole block in one pass by rejection sampling and commits the
+ * accepted prefix plus a bonus token ([Stack], section "What problem does
+ * it solve"; [Hamidun], section "Qu'est-ce que le speculative decoding").
+ * The pages print no accept rule; the calls implement the standard
+ * speculative-sampling construction (Leviathan et al. 2023; Chen et al.
+ * 2023), the textbook method with the lossless property the pages state.
+ *
+ * Conventions shared by every call
+ *   Pointers.  Every array argument is a DEVICE pointer on the current HIP
+ *     device.  Logit arrays must be 16-byte aligned.  Layouts are contiguous
+ *     row-major with the vocabulary fastest: target row (b, k) starts at
+ *     element (b*(K+1) + k)*V, draft row (b, k) at (b*K + k)*V.
+ *   Ownership.  The caller owns every buffer, including the workspace; the
+ *     library allocates no device memory and keeps no state between calls.
+ *   Execution.  Calls are asynchronous and ordered on `stream`; a call that
+ *     returns SV_OK has only enqueued work.  Calls that share a workspace must
+ *     be ordered (the same stream, or synchronised): their kernels use the
+ *     workspace's counters.
+ *   Workspace.  spec_verify_workspace_size(B, K, V) bytes, 256-byte aligned,
+ *     ZERO-FILLED before its first use.  Every call leaves the counters it
+ *     uses at zero when its kernels finish, so a workspace is reusable
+ *     without clearing as long as every call on it ran to completion.
+ *   Errors.  Arguments the host can check (null pointers, sizes, dtype,
+ *     alignment, workspace size, budget) are rejected with a status before
+ *     anything is enqueued.  Bad DATA is found on the device and reported per
+ *     request as num_accepted[b] = -1 with out_tokens[b, :] = -1: a depth
+ *     outside [0, K], a temperature that is negative or NaN, a drafted token
+ *     outside [0, V), a uniform outside [0, 1), or a row that is read and
+ *     holds a NaN or +inf, or only -inf.  -inf logits (masked tokens) are
+ *     allowed otherwise.  No C++ exception crosses this interface.
+ *   Limits.  1 <= B <= 4096, 0 <= K <= 1024, 1 <= V <= 2097152.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned logits   */
+    SV_ERR_UNSUPPORTED = 2,   /* size beyond the limits above                 */
+    SV_ERR_WORKSPACE = 3,     /* workspace missing, too small or misaligned   */
+    SV_ERR_BUDGET = 4,        /* D-cut budget smaller than the batch          */
+    SV_ERR_BAD_INPUT = 5,     /* reserved: bad data found while checking      */
+    SV_ERR_HIP = 6            /* a HIP launch or query failed                 */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Version of this interface (incremented on any signature change). */
+int32_t spec_verify_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *spec_verify_status_string(sv_status s);
+
+/* Bytes of workspace spec_verify_greedy, spec_verify_sample and
+ * spec_draft_confidence need for a batch of this shape; 0 for sizes the
+ * library rejects. */
+size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V);
+
+/* Greedy (T = 0) verification.
+ * For request b with depth d = depth[b] (or K when depth is NULL): drafted
+ * token k is accepted iff it equals the argmax of target row (b, k) (values
+ * compared as numbers, -0.0 == +0.0, lowest index wins ties); the accepted
+ * length n_b counts the drafted tokens accepted before the first mismatch
+ * ([Remio], section "Come AngelSpec rende DFly più selettivo"); the emitted
+ * token is the argmax of target row (b, n_b): the correction when n_b < d,
+ * the bonus token when n_b = d ([Stack], section "What problem does it
+ * solve").  Acceptance at T = 0 is what [Hamidun]'s list of numbers reports.
+ *   target_logits  [B, K+1, V] of dt          (read: rows 0..d of each request)
+ *   draft_tokens   [B, K] int32               (read: 0..d-1)
+ *   depth          [B] int32 or NULL
+ *   out_tokens     [B, K+1] int32  out: x_0..x_{n-1}, emitted token, then -1
+ *   num_accepted   [B] int32       out: n_b, or -1 for bad data */
+sv_status spec_verify_greedy(const void *target_logits, sv_dtype dt,
+                             const int32_t *draft_tokens, const int32_t *depth,
+                             int32_t B, int32_t K, int32_t V,
+                             int32_t *out_tokens, int32_t *num_accepted,
+                             void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Sampled verification by rejection sampling, per-request temperature.
+ * For request b with depth d and temperature T = temperature[b]:
+ *   T == 0: the greedy rule of spec_verify_greedy.
+ *   T  > 0: with p_k = softmax(z_{b,k} / T) and q_k = softmax(y_{b,k} / T)
+ *     (T applies to target and draft rows alike), drafted token x = x_{b,k}
+ *     is accepted iff u_accept[b,k] < min(1, p_k(x) / q_k(x)) (ratio 1 when
+ *     q_k(x) = 0 < p_k(x), 0 when both are 0); n_b = first rejected k, or d.
+ *     n_b < d: the emitted token is drawn from max(0, p_n - q_n) (normalised;
+ *       p_n itself if that has no mass) by the inverse CDF at u_sample[b];
+ *     n_b = d: the bonus token is drawn from p_d the same way.
+ *   The inverse CDF takes the first token, in index order, whose inclusive
+ *   prefix of the distribution exceeds u_sample[b] times its total.
+ *   This keeps the output distributed as the target's ([Hamidun], section
+ *   "Qu'est-ce que le speculative decoding"; [Remio], section "Cosa non
+ *   dimostrano i numeri di AngelSpec").
+ *   draft_logits  [B, K, V] of dt (read: rows 0..d-1 of requests with T > 0)
+ *   temperature   [B] float >= 0
+ *   u_accept      [B, K] float in [0, 1);  u_sample [B] float in [0, 1)
+ *   p_draft, q_draft  [B, K] float or NULL  out: p_k(x_k), q_k(x_k) for every
+ *     k < d of requests with T > 0; 0 elsewhere.
+ *   Other arguments as in spec_verify_greedy.  Target row (b, d) of a request
+ *   with T > 0 is read only when nothing is rejected. */
+sv_status spec_verify_sample(const void *target_logits, const void *draft_logits,
+                             sv_dtype dt, const int32_t *draft_tokens,
+                             const int32_t *depth, const float *temperature,
+                             const float *u_accept, const float *u_sample,
+                             int32_t B, int32_t K, int32_t V,
+                             int32_t *out_tokens, int32_t *num_accepted,
+                             float *p_draft, float *q_draft,
+                             void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Draft confidence: conf[b,k] = max_v softmax(y_{b,k})_v at T = 1, the
+ * per-position confidence whose running product is the prefix confidence
+ * that drives D-cut ([Stack], section "What problem does it solve",
+ * inference layer; [AIbase]).  Rows k >= max_depth[b] (NULL => K) are not
+ * read and get 0; a bad row (NaN, +inf, all -inf) gets NaN; a max_depth
+ * outside [0, K] gives NaN for the whole request.
+ *   draft_logits [B, K, V] of dt;  conf [B, K] float (out). */
+sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt,
+                                const int32_t *max_depth,
+                                int32_t B, int32_t K, int32_t V, float *conf,
+                                void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* D-cut verification-depth allocation: verification compute is a shared
+ * batch-level budget that is moved toward the requests whose drafted
+ * prefixes are most likely to be accepted ([Stack], section "What problem
+ * does it solve", inference layer; [Remio], section "Come AngelSpec rende
+ * DFly più selettivo"), built as a global top-k of prefix confidence:
+ *   s(c) = 0 for NaN or c <= 0, 1 for c > 1, c otherwise;
+ *   c_{b,0} = s(conf[b,0]); c_{b,k} = float(c_{b,k-1} * s(conf[b,k]))
+ *   (float products, sequential in k).  Each request with K_b = max_depth[b]
+ *   (NULL => K) in [0, K] first gets min(1, K_b); the remaining budget goes
+ *   to the entries (b, k), 1 <= k < K_b, by c descending and then flat index
+ *   b*K + k ascending; depth_out[b] = its floor + its entries taken.  A
+ *   request with K_b outside [0, K] gets -1 and takes nothing.  The result is
+ *   a prefix per request, sum(depth_out) = min(budget, sum of valid K_b).
+ *   conf [B, K] float, max_depth [B] int32 or NULL, depth_out [B] int32.
+ *   Limits: B*K <= 32768.  budget < B -> SV_ERR_BUDGET. */
+sv_status dcut_allocate(const float *conf, const int32_t *max_depth,
+                        int32_t B, int32_t K, int32_t budget, int32_t *depth_out,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -71,15 +71,17 @@ static const void *row_ptr(const void *base, int dtype, int64_t row, int64_t V)
     return (const char *)base + (size_t)row * (size_t)V * esize;
 }
 
-/* A row the method reads must hold no NaN and at least one finite or +inf
- * entry; otherwise the softmax (or argmax over real scores) is undefined. */
+/* A row the method reads must hold only finite values and -inf (a masked
+ * token), with at least one finite value.  NaN or +inf makes the softmax
+ * undefined (inf - inf); an all -inf row has no distribution.  The same rule
+ * is applied to greedy rows so that one contract covers both modes. */
 static int row_check(const void *row, int dtype, int64_t V)
 {
     int any = 0;
     for (int64_t v = 0; v < V; ++v) {
         double z = logit_at(row, dtype, v);
-        if (isnan(z)) return ROW_HAS_NAN;
-        if (!(isinf(z) && z < 0)) any = 1;
+        if (isnan(z) || (isinf(z) && z > 0)) return ROW_HAS_NAN;
+        if (!isinf(z)) any = 1;
     }
     return any ? ROW_OK : ROW_ALL_NEG_INF;
 }
@@ -245,6 +247,11 @@ int oracle_verify_greedy(const void *target, int dtype, const int32_t *tokens,
 
 static int bad_uniform(float u) { return !(u >= 0.0f && u < 1.0f); }
 
+/* Temperatures the contract accepts: 0 (the greedy rule) or a finite value in
+ * [1e-6, 1e6]; NaN, negatives, infinities and values in (0, 1e-6) are bad
+ * data (the last keep log2(e)/T finite in single precision). */
+static int bad_temperature(float T) { return !(T == 0.0f || (T >= 1e-6f && T <= 1e6f)); }
+
 /* Sampled verification (rejection sampling) of a batch.
  *
  * For each request b with depth d and temperature T:
@@ -266,7 +273,7 @@ static int bad_uniform(float u) { return !(u >= 0.0f && u < 1.0f); }
  * every k < d of sampled requests, 0 elsewhere.  ratio_out [B, K] (may be
  * NULL) receives the ratio, NaN where none is computed.
  *
- * Bad data (depth outside [0,K], T < 0 or NaN, token outside [0,V), a
+ * Bad data (depth outside [0,K], T outside {0} u [1e-6, 1e6], token outside [0,V), a
  * uniform outside [0,1), NaN or all -inf in a row that is read) gives
  * num_accepted = -1 and out_tokens = -1 for that request.  The rows read
  * are target and draft rows 0..d-1, plus target row d only when nothing
@@ -289,7 +296,7 @@ int oracle_verify_sample(const void *target, const void *draft, int dtype,
             if (q_draft) q_draft[b * K + k] = 0.0f;
             if (ratio_out) ratio_out[b * K + k] = NAN;
         }
-        if (d < 0 || d > K || isnan(T) || T < 0.0) {
+        if (d < 0 || d > K || bad_temperature(temperature ? temperature[b] : 0.0f)) {
             mark_bad(out_row, K, num_accepted + b);
             continue;
         }

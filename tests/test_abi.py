@@ -1,0 +1,114 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/specverify.h declares, and rejects bad arguments on the host before
+anything is enqueued (status codes only; no compute call runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+sv = pytest.importorskip("draft_verification_verify_amd",
+                         reason="libspecverify.so not built (run draft_verification_verify_amd/build.py)")
+L = sv.lib
+
+FAKE = ctypes.c_void_p(0x100000)       # 16/256-byte aligned, never dereferenced on these paths
+FAKE_MIS = ctypes.c_void_p(0x100008)   # misaligned for logits
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_\w+|dcut_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sv.EXPORTED)
+
+
+def test_status_strings_and_version():
+    assert L.spec_verify_abi_version() == 1
+    for code, name in sv.STATUS.items():
+        assert L.spec_verify_status_string(code).decode() == name
+    assert L.spec_verify_status_string(99).decode() == "SV_ERR_UNKNOWN"
+
+
+def test_workspace_size():
+    assert sv.workspace_size(0, 3, 10) == 0
+    assert sv.workspace_size(1, -1, 10) == 0
+    assert sv.workspace_size(1, 3, 0) == 0
+    assert sv.workspace_size(4097, 3, 10) == 0
+    assert sv.workspace_size(1, 1025, 10) == 0
+    assert sv.workspace_size(1, 3, 2_000_001) == 0
+    small = sv.workspace_size(1, 3, 1000)
+    big = sv.workspace_size(64, 16, 128000)
+    assert 0 < small < big
+    assert big % 256 == 0
+    assert sv.workspace_size(64, 16, 152064) >= big
+    assert big < 64 << 20           # a few MiB, not a copy of the logits
+
+
+def greedy(target=FAKE, dt=1, tokens=FAKE, depth=NULL, B=4, K=3, V=1000, out=FAKE, num=FAKE,
+           ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = sv.workspace_size(max(B, 1), max(K, 0), max(V, 1))
+    return L.spec_verify_greedy(target, dt, tokens, depth, B, K, V, out, num, ws, wsb, NULL)
+
+
+def sample(target=FAKE, draft=FAKE, dt=1, tokens=FAKE, depth=NULL, T=FAKE, ua=FAKE, us=FAKE,
+           B=4, K=3, V=1000, out=FAKE, num=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = sv.workspace_size(max(B, 1), max(K, 0), max(V, 1))
+    return L.spec_verify_sample(target, draft, dt, tokens, depth, T, ua, us, B, K, V, out, num,
+                                NULL, NULL, ws, wsb, NULL)
+
+
+def test_greedy_host_errors():
+    assert greedy(target=NULL) == 1
+    assert greedy(tokens=NULL) == 1
+    assert greedy(out=NULL) == 1
+    assert greedy(num=NULL) == 1
+    assert greedy(dt=7) == 1
+    assert greedy(B=0) == 1
+    assert greedy(K=-1) == 1
+    assert greedy(V=0) == 1
+    assert greedy(B=5000) == 2
+    assert greedy(K=2000) == 2
+    assert greedy(V=3_000_000) == 2
+    assert greedy(target=FAKE_MIS) == 1
+    assert greedy(ws=NULL) == 3
+    assert greedy(wsb=100) == 3
+    assert greedy(ws=ctypes.c_void_p(0x100010)) == 3     # workspace must be 256-byte aligned
+
+
+def test_sample_host_errors():
+    assert sample(target=NULL) == 1
+    assert sample(draft=NULL) == 1
+    assert sample(T=NULL) == 1
+    assert sample(ua=NULL) == 1
+    assert sample(us=NULL) == 1
+    assert sample(tokens=NULL) == 1
+    assert sample(draft=FAKE_MIS) == 1
+    assert sample(dt=2) == 1
+    assert sample(B=0) == 1
+    assert sample(wsb=10) == 3
+
+
+def test_confidence_and_dcut_host_errors():
+    wsb = sv.workspace_size(4, 3, 1000)
+    assert L.spec_draft_confidence(NULL, 1, NULL, 4, 3, 1000, FAKE, FAKE, wsb, NULL) == 1
+    assert L.spec_draft_confidence(FAKE, 1, NULL, 4, 3, 1000, NULL, FAKE, wsb, NULL) == 1
+    assert L.spec_draft_confidence(FAKE, 1, NULL, 4, 3, 1000, FAKE, FAKE, 16, NULL) == 3
+    assert L.spec_draft_confidence(FAKE, 1, NULL, 0, 3, 1000, FAKE, FAKE, wsb, NULL) == 1
+    assert L.dcut_allocate(FAKE, NULL, 4, 3, 3, FAKE, NULL) == 4         # budget < B
+    assert L.dcut_allocate(FAKE, NULL, 0, 3, 3, FAKE, NULL) == 1
+    assert L.dcut_allocate(NULL, NULL, 4, 3, 8, FAKE, NULL) == 1
+    assert L.dcut_allocate(FAKE, NULL, 4, 3, 8, NULL, NULL) == 1
+    assert L.dcut_allocate(FAKE, NULL, 4096, 16, 9000, FAKE, NULL) == 2  # B*K > 32768

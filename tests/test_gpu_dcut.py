@@ -1,0 +1,72 @@
+"""dcut_allocate on the GPU is bit-exact with the oracle given the same fp32
+confidences: random, tie-heavy, underflowing (denormal) products, ragged and
+invalid max_depth, budgets from B to beyond sum K_b, and the largest B*K."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build(force=False)
+
+
+def run(conf, budget, max_depth=None):
+    import draft_verification_verify_amd as sv
+    d = sv.dcut_allocate(dev(conf), budget, dev(max_depth))
+    torch.cuda.synchronize()
+    return host(d)
+
+
+def test_dcut_random_bit_exact():
+    g = np.random.default_rng(31)
+    for trial in range(60):
+        B = int(g.integers(1, 130))
+        K = int(g.integers(1, 20))
+        conf = g.uniform(0.0, 1.0, (B, K)).astype(np.float32)
+        if trial % 4 == 0:
+            conf = np.round(conf * 3) / 3
+        if trial % 5 == 0:
+            conf[g.random((B, K)) < 0.1] = np.nan
+        kb = g.integers(0, K + 1, B).astype(np.int32) if trial % 2 else None
+        budget = int(g.integers(B, B * K + 5))
+        want = oracle.dcut_allocate(conf, budget, kb)
+        got = run(conf, budget, kb)
+        assert np.array_equal(want, got), (trial, B, K, budget)
+
+
+def test_dcut_denormal_products_and_ties():
+    B, K = 40, 16
+    conf = np.full((B, K), 1e-3, np.float32)
+    conf[::3] = 2e-3
+    conf[5, :] = 1.0
+    for budget in (B, B + 1, 100, 300, B * K, B * K + 100):
+        want = oracle.dcut_allocate(conf, budget)
+        assert np.array_equal(run(conf, budget), want), budget
+
+
+def test_dcut_invalid_max_depth_and_largest_batch():
+    conf = np.full((4, 5), 0.9, np.float32)
+    kb = np.array([5, 6, -1, 0], np.int32)
+    assert run(conf, 9, kb).tolist() == oracle.dcut_allocate(conf, 9, kb).tolist() == [5, -1, -1, 0]
+    g = np.random.default_rng(7)
+    B, K = 2048, 16                      # B*K = 32768, the limit
+    conf = g.uniform(0.2, 1.0, (B, K)).astype(np.float32)
+    for budget in (B, 9000, B * K):
+        assert np.array_equal(run(conf, budget), oracle.dcut_allocate(conf, budget))
+
+
+def test_dcut_config_sizes():
+    # the two workload budgets: B=64,K=16 budget 384; B=64 mixed K_b in {3,16} budget 512
+    g = np.random.default_rng(3)
+    conf = g.uniform(0.001, 0.3, (64, 16)).astype(np.float32)
+    assert np.array_equal(run(conf, 384), oracle.dcut_allocate(conf, 384))
+    kb = np.where(g.random(64) < 0.5, 3, 16).astype(np.int32)
+    assert np.array_equal(run(conf, 512, kb), oracle.dcut_allocate(conf, 512, kb))

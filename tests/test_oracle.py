@@ -77,6 +77,8 @@ def test_softmax_masked_entries_and_bad_rows():
         oracle.softmax(f32([1.0, np.nan, 2.0]), 1.0)
     with pytest.raises(ValueError):
         oracle.softmax(f32([-np.inf, -np.inf]), 1.0)
+    with pytest.raises(ValueError):
+        oracle.softmax(f32([1.0, np.inf]), 1.0)      # +inf: inf - inf is undefined
 
 
 # --------------------------------------------------------------------------
@@ -245,6 +247,9 @@ def test_greedy_bad_inputs():
     depth = np.array([3, 3, 2, 3], np.int32)
     out, n = oracle.verify_greedy(target, tokens, depth)
     assert n.tolist() == [-1, -1, 2, -1]
+    t2 = target.copy()
+    t2[2, 1, 7] = np.inf        # +inf inside the window
+    assert oracle.verify_greedy(t2, tokens, depth)[1][2] == -1
     assert np.all(out[[0, 1, 3]] == -1)
     out, n = oracle.verify_greedy(target, tokens, np.array([4, -1, 2, 3], np.int32))
     assert n[0] == -1 and n[1] == -1
@@ -417,6 +422,10 @@ def test_sample_bad_inputs_and_window():
     res = oracle.verify_sample(t, d, tok, T, ua, us, depth)
     assert res["n"].tolist()[:3] == [-1, -1, -1]
     assert res["n"][3] >= 0 and res["n"][4] == -1 and res["n"][5] == -1
+    T2 = w.temperature.copy()
+    T2[:4] = [np.inf, 1e-7, 2e6, 1e-6]    # outside [1e-6, 1e6] is bad; 1e-6 itself is fine
+    res2 = oracle.verify_sample(w.target, w.draft, w.tokens, T2, w.u_accept, w.u_sample)
+    assert res2["n"].tolist()[:3] == [-1, -1, -1] and res2["n"][3] >= 0
     assert np.all(res["out"][[0, 1, 2, 4, 5]] == -1)
     assert np.all(res["p_draft"][3, 1:] == 0)
 
