@@ -29,20 +29,27 @@ STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED", 3: "SV_E
 
 
 class SpecVerifyError(RuntimeError):
-    def __init__(self, fn: str, status: int):
+    def __init__(self, fn: str, status: int, detail: str = ""):
         self.status = status
-        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}" + (f": {detail}" if detail else ""))
 
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python draft_verification_verify_amd/build.py`")
+    # torch ships its own HIP runtime (loaded by its unversioned file name).
+    # Import it first so that libspecverify binds to that same runtime via its
+    # soname; loading ours first would put two HIP runtimes in the process,
+    # and device memory from one is unusable by kernels launched on the other.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.spec_verify_abi_version.restype = i32
     L.spec_verify_abi_version.argtypes = []
     L.spec_verify_status_string.restype = ctypes.c_char_p
     L.spec_verify_status_string.argtypes = [ctypes.c_int]
+    L.spec_verify_last_error.restype = ctypes.c_char_p
+    L.spec_verify_last_error.argtypes = []
     L.spec_verify_workspace_size.restype = sz
     L.spec_verify_workspace_size.argtypes = [i32, i32, i32]
     L.spec_verify_greedy.restype = ctypes.c_int
@@ -61,7 +68,8 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
-EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify_workspace_size",
+EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify_last_error",
+            "spec_verify_workspace_size",
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate")
 
 
@@ -113,11 +121,10 @@ def _check(t, name, dtype=None, shape=None):
 
 
 class Workspace:
-    """A zero-filled device buffer reused across calls on one device.
+    """A device buffer reused across calls on one device (grown on demand).
 
-    The library leaves its counters at zero after every call, so the buffer
-    is zeroed only when it is (re)allocated.  Calls that share a workspace
-    must be ordered on one stream."""
+    Each call clears the counters it uses, so contents never matter.  Calls
+    that share a workspace must be ordered on one stream."""
 
     def __init__(self):
         self._buf = {}
@@ -129,7 +136,7 @@ class Workspace:
         with self._lock:
             buf = self._buf.get(key)
             if buf is None or buf.numel() < nbytes:
-                buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=torch.device("cuda", key))
+                buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=torch.device("cuda", key))
                 self._buf[key] = buf
             return buf
 
@@ -148,7 +155,8 @@ def _ws(device, B, K, V, workspace):
 
 def _raise(fn, st):
     if st != 0:
-        raise SpecVerifyError(fn, st)
+        detail = lib.spec_verify_last_error().decode() if st == 6 else ""
+        raise SpecVerifyError(fn, st, detail)
 
 
 def verify_greedy(target, tokens, depth=None, *, out_tokens=None, num_accepted=None,

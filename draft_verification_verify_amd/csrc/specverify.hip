@@ -17,30 +17,34 @@
 // rule is the standard speculative-sampling construction (Leviathan et al.
 // 2023; Chen et al. 2023).
 //
-// Structure of one verification call (all kernels on the caller's stream):
-//  1. row_stats_kernel -- persistent grid; every workgroup plans the batch
-//     itself from depth[] and temperature[] (no host round trip), then walks
-//     (row, chunk) tasks.  A task streams one chunk of one logit row from HBM
-//     with 16-byte loads and reduces it to (max, lowest argmax) or to
-//     (max, sum of exp) in fp32 with a double accumulator.  The last chunk of
-//     a row to finish (device-scope atomic) merges the chunk partials; the
-//     last row of a request to finish runs that request's accept test and
-//     first-rejection scan (one wave, lanes over positions).
-//  2. sampler_sums_kernel -- per (request, chunk) of the one row pair a
-//     sampled request draws from: fp64 softmax normalisers of that pair.
-//  3. sampler_draw_kernel -- per (request, chunk): fp64 residual
-//     max(0, p - q) (or p for the bonus) chunk totals; the last chunk of a
-//     request to finish locates u*R among the chunk totals and scans that
-//     chunk for the token.
-// Greedy calls run only step 1.  The draft-confidence call runs step 1 in a
-// third mode.  dcut_allocate is one workgroup: fp32 running products and an
-// LDS radix select.
-//
-// Nothing on this path is a dense contraction, so there is no MFMA here: the
-// row pass is bound by HBM bandwidth, the sampler by fp64 VALU throughput.
+// One verification call is three kernels on the caller's stream:
+//  A. row_pass_kernel -- the HBM stream.  A persistent grid of independent
+//     waves; every workgroup plans the batch itself from depth[] and
+//     temperature[] (no host round trip).  A wave task is one chunk of one
+//     logit row, read with 16-byte nontemporal loads, double-buffered across
+//     batches and across consecutive tasks, and reduced to (max, lowest
+//     argmax) for greedy rows or (max, sum of exp) for sampled rows.  Each
+//     task stores its partial with plain stores: no atomics, no waits.
+//  B. finish_kernel -- one workgroup per (request, sampler chunk).  It
+//     gathers the request's chunk partials into LDS, merges them per row, and
+//     runs the accept test and first-rejection scan (every chunk's workgroup
+//     does this cheap step itself, so none waits on another).  For a request
+//     that draws a token it then reduces its chunk of the row pair in fp64:
+//     the softmax normalisers.
+//  C. draw_kernel -- per (request, chunk): fp64 residual max(0, p - q) (or p
+//     for the bonus token) chunk totals; the last chunk of a request to
+//     finish locates u*R among the totals and scans that chunk.
+// The kernel boundaries order all data between phases.  Inside B and C the
+// last workgroup of a request is found with a device-scope counter and reads
+// the others' partials back with device-scope loads (no cache flushes).
+// dcut_allocate is one workgroup: fp32 running products and an LDS radix
+// select.  Nothing here is a dense contraction, so there is no MFMA: A is
+// bound by HBM bandwidth, B and C by fp64 arithmetic on one row pair per
+// request.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
@@ -52,24 +56,28 @@ namespace {
 
 constexpr int WG = 256;           // threads per workgroup
 constexpr int NWAVE = WG / 64;    // wave64
-constexpr int UMAX = 8;           // 16-byte loads per thread per row task
-constexpr int US = 4;             // 16-byte loads per thread per sampler task
+constexpr int UW = 4;             // 16-byte loads per lane per row-pass batch
+constexpr int WVEC = UW * 64;     // vectors per wave batch
+constexpr int US = 4;             // 16-byte loads per thread per sampler chunk
 constexpr int CPR_CAP = 256;      // chunks per row, at most
+constexpr int STAGE = 1024;       // partials staged in LDS at a time (finish kernel)
 constexpr int B_MAX = 4096;
 constexpr int K_MAX = 1024;
 constexpr int V_MAX = 2000000;
-constexpr int DCUT_MAX = 32768;   // B*K for dcut_allocate
+constexpr int DCUT_MAX = 32768;   // B*K for dcut_allocate (keys held in LDS)
 constexpr int DCUT_WG = 1024;
+constexpr int EXP2_TAB = 512;     // table entries of the fp64 exp2
 
 enum : int { MODE_GREEDY = 0, MODE_SAMPLE = 1, MODE_CONF = 2 };
 enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3 };
 enum : int { SREQ_NONE = 0, SREQ_RESID = 1, SREQ_BONUS = 2 };
 
 constexpr double LOG2E = 1.4426950408889634;
+constexpr double LN2 = 0.6931471805599453;
 
 // Partial or merged statistics of (part of) a row.  Argmax rows use (m, idx);
-// log-sum-exp rows use (m, s) with s = sum exp2((v - m) * log2e / T).  A row
-// that is unusable (NaN, +inf, nothing but -inf) has m = NaN.
+// log-sum-exp rows use (m, s) with s = sum exp2((v - m) * c32).  A row that
+// is unusable (NaN, +inf, nothing but -inf) has m = NaN or infinite.
 struct alignas(16) Stat {
     float m;
     int32_t idx;
@@ -94,20 +102,18 @@ struct alignas(16) S2Part {
 };
 
 struct Ws {
-    uint32_t *row_cnt;   // [R_max]
-    uint32_t *req_cnt;   // [B]
-    Stat *part;          // [R_max * cpr_max]
-    Stat *rows;          // [R_max]
+    int32_t *meta;       // [4]: chunks per row and batches per chunk of the row pass
+    uint32_t *s1cnt;     // [B]  (cleared by the row pass)
+    uint32_t *s2cnt;     // [B]  (cleared by the finish kernel)
+    Stat *part;          // [R_max * cpr_max] row-pass chunk partials
     ReqDesc *req;        // [B]
     S1Part *s1;          // [B * cs_max]
-    uint32_t *s1cnt;     // [B]
     S1Part *s1tot;       // [B]
     S2Part *s2;          // [B * cs_max]
-    uint32_t *s2cnt;     // [B]
 };
 
 struct Layout {
-    size_t off[10];
+    size_t off[6];
     size_t total;
     int64_t r_max;
     int cpr_max;
@@ -127,22 +133,18 @@ bool make_layout(int B, int K, int V, Layout &L)
     if (B < 1 || B > B_MAX || K < 0 || K > K_MAX || V < 1 || V > V_MAX) return false;
     const int64_t nv = nvec_max(V, 4);   // fp32 is the worst case
     L.r_max = (int64_t)B * (2 * K + 1);
-    L.cpr_max = (int)std::min<int64_t>(CPR_CAP, ceil_div(nv, WG));
+    L.cpr_max = (int)std::min<int64_t>(CPR_CAP, ceil_div(nv, WVEC));
     L.cs_max = (int)ceil_div(nv, (int64_t)WG * US);
-    const size_t sz[10] = {
-        sizeof(uint32_t) * (size_t)L.r_max,
-        sizeof(uint32_t) * (size_t)B,
+    const size_t sz[6] = {
+        sizeof(int32_t) * 4 + sizeof(uint32_t) * 2 * (size_t)B,
         sizeof(Stat) * (size_t)L.r_max * (size_t)L.cpr_max,
-        sizeof(Stat) * (size_t)L.r_max,
         sizeof(ReqDesc) * (size_t)B,
         sizeof(S1Part) * (size_t)B * (size_t)L.cs_max,
-        sizeof(uint32_t) * (size_t)B,
         sizeof(S1Part) * (size_t)B,
         sizeof(S2Part) * (size_t)B * (size_t)L.cs_max,
-        sizeof(uint32_t) * (size_t)B,
     };
     size_t o = 0;
-    for (int i = 0; i < 10; ++i) {
+    for (int i = 0; i < 6; ++i) {
         L.off[i] = o;
         o += align256(sz[i]);
     }
@@ -150,20 +152,18 @@ bool make_layout(int B, int K, int V, Layout &L)
     return true;
 }
 
-Ws carve(void *base, const Layout &L)
+Ws carve(void *base, const Layout &L, int B)
 {
     char *p = (char *)base;
     Ws w;
-    w.row_cnt = (uint32_t *)(p + L.off[0]);
-    w.req_cnt = (uint32_t *)(p + L.off[1]);
-    w.part = (Stat *)(p + L.off[2]);
-    w.rows = (Stat *)(p + L.off[3]);
-    w.req = (ReqDesc *)(p + L.off[4]);
-    w.s1 = (S1Part *)(p + L.off[5]);
-    w.s1cnt = (uint32_t *)(p + L.off[6]);
-    w.s1tot = (S1Part *)(p + L.off[7]);
-    w.s2 = (S2Part *)(p + L.off[8]);
-    w.s2cnt = (uint32_t *)(p + L.off[9]);
+    w.meta = (int32_t *)(p + L.off[0]);
+    w.s1cnt = (uint32_t *)(p + L.off[0] + 16);
+    w.s2cnt = w.s1cnt + B;
+    w.part = (Stat *)(p + L.off[1]);
+    w.req = (ReqDesc *)(p + L.off[2]);
+    w.s1 = (S1Part *)(p + L.off[3]);
+    w.s1tot = (S1Part *)(p + L.off[4]);
+    w.s2 = (S2Part *)(p + L.off[5]);
     return w;
 }
 
@@ -196,7 +196,7 @@ struct Params {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Element e of a 16-byte vector, as fp32 (exact widening for bf16).
+// The elements of a 16-byte vector as fp32 (exact widening for bf16).
 template <bool BF16>
 __device__ __forceinline__ void unpack(const uint4 &v, float *f)
 {
@@ -223,20 +223,91 @@ __device__ __forceinline__ float load_logit_dt(const void *base, bool bf16, int6
     return bf16 ? load_logit<true>(base, i) : load_logit<false>(base, i);
 }
 
-// Device-scope release/acquire around the cross-workgroup hand-offs.  The
-// eight XCDs have separate L2s, so a partial written by one workgroup is made
-// visible to a workgroup on another XCD only through agent-scope fences.
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Pointers into device memory in the global address space: loads through
+// them compile to global_load (a generic pointer, e.g. one taken out of a
+// struct kernel argument, would compile to flat_load).
+typedef const __attribute__((address_space(1))) uint4 *gvec_t;
 
-__device__ __forceinline__ uint32_t atomic_inc_agent(uint32_t *p)
+// Plain 16-byte load (the sampler re-reads rows the row pass streamed).
+__device__ __forceinline__ uint4 ld_plain(gvec_t p)
 {
-    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const u4v w = *(const __attribute__((address_space(1))) u4v *)p;
+    return make_uint4(w.x, w.y, w.z, w.w);
 }
 
-__device__ __forceinline__ void store_zero_agent(uint32_t *p)
+// Streaming 16-byte load (nontemporal: the row pass reads each logit once).
+__device__ __forceinline__ uint4 ld_stream(gvec_t p)
 {
-    __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const u4v w = __builtin_nontemporal_load((const __attribute__((address_space(1))) u4v *)p);
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+
+// Cross-workgroup hand-off inside a kernel, without cache maintenance.  Data
+// another workgroup will read is written with device-scope (sc1) atomic
+// stores, which complete at the device coherence point; an s_waitcnt waits
+// for them to complete before the counter's atomic increment is issued, and
+// the workgroup that sees the final count reads the data back with
+// device-scope atomic loads, which never return stale cache lines.  (An
+// agent-scope release/acquire fence would instead write back and invalidate
+// the XCD's whole L2.)
+__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t *p)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ uint32_t count_in(uint32_t *p)
+{
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void after_count() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+__device__ __forceinline__ uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x); }
+__device__ __forceinline__ double bitsd(uint64_t x) { return __longlong_as_double((long long)x); }
+
+__device__ __forceinline__ void put_s1(S1Part *p, const S1Part &v)
+{
+    st_dev((uint64_t *)p, (uint64_t)__float_as_uint(v.mz) | ((uint64_t)__float_as_uint(v.my) << 32));
+    st_dev((uint64_t *)p + 1, (uint64_t)(uint32_t)v.bad);
+    st_dev((uint64_t *)p + 2, dbits(v.sz));
+    st_dev((uint64_t *)p + 3, dbits(v.sy));
+}
+
+__device__ __forceinline__ S1Part get_s1(const S1Part *p)
+{
+    const uint64_t w0 = ld_dev((const uint64_t *)p), w1 = ld_dev((const uint64_t *)p + 1);
+    S1Part v;
+    v.mz = __uint_as_float((uint32_t)w0);
+    v.my = __uint_as_float((uint32_t)(w0 >> 32));
+    v.bad = (int32_t)w1;
+    v.pad = 0;
+    v.sz = bitsd(ld_dev((const uint64_t *)p + 2));
+    v.sy = bitsd(ld_dev((const uint64_t *)p + 3));
+    return v;
+}
+
+__device__ __forceinline__ void put_s2(S2Part *p, const S2Part &v)
+{
+    st_dev((uint64_t *)p, dbits(v.r));
+    st_dev((uint64_t *)p + 1, dbits(v.p));
+}
+
+__device__ __forceinline__ S2Part get_s2(const S2Part *p)
+{
+    S2Part v;
+    v.r = bitsd(ld_dev((const uint64_t *)p));
+    v.p = bitsd(ld_dev((const uint64_t *)p + 1));
+    return v;
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -263,7 +334,7 @@ __device__ __forceinline__ int wave_or(int v)
     return v;
 }
 
-// (value desc, index asc) argmax merge; NaN values are carried by a flag.
+// (value desc, index asc) argmax merge.
 __device__ __forceinline__ void argmax_merge(float &m, int &i, float m2, int i2)
 {
     if (m2 > m || (m2 == m && i2 < i)) { m = m2; i = i2; }
@@ -273,8 +344,8 @@ __device__ __forceinline__ void wave_argmax(float &m, int &i)
 {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        float m2 = __shfl_xor(m, o, 64);
-        int i2 = __shfl_xor(i, o, 64);
+        const float m2 = __shfl_xor(m, o, 64);
+        const int i2 = __shfl_xor(i, o, 64);
         argmax_merge(m, i, m2, i2);
     }
 }
@@ -284,7 +355,6 @@ struct RedSmem {
     float f[NWAVE];
     int i[NWAVE];
     double d[NWAVE];
-    int flag;
 };
 
 __device__ float wg_max(float v, RedSmem &sm)
@@ -335,6 +405,55 @@ __device__ void wg_argmax(float &m, int &i, RedSmem &sm)
     for (int w = 1; w < NWAVE; ++w) argmax_merge(m, i, sm.f[w], sm.i[w]);
 }
 
+// Exclusive scan of one double per thread over the workgroup, in thread order.
+__device__ double wg_excl_scan(double v, double *sm4, double &total)
+{
+    const int lane = lane_id();
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    double excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0;
+    __syncthreads();
+    if (lane == 63) sm4[wave_id()] = incl;
+    __syncthreads();
+    double wb = 0.0, tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+        if (w < wave_id()) wb += sm4[w];
+        tot += sm4[w];
+    }
+    total = tot;
+    return wb + excl;
+}
+
+// fp64 2^x for x <= 0: x = k/512 + r with k = rint(512 x) and |r| <= 1/1024;
+// 2^(k/512) = 2^(k >> 9) * T[k & 511] with T[j] = 2^(j/512) tabulated in LDS
+// at kernel start, and 2^r = exp(r ln2) by its Taylor polynomial of degree 4
+// (truncation below 2e-18 relative).  Total error about 2 ulp.  Arguments at
+// or below -1070 give 0; NaN propagates.
+__device__ void init_exp2_table(double *tab)
+{
+    for (int j = threadIdx.x; j < EXP2_TAB; j += blockDim.x) tab[j] = exp2((double)j / EXP2_TAB);
+    __syncthreads();
+}
+
+__device__ __forceinline__ double exp2_tab(double x, const double *tab)
+{
+    if (!(x > -1070.0)) return (x != x) ? x : 0.0;
+    const double kd = rint(x * EXP2_TAB);
+    const int k = (int)kd;
+    const double t = fma(kd, -1.0 / EXP2_TAB, x) * LN2;
+    double p = fma(t, 1.0 / 24.0, 1.0 / 6.0);
+    p = fma(t, p, 0.5);
+    p = fma(t, p, 1.0);
+    p = fma(t, p, 1.0);
+    return ldexp(tab[k & (EXP2_TAB - 1)] * p, k >> 9);
+}
+
 // ---------------------------------------------------------------------------
 // Batch plan: rows each request contributes to the row pass.
 //   greedy request (greedy call, or T == 0): target rows 0..d
@@ -348,47 +467,58 @@ __device__ __forceinline__ bool temp_ok(float T)
     return T == 0.0f || (T >= 1e-6f && T <= 1e6f);   // excludes NaN, < 0, inf
 }
 
+struct ReqPlan {
+    int d, kind, rows;
+    float T;
+};
+
+__device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
+{
+    ReqPlan q;
+    q.T = 0.0f;
+    if (P.mode == MODE_CONF) {
+        q.d = P.max_depth ? P.max_depth[b] : P.K;
+        const bool ok = q.d >= 0 && q.d <= P.K;
+        q.kind = ok ? KIND_CONF : KIND_BAD;
+        q.rows = ok ? q.d : 0;
+    } else {
+        q.d = P.depth ? P.depth[b] : P.K;
+        q.T = (P.mode == MODE_SAMPLE) ? P.temperature[b] : 0.0f;
+        const bool ok = q.d >= 0 && q.d <= P.K && temp_ok(q.T);
+        q.kind = !ok ? KIND_BAD : (q.T > 0.0f ? KIND_SAMPLED : KIND_GREEDY);
+        q.rows = !ok ? 0 : (q.kind == KIND_SAMPLED ? 2 * q.d : q.d + 1);
+    }
+    if (q.kind == KIND_BAD) q.d = 0;
+    return q;
+}
+
 struct Plan {
     int *row_off;   // [B + 1] in LDS
     int *info;      // [B] in LDS: d | kind << 16
     float *T;       // [B] in LDS
 };
 
+// Whole-workgroup plan: row_off = exclusive prefix of per-request rows.
 __device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
 {
-    const int B = P.B, K = P.K;
+    const int B = P.B;
     const int per = (int)ceil_div(B, WG);
     const int b0 = threadIdx.x * per;
     int local = 0;
     for (int j = 0; j < per; ++j) {
-        int b = b0 + j;
+        const int b = b0 + j;
         if (b >= B) break;
-        int d, kind, rows;
-        float T = 0.0f;
-        if (P.mode == MODE_CONF) {
-            d = P.max_depth ? P.max_depth[b] : K;
-            bool ok = d >= 0 && d <= K;
-            kind = ok ? KIND_CONF : KIND_BAD;
-            rows = ok ? d : 0;
-        } else {
-            d = P.depth ? P.depth[b] : K;
-            T = (P.mode == MODE_SAMPLE) ? P.temperature[b] : 0.0f;
-            bool ok = d >= 0 && d <= K && temp_ok(T);
-            kind = !ok ? KIND_BAD : (T > 0.0f ? KIND_SAMPLED : KIND_GREEDY);
-            rows = !ok ? 0 : (kind == KIND_SAMPLED ? 2 * d : d + 1);
-        }
-        if (kind == KIND_BAD) d = 0;
-        pl.info[b] = d | (kind << 16);
-        pl.T[b] = T;
-        pl.row_off[b] = rows;    // count for now
-        local += rows;
+        const ReqPlan q = plan_request(P, b);
+        pl.info[b] = q.d | (q.kind << 16);
+        pl.T[b] = q.T;
+        pl.row_off[b] = q.rows;   // count for now
+        local += q.rows;
     }
-    // exclusive scan of the per-thread totals
     int v = local;
-    int lane = lane_id();
+    const int lane = lane_id();
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(v, o, 64);
+        const int y = __shfl_up(v, o, 64);
         if (lane >= o) v += y;
     }
     if (lane == 63) scan_tmp[wave_id()] = v;
@@ -397,9 +527,9 @@ __device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
     for (int w = 0; w < wave_id(); ++w) wave_base += scan_tmp[w];
     int run = wave_base + v - local;
     for (int j = 0; j < per; ++j) {
-        int b = b0 + j;
+        const int b = b0 + j;
         if (b >= B) break;
-        int c = pl.row_off[b];
+        const int c = pl.row_off[b];
         pl.row_off[b] = run;
         run += c;
     }
@@ -412,170 +542,345 @@ __device__ __forceinline__ int find_request(const int *row_off, int B, int r)
 {
     int lo = 0, hi = B;   // row_off[lo] <= r < row_off[hi]
     while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if (row_off[mid] <= r) lo = mid; else hi = mid;
     }
     return lo;
 }
 
+// Chunking of the row pass: cpr chunks per row of nb batches each, with cpr
+// chosen so that every wave gets about eight tasks (bounded tail imbalance)
+// but a task is never shorter than one batch.
+__device__ __forceinline__ void row_chunking(int R, int V, bool bf16, int64_t nwaves, int &cpr, int &nb)
+{
+    const int64_t nv = nvec_max(V, bf16 ? 8 : 4);
+    const int nbt = (int)ceil_div(nv, WVEC);
+    const int64_t want = ceil_div(8 * nwaves, (int64_t)(R > 0 ? R : 1));
+    cpr = (int)std::min<int64_t>(std::max<int64_t>(want, 1), std::min(nbt, CPR_CAP));
+    nb = (int)ceil_div(nbt, cpr);
+    cpr = (int)ceil_div(nbt, nb);
+}
+
 // ---------------------------------------------------------------------------
-// Row-pass chunk reductions.  A chunk of a row is the 16-byte vectors
-// [vbeg, vbeg + U*WG) of the row's vector grid; thread t reads vectors
-// vbeg + j*WG + t, j < U, so each wave load is one contiguous 1 KiB.  The
-// vector grid starts at the row's first element rounded down to 16 bytes;
-// `head` elements of the first vector belong to the previous row and are
-// masked, as are elements past the row end.
+// Row pass (kernel A).  A wave task reads a run of batches of one logit row;
+// a batch is UW 16-byte vectors per lane, lane l reading vectors
+// vbeg + j*64 + l, so every wave load instruction is one contiguous 1 KiB.
+// The vector grid starts at the row's first element rounded down to 16
+// bytes; elements before the row start or past its end are masked to -inf.
 // ---------------------------------------------------------------------------
 
 template <bool BF16>
 struct RowView {
     static constexpr int EPV = BF16 ? 8 : 4;
-    const uint4 *vec;   // 16-byte aligned start of the vector grid
+    gvec_t vec;         // 16-byte aligned start of the vector grid
     int head;           // elements of vector 0 before the row start
-    int64_t nvec;       // vectors covering the row
+    int nvec;           // vectors covering the row
     int V;
 
+    __device__ RowView() {}
     __device__ RowView(const void *row_start, int V_) : V(V_)
     {
-        uintptr_t a = (uintptr_t)row_start;
-        uintptr_t a0 = a & ~uintptr_t(15);
-        vec = (const uint4 *)a0;
-        head = (int)((a - a0) / (BF16 ? 2 : 4));
-        nvec = ceil_div((int64_t)head + V, EPV);
+        const int off = (int)((uintptr_t)row_start & 15u);
+        vec = (gvec_t)((const char *)row_start - off);
+        head = off / (BF16 ? 2 : 4);
+        nvec = (int)ceil_div((int64_t)head + V, EPV);
     }
     // element index (within the row) of element e of vector vi
-    __device__ __forceinline__ int64_t elem(int64_t vi, int e) const { return vi * EPV + e - head; }
-    __device__ __forceinline__ bool edge(int64_t vi) const
+    __device__ __forceinline__ int elem(int vi, int e) const { return vi * EPV + e - head; }
+    // does vector vi hold elements outside the row?
+    __device__ __forceinline__ bool edge(int vi) const { return vi * EPV < head || (vi + 1) * EPV - head > V; }
+    // does the batch of vectors [vbeg, vbeg + n) touch a row edge?
+    __device__ __forceinline__ bool batch_edge(int vbeg, int n) const
     {
-        return vi * EPV < head || (vi + 1) * EPV - head > V;
+        return vbeg * EPV < head || (vbeg + n) * EPV - head > V;
     }
 };
 
-// Greedy row chunk: largest value and its lowest index; NaN flagged.
-template <bool BF16>
-__device__ void chunk_argmax(const RowView<BF16> &rv, int64_t vbeg, int U, float &best, int &bidx, int &nanf)
+// Issues one batch of loads.  Branch-free: vectors past the row are loaded
+// from the row's last vector instead (always a valid address) and their
+// elements, whose indices lie past V, are masked when the batch is widened.
+// A load under a branch would make the compiler wait for every outstanding
+// load at the join, which would defeat the double buffering.
+__device__ __forceinline__ void issue_batch(gvec_t vec, int nvec, int vbeg, uint4 (&raw)[UW])
 {
-    constexpr int EPV = RowView<BF16>::EPV;
-    const uint32_t NEG = BF16 ? 0xff80ff80u : 0xff800000u;
-    uint4 raw[UMAX];
+    const int lane = lane_id();
 #pragma unroll
-    for (int j = 0; j < UMAX; ++j) {
-        int64_t vi = vbeg + (int64_t)j * WG + threadIdx.x;
-        if (j < U && vi < rv.nvec) raw[j] = rv.vec[vi];
-        else raw[j] = make_uint4(NEG, NEG, NEG, NEG);
-    }
-    best = -INFINITY;
-    int bj = -1;
-    uint4 bvec = make_uint4(NEG, NEG, NEG, NEG);
-    int un = 0;
+    for (int j = 0; j < UW; ++j) raw[j] = ld_stream(vec + min(vbeg + j * 64 + lane, nvec - 1));
+}
+
+template <bool BF16, bool EDGE>
+__device__ __forceinline__ void widen(const RowView<BF16> &rv, int vi, const uint4 &raw, float (&f)[RowView<BF16>::EPV])
+{
+    unpack<BF16>(raw, f);
+    if (EDGE) {
 #pragma unroll
-    for (int j = 0; j < UMAX; ++j) {
-        int64_t vi = vbeg + (int64_t)j * WG + threadIdx.x;
-        float f[EPV];
-        unpack<BF16>(raw[j], f);
-        if (rv.edge(vi)) {
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                int64_t x = rv.elem(vi, e);
-                if (x < 0 || x >= rv.V) f[e] = -INFINITY;
-            }
+        for (int e = 0; e < RowView<BF16>::EPV; ++e) {
+            const int x = rv.elem(vi, e);
+            if (x < 0 || x >= rv.V) f[e] = -INFINITY;
         }
-#pragma unroll
-        for (int e = 0; e < EPV; e += 2) un |= __builtin_isunordered(f[e], f[e + 1]);
-        float m = f[0];
-#pragma unroll
-        for (int e = 1; e < EPV; ++e) m = fmaxf(m, f[e]);
-        if (m > best) { best = m; bj = j; bvec = raw[j]; }
-    }
-    nanf = un;
-    bidx = 0x7fffffff;
-    if (bj >= 0) {
-        int64_t vi = vbeg + (int64_t)bj * WG + threadIdx.x;
-        float f[EPV];
-        unpack<BF16>(bvec, f);
-        int found = -1;
-#pragma unroll
-        for (int e = EPV - 1; e >= 0; --e) {
-            int64_t x = rv.elem(vi, e);
-            if (x >= 0 && x < rv.V && f[e] == best) found = e;
-        }
-        if (found >= 0) bidx = (int)rv.elem(vi, found);
     }
 }
 
-// Sampled / confidence row chunk: thread max m and s = sum exp2((v-m)*c),
-// with c = log2(e)/T rounded to fp32 (c32).  The per-element exponent is one
-// FMA, v*c32 - fl(m*c32); its constant offset fl(m*c32) - m*c32 is exact
-// (FMA residual) and is removed from the sum in double.  Terms are summed in
-// fp32 per vector (a short tree) and the vector sums in double.
-template <bool BF16>
-__device__ void chunk_lse(const RowView<BF16> &rv, int64_t vbeg, int U, float c32, float &m_out, double &s_out)
+// Greedy rows: running largest value and its lowest index (lane level); NaN
+// is flagged.  A lane visits its elements in index order, so a strict >
+// keeps the lowest index of the lane's maximum.
+struct ArgmaxLane {
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+    int nanf = 0;
+};
+
+template <bool BF16, bool EDGE>
+__device__ __forceinline__ void argmax_batch(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW], ArgmaxLane &st)
 {
     constexpr int EPV = RowView<BF16>::EPV;
-    const uint32_t NEG = BF16 ? 0xff80ff80u : 0xff800000u;
-    uint4 raw[UMAX];
+    const int lane = lane_id();
 #pragma unroll
-    for (int j = 0; j < UMAX; ++j) {
-        int64_t vi = vbeg + (int64_t)j * WG + threadIdx.x;
-        if (j < U && vi < rv.nvec) raw[j] = rv.vec[vi];
-        else raw[j] = make_uint4(NEG, NEG, NEG, NEG);
-    }
-    float f[UMAX][EPV];
-    float m = -INFINITY;
+    for (int j = 0; j < UW; ++j) {
+        const int vi = vbeg + j * 64 + lane;
+        float f[EPV];
+        widen<BF16, EDGE>(rv, vi, raw[j], f);
 #pragma unroll
-    for (int j = 0; j < UMAX; ++j) {
-        int64_t vi = vbeg + (int64_t)j * WG + threadIdx.x;
-        unpack<BF16>(raw[j], f[j]);
-        if (rv.edge(vi)) {
+        for (int e = 0; e < EPV; e += 2) st.nanf |= __builtin_isunordered(f[e], f[e + 1]);
+        float m = f[0];
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                int64_t x = rv.elem(vi, e);
-                if (x < 0 || x >= rv.V) f[j][e] = -INFINITY;
-            }
+        for (int e = 1; e < EPV; ++e) m = fmaxf(m, f[e]);
+        if (m > st.best) {
+            // first element of this vector equal to its maximum
+            int found = EPV - 1;
+#pragma unroll
+            for (int e = EPV - 2; e >= 0; --e)
+                if (f[e] == m) found = e;
+            st.best = m;
+            st.bidx = rv.elem(vi, found);
         }
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) m = fmaxf(m, f[j][e]);
     }
-    m_out = m;
-    if (m == -INFINITY) {   // nothing but -inf / masked in this thread
-        // a NaN still has to poison the sum
+}
+
+// Sampled / confidence rows: the lane's running max M and
+// s = sum exp2((v - M) * c32) with c32 = fl(log2(e)/T) (every exponent of the
+// row statistics and of the accept test uses this same fp32 scale, which
+// differs from log2(e)/T by at most 6e-8 relative), s kept in double.  Each
+// term's exponent is one FMA, v*c32 - fl(M*c32); the constant offset
+// delta = M*c32 - fl(M*c32) is exact (FMA residual) and is taken out of every
+// batch sum by the factor 2^-delta = 1 - delta*ln2 + (delta*ln2)^2/2 (|delta|
+// is below 1e-5, so the series is exact in double).  When a batch raises M,
+// s is rescaled once by 2^((M_old - M_new)*c32) (fp32 exp2, within 2 ulp).
+// Terms are summed in fp32 per vector (a short tree) and the vector sums in
+// a second short tree.
+struct LseLane {
+    float M = -INFINITY;
+    float mc = 0.0f;      // fl(M*c32)
+    double corr = 1.0;    // 2^-delta
+    double s = 0.0;
+};
+
+template <bool BF16, bool EDGE>
+__device__ __forceinline__ void lse_batch(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW], float c32,
+                                          LseLane &st)
+{
+    constexpr int EPV = RowView<BF16>::EPV;
+    const int lane = lane_id();
+    float bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < UW; ++j) {
+        float f[EPV];
+        widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) bm = fmaxf(bm, f[e]);
+    }
+    if (bm > st.M) {
+        if (st.M != -INFINITY) st.s *= (double)__builtin_amdgcn_exp2f((st.M - bm) * c32);
+        st.M = bm;
+        st.mc = bm * c32;
+        const double dl = (double)__builtin_fmaf(bm, c32, -st.mc) * LN2;
+        st.corr = 1.0 - dl + 0.5 * dl * dl;
+    }
+    if (st.M == -INFINITY) {
+        // nothing but -inf / masked so far; a NaN must still poison the sum
         int un = 0;
 #pragma unroll
-        for (int j = 0; j < UMAX; ++j)
+        for (int j = 0; j < UW; ++j) {
+            float f[EPV];
+            widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) un |= (f[j][e] != f[j][e]);
-        s_out = un ? (double)NAN : 0.0;
+            for (int e = 0; e < EPV; e += 2) un |= __builtin_isunordered(f[e], f[e + 1]);
+        }
+        if (un) st.s = NAN;
         return;
     }
-    const float mc = m * c32;
-    const float delta = __builtin_fmaf(m, c32, -mc);   // exact: m*c32 - fl(m*c32)
-    double s = 0.0;
+    float vs[UW];
 #pragma unroll
-    for (int j = 0; j < UMAX; ++j) {
+    for (int j = 0; j < UW; ++j) {
+        float f[EPV];
+        widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
         float t[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[j][e], c32, -mc));
+        for (int e = 0; e < EPV; ++e) t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c32, -st.mc));
 #pragma unroll
         for (int w = EPV / 2; w > 0; w >>= 1)
 #pragma unroll
             for (int e = 0; e < w; ++e) t[e] += t[e + w];
-        s += (double)t[0];
+        vs[j] = t[0];
     }
-    // the exponents above are (v - m)*c32 + delta; take delta back out
-    s_out = s * exp2(-(double)delta);
+#pragma unroll
+    for (int w = UW / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int j = 0; j < w; ++j) vs[j] += vs[j + w];
+    st.s += (double)vs[0] * st.corr;
 }
 
-// Merge (m_i, s_i) pairs of log-sum-exp partials into (M, S); s_i is relative
-// to m_i with exponent scale c.  Unusable partials (NaN) poison S.
-__device__ __forceinline__ double lse_rescale(float m_i, double s_i, float M, double cd)
+template <bool BF16, bool LSE, typename State>
+__device__ __forceinline__ void process_batch(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW], float c32,
+                                              State &st)
 {
-    if (m_i == -INFINITY) return (s_i != s_i) ? s_i : 0.0;
-    return s_i * exp2(((double)m_i - (double)M) * cd);
+    if constexpr (LSE) {
+        if (rv.batch_edge(vbeg, WVEC)) lse_batch<BF16, true>(rv, vbeg, raw, c32, st);
+        else lse_batch<BF16, false>(rv, vbeg, raw, c32, st);
+    } else {
+        if (rv.batch_edge(vbeg, WVEC)) argmax_batch<BF16, true>(rv, vbeg, raw, st);
+        else argmax_batch<BF16, false>(rv, vbeg, raw, st);
+    }
+}
+
+// Exponent scale of a row's log-sum-exp statistics.
+__device__ __forceinline__ float c32_of(int kind, float T)
+{
+    return (float)(LOG2E / (double)(kind == KIND_CONF ? 1.0f : T));
+}
+
+// One chunk of one row: the row view and the batches [b0, b1) it covers.  A
+// chunk past the end of a short row (rows whose start is not 16-byte aligned
+// cover one vector more) gets one fully masked batch, so b1 > b0 always.
+template <bool BF16>
+struct Task {
+    RowView<BF16> rv;
+    int r, c, b0, b1;
+    bool lse;
+    float c32;
+};
+
+template <bool BF16>
+__device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl, int64_t t, int cpr, int nb)
+{
+    Task<BF16> k;
+    k.r = (int)(t / cpr);
+    k.c = (int)(t - (int64_t)k.r * cpr);
+    const int b = find_request(pl.row_off, P.B, k.r);
+    const int local = k.r - pl.row_off[b];
+    const int info = pl.info[b];
+    const int d = info & 0xffff, kind = info >> 16;
+    bool is_draft;
+    int kk;
+    if (kind == KIND_GREEDY) { is_draft = false; kk = local; k.lse = false; }
+    else if (kind == KIND_SAMPLED) { is_draft = local >= d; kk = is_draft ? local - d : local; k.lse = true; }
+    else { is_draft = true; kk = local; k.lse = true; }   // KIND_CONF
+    k.c32 = k.lse ? c32_of(kind, pl.T[b]) : 0.0f;
+    const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
+    k.rv = RowView<BF16>((const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4), P.V);
+    const int nbr = (int)ceil_div(k.rv.nvec, WVEC);
+    k.b0 = k.c * nb;
+    k.b1 = std::max(std::min(nbr, k.b0 + nb), k.b0 + 1);
+    return k;
+}
+
+__device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, const LseLane &ls, float c32)
+{
+    Stat st;
+    if (!lse) {
+        const int nanf = wave_or(am.nanf);
+        float best = am.best;
+        int bidx = am.bidx;
+        wave_argmax(best, bidx);
+        st.m = nanf ? NAN : best;
+        st.idx = bidx;
+        st.s = 0.0;
+    } else {
+        const float M = wave_max(ls.M);
+        double sl = 0.0;
+        if (ls.M != -INFINITY) sl = ls.s * (double)__builtin_amdgcn_exp2f((ls.M - M) * c32);
+        else if (ls.s != ls.s) sl = ls.s;
+        st.m = M;
+        st.idx = 0;
+        st.s = wave_sum(sl);
+    }
+    return st;
+}
+
+// Four waves per SIMD (128 VGPRs) keep enough 16-byte loads in flight per CU
+// to cover HBM latency; the register budget fits without spills.
+template <bool BF16>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void row_pass_kernel(Params P)
+{
+    extern __shared__ int plan_smem[];
+    __shared__ int scan_tmp[NWAVE];
+    Plan pl;
+    pl.row_off = plan_smem;
+    pl.info = plan_smem + P.B + 1;
+    pl.T = (float *)(plan_smem + 2 * P.B + 1);
+    make_plan(P, pl, scan_tmp);
+
+    const int R = pl.row_off[P.B];
+    const int64_t nwaves = (int64_t)gridDim.x * NWAVE;
+    int cpr, nb;
+    row_chunking(R, P.V, BF16, nwaves, cpr, nb);
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) {
+            P.ws.meta[0] = cpr;
+            P.ws.meta[1] = nb;
+        }
+        if (P.mode == MODE_SAMPLE)
+            for (int i = threadIdx.x; i < P.B; i += WG) P.ws.s1cnt[i] = 0u;
+    }
+
+    // Static assignment: wave w takes tasks w, w + nwaves, ...  The next
+    // batch -- of this task, or the first of the wave's next task -- is in
+    // flight while the current batch is reduced, so the load stream never
+    // drains at task boundaries.  Partials go out with plain stores; the
+    // finish kernel reads them after the kernel boundary.
+    const int64_t ntask = (int64_t)R * cpr;
+    int64_t t = (int64_t)blockIdx.x * NWAVE + wave_id();
+    if (t >= ntask) return;
+    Task<BF16> cur = make_task<BF16>(P, pl, t, cpr, nb);
+    ArgmaxLane am;
+    LseLane ls;
+    uint4 A[UW], Bv[UW];
+    issue_batch(cur.rv.vec, cur.rv.nvec, cur.b0 * WVEC, A);
+    int i = cur.b0;
+    for (;;) {
+        const bool last = i + 1 >= cur.b1;
+        const int64_t tn = t + nwaves;
+        const bool more = tn < ntask;
+        Task<BF16> nxt = cur;
+        if (last && more) nxt = make_task<BF16>(P, pl, tn, cpr, nb);
+        // next batch: this task's, the next task's first, or (no work left)
+        // a harmless reload of a valid batch
+        const gvec_t nvec_ptr = last ? nxt.rv.vec : cur.rv.vec;
+        const int nnv = last ? nxt.rv.nvec : cur.rv.nvec;
+        const int nvb = last ? nxt.b0 : i + 1;
+        issue_batch(nvec_ptr, nnv, nvb * WVEC, Bv);
+        if (cur.lse) process_batch<BF16, true>(cur.rv, i * WVEC, A, cur.c32, ls);
+        else process_batch<BF16, false>(cur.rv, i * WVEC, A, 0.0f, am);
+        if (last) {
+            const Stat st = finish_task(cur.lse, am, ls, cur.c32);
+            if (lane_id() == 0) P.ws.part[(int64_t)cur.r * P.cpr_max + cur.c] = st;
+            if (!more) break;
+            am = ArgmaxLane();
+            ls = LseLane();
+            cur = nxt;
+            t = tn;
+            i = cur.b0;
+        } else {
+            ++i;
+        }
+#pragma unroll
+        for (int j = 0; j < UW; ++j) A[j] = Bv[j];
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Per-request accept test and first-rejection scan (one wave, lanes over the
-// drafted positions).
+// Accept test and first-rejection scan of one request (one wave, lanes over
+// the drafted positions), from the request's merged row statistics.
 // ---------------------------------------------------------------------------
 
 __device__ void mark_bad_request(const Params &P, int b)
@@ -602,8 +907,11 @@ __device__ __forceinline__ bool stat_bad(const Stat &s, bool lse)
 
 __device__ __forceinline__ bool unif_ok(float u) { return u >= 0.0f && u < 1.0f; }
 
-// One full wave.  rowbase = first active row of request b in the plan.
-__device__ void scan_request(const Params &P, int b, int d, int kind, float T, int rowbase)
+// rows: target rows 0..d (greedy) or target rows 0..d-1 then draft rows
+// 0..d-1 (sampled), in LDS.  Only the workgroup with `write` set publishes
+// the outputs; every caller gets the sampler descriptor.
+__device__ ReqDesc scan_request(const Params &P, int b, int d, int kind, float T, const Stat *rows, bool write,
+                                const double *tab)
 {
     const int K = P.K;
     const int lane = lane_id();
@@ -612,12 +920,9 @@ __device__ void scan_request(const Params &P, int b, int d, int kind, float T, i
     ReqDesc desc = {SREQ_NONE, 0, 0, T};
 
     if (kind == KIND_BAD) {
-        mark_bad_request(P, b);
-        if (P.mode == MODE_SAMPLE && lane == 0) P.ws.req[b] = desc;
-        return;
+        if (write) mark_bad_request(P, b);
+        return desc;
     }
-    const Stat *rows = P.ws.rows + rowbase;
-
     if (kind == KIND_GREEDY) {
         // accept k iff x_k == argmax of target row k; emit argmax of row n
         int n = d;
@@ -638,6 +943,7 @@ __device__ void scan_request(const Params &P, int b, int d, int kind, float T, i
             if (mm && n == d) n = k0 + __builtin_ctzll(mm);
         }
         bad = wave_or(bad);
+        if (!write) return desc;
         if (bad) {
             mark_bad_request(P, b);
         } else {
@@ -652,36 +958,37 @@ __device__ void scan_request(const Params &P, int b, int d, int kind, float T, i
             }
             if (lane == 0) P.num_accepted[b] = n;
         }
-        if (P.mode == MODE_SAMPLE && lane == 0) P.ws.req[b] = desc;
-        return;
+        return desc;
     }
 
-    // Sampled request (T > 0): target rows 0..d-1, then draft rows 0..d-1.
-    // accept k iff u_k < min(1, p_k(x)/q_k(x)), evaluated in double from the
-    // row statistics and the two logits at x.
+    // Sampled request (T > 0): accept k iff u_k < min(1, p_k(x)/q_k(x)), in
+    // double from the row statistics and the two logits at x, with the same
+    // exponent scale c32 as the statistics.
     int bad = unif_ok(P.u_sample[b]) ? 0 : 1;
     int n = d;
-    const double Td = (double)T;
+    const double c2 = (double)c32_of(kind, T);
     const int64_t V = P.V;
     for (int k0 = 0; k0 < d; k0 += 64) {
         const int k = k0 + lane;
         const bool active = k < d;
         bool rej = false;
+        double a = 0.0, c = 0.0;
         if (active) {
             const int x = P.tokens[tb + k];
             const float ua = P.u_accept[tb + k];
             const Stat st = rows[k], sd = rows[d + k];
             const bool lb = (x < 0 || x >= P.V) || !unif_ok(ua) || stat_bad(st, true) || stat_bad(sd, true);
-            double a = 0.0, c = 0.0;
             if (!lb) {
                 const float zx = load_logit_dt(P.target, P.bf16, ((int64_t)b * (K + 1) + k) * V + x);
                 const float yx = load_logit_dt(P.draft, P.bf16, (tb + k) * V + x);
-                a = exp(((double)zx - (double)st.m) / Td) / st.s;
-                c = exp(((double)yx - (double)sd.m) / Td) / sd.s;
+                a = exp2_tab(((double)zx - (double)st.m) * c2, tab) / st.s;
+                c = exp2_tab(((double)yx - (double)sd.m) * c2, tab) / sd.s;
                 const double ratio = (c > 0.0) ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
                 rej = !((double)ua < ratio);
             }
             bad |= lb;
+        }
+        if (write && active) {
             if (P.p_draft) P.p_draft[tb + k] = (float)a;
             if (P.q_draft) P.q_draft[tb + k] = (float)c;
         }
@@ -690,210 +997,83 @@ __device__ void scan_request(const Params &P, int b, int d, int kind, float T, i
     }
     bad = wave_or(bad);
     if (bad) {
-        mark_bad_request(P, b);
-        if (lane == 0) P.ws.req[b] = desc;
-        return;
+        if (write) mark_bad_request(P, b);
+        return desc;
     }
-    for (int k = d + lane; k < K; k += 64) {
-        if (P.p_draft) P.p_draft[tb + k] = 0.0f;
-        if (P.q_draft) P.q_draft[tb + k] = 0.0f;
+    desc.state = (n == d) ? SREQ_BONUS : SREQ_RESID;
+    desc.n = n;
+    if (write) {
+        for (int k = d + lane; k < K; k += 64) {
+            if (P.p_draft) P.p_draft[tb + k] = 0.0f;
+            if (P.q_draft) P.q_draft[tb + k] = 0.0f;
+        }
+        // the emitted token at position n is written by the draw kernel
+        for (int k = lane; k <= K; k += 64) P.out_tokens[ob + k] = (k < n) ? P.tokens[tb + k] : -1;
+        if (lane == 0) P.num_accepted[b] = n;
     }
-    // the emitted token at position n is written by the sampler
-    for (int k = lane; k <= K; k += 64) P.out_tokens[ob + k] = (k < n) ? P.tokens[tb + k] : -1;
-    if (lane == 0) {
-        P.num_accepted[b] = n;
-        desc.state = (n == d) ? SREQ_BONUS : SREQ_RESID;
-        desc.n = n;
-        P.ws.req[b] = desc;
-    }
+    return desc;
 }
 
 // ---------------------------------------------------------------------------
-// Row pass
+// Finish kernel (B)
 // ---------------------------------------------------------------------------
 
-template <bool BF16>
-__device__ void row_task(const Params &P, const Plan &pl, RedSmem &sm, int r, int c, int cpr, int U)
+// s_i (relative to m_i, exponent scale cs) rescaled to M; unusable partials
+// (NaN) poison the sum.
+__device__ __forceinline__ double rescale(float m_i, double s_i, float M, double cs, const double *tab)
 {
-    const int B = P.B, K = P.K, V = P.V;
-    const int b = find_request(pl.row_off, B, r);
-    const int local = r - pl.row_off[b];
-    const int info = pl.info[b];
-    const int d = info & 0xffff, kind = info >> 16;
-    const float T = pl.T[b];
+    if (m_i == -INFINITY) return (s_i != s_i) ? s_i : 0.0;
+    return s_i * exp2_tab(((double)m_i - (double)M) * cs, tab);
+}
 
-    bool is_draft, lse;
-    int k;
-    if (kind == KIND_GREEDY) { is_draft = false; k = local; lse = false; }
-    else if (kind == KIND_SAMPLED) { is_draft = local >= d; k = is_draft ? local - d : local; lse = true; }
-    else { is_draft = true; k = local; lse = true; }   // KIND_CONF
-    const int64_t row = is_draft ? ((int64_t)b * K + k) : ((int64_t)b * (K + 1) + k);
-    const char *row_start = (const char *)(is_draft ? P.draft : P.target) + row * (int64_t)V * (BF16 ? 2 : 4);
-    const RowView<BF16> rv(row_start, V);
-    const int64_t vbeg = (int64_t)c * U * WG;
-
-    const double cd = LOG2E / (double)(kind == KIND_CONF ? 1.0f : T);
+// Merge n chunk partials of one row (one thread, from LDS).
+__device__ Stat merge_chunks(const Stat *q, int n, bool lse, double cs, const double *tab)
+{
     Stat st;
     if (!lse) {
-        float best;
-        int bidx, nanf;
-        chunk_argmax<BF16>(rv, vbeg, U, best, bidx, nanf);
-        nanf = wg_or(nanf, sm);
-        wg_argmax(best, bidx, sm);
-        st.m = nanf ? NAN : best;
-        st.idx = bidx;
+        float m = -INFINITY;
+        int i = 0x7fffffff, nanf = 0;
+        for (int j = 0; j < n; ++j) {
+            const Stat p = q[j];
+            if (!(p.m == p.m)) nanf = 1;
+            else argmax_merge(m, i, p.m, p.idx);
+        }
+        st.m = nanf ? NAN : m;
+        st.idx = i;
         st.s = 0.0;
     } else {
-        float m;
-        double s;
-        chunk_lse<BF16>(rv, vbeg, U, (float)cd, m, s);
-        const float M = wg_max(m, sm);
-        const double S = wg_sum(lse_rescale(m, s, M, cd), sm);
+        float M = -INFINITY;
+        double S = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const Stat p = q[j];
+            if (p.m > M) {
+                S = rescale(M, S, p.m, cs, tab) + p.s;
+                M = p.m;
+            } else {
+                S += rescale(p.m, p.s, M, cs, tab);
+            }
+        }
         st.m = M;
         st.idx = 0;
         st.s = S;
     }
-
-    __shared__ int sh_last;
-    if (cpr > 1) {
-        if (threadIdx.x == 0) {
-            P.ws.part[(int64_t)r * P.cpr_max + c] = st;
-            fence_release();
-            const uint32_t old = atomic_inc_agent(&P.ws.row_cnt[r]);
-            sh_last = (old == (uint32_t)(cpr - 1));
-        }
-        __syncthreads();
-        const int last = sh_last;
-        __syncthreads();
-        if (!last) return;
-        if (wave_id() != 0) return;
-        // merge the chunk partials of row r (wave 0)
-        fence_acquire();
-        const Stat *pp = P.ws.part + (int64_t)r * P.cpr_max;
-        if (!lse) {
-            float m = -INFINITY;
-            int i = 0x7fffffff, nanf = 0;
-            for (int j = lane_id(); j < cpr; j += 64) {
-                const Stat s = pp[j];
-                if (!(s.m == s.m)) nanf = 1;
-                else argmax_merge(m, i, s.m, s.idx);
-            }
-            wave_argmax(m, i);
-            nanf = wave_or(nanf);
-            st.m = nanf ? NAN : m;
-            st.idx = i;
-            st.s = 0.0;
-        } else {
-            float M = -INFINITY;
-            for (int j = lane_id(); j < cpr; j += 64) M = fmaxf(M, pp[j].m);
-            M = wave_max(M);
-            double S = 0.0;
-            for (int j = lane_id(); j < cpr; j += 64) S += lse_rescale(pp[j].m, pp[j].s, M, cd);
-            st.m = M;
-            st.idx = 0;
-            st.s = wave_sum(S);
-        }
-        if (lane_id() == 0) {
-            P.ws.rows[r] = st;
-            store_zero_agent(&P.ws.row_cnt[r]);
-        }
-    } else {
-        if (wave_id() != 0) return;
-        if (lane_id() == 0) P.ws.rows[r] = st;
-    }
-
-    // Row r is complete (wave 0 only from here on).
-    if (kind == KIND_CONF) {
-        if (lane_id() == 0)
-            P.conf[(int64_t)b * K + k] = stat_bad(st, true) ? NAN : (float)(1.0 / st.s);
-        return;
-    }
-    const int nrows = pl.row_off[b + 1] - pl.row_off[b];
-    int lastreq = 0;
-    if (lane_id() == 0) {
-        fence_release();
-        const uint32_t old = atomic_inc_agent(&P.ws.req_cnt[b]);
-        lastreq = (old == (uint32_t)(nrows - 1));
-    }
-    lastreq = __shfl(lastreq, 0, 64);
-    if (!lastreq) return;
-    fence_acquire();
-    if (lane_id() == 0) store_zero_agent(&P.ws.req_cnt[b]);
-    scan_request(P, b, d, kind, T, pl.row_off[b]);
+    return st;
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(WG) void row_stats_kernel(Params P)
-{
-    extern __shared__ int plan_smem[];
-    __shared__ RedSmem sm;
-    __shared__ int scan_tmp[NWAVE];
-    Plan pl;
-    pl.row_off = plan_smem;
-    pl.info = plan_smem + P.B + 1;
-    pl.T = (float *)(plan_smem + 2 * P.B + 1);
-    make_plan(P, pl, scan_tmp);
-
-    const int B = P.B, K = P.K;
-    const int R = pl.row_off[B];
-
-    // Requests with no rows in the pass (bad plan, sampled with depth 0,
-    // confidence with K_b = 0) and confidence entries beyond K_b are
-    // finished here by workgroup 0.
-    if (blockIdx.x == 0 && wave_id() == 0) {
-        for (int b = 0; b < B; ++b) {
-            const int info = pl.info[b];
-            const int d = info & 0xffff, kind = info >> 16;
-            if (P.mode == MODE_CONF) {
-                for (int k = lane_id(); k < K; k += 64)
-                    if (kind == KIND_BAD || k >= d) P.conf[(int64_t)b * K + k] = (kind == KIND_BAD) ? NAN : 0.0f;
-            } else if (pl.row_off[b + 1] == pl.row_off[b]) {
-                scan_request(P, b, d, kind, pl.T[b], pl.row_off[b]);
-            }
-        }
-    }
-
-    // Chunking: 16-byte loads per thread U in {8,4,2,1}; smaller when the
-    // batch has too few rows to give every workgroup two tasks.
-    constexpr int EPV = BF16 ? 8 : 4;
-    const int64_t nv = nvec_max(P.V, EPV);
-    const int u_lo = (int)ceil_div(nv, (int64_t)WG * CPR_CAP);
-    int U = UMAX;
-    while (U > 1 && U > u_lo && (int64_t)R * ceil_div(nv, (int64_t)WG * U) < 2 * (int64_t)gridDim.x) U >>= 1;
-    if (U < u_lo) U = u_lo;
-    const int cpr = (int)ceil_div(nv, (int64_t)WG * U);
-    const int64_t ntask = (int64_t)R * cpr;
-    for (int64_t t = blockIdx.x; t < ntask; t += gridDim.x) {
-        const int r = (int)(t / cpr);
-        const int c = (int)(t - (int64_t)r * cpr);
-        row_task<BF16>(P, pl, sm, r, c, cpr, U);
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Sampler.  A sampled request draws one token from one row pair: after a
-// rejection at n, r = max(0, p_n - q_n); without one, r = p_d.  Both kernels
-// split that row pair into chunks of US*WG vectors, one workgroup each, and
-// work in fp64 throughout (terms, sums, prefix scan): the draw compares u*R
-// against prefix sums over V terms, and fp32 terms would move the result
-// for about one draw in a thousand.
-// ---------------------------------------------------------------------------
-
-template <bool BF16>
-__device__ __forceinline__ void load_sampler_chunk(const RowView<BF16> &rv, int64_t vbeg, float (&f)[US][RowView<BF16>::EPV], int &flag)
+__device__ __forceinline__ void load_sampler_chunk(const RowView<BF16> &rv, int vbeg, float (&f)[US][RowView<BF16>::EPV],
+                                                   int &flag)
 {
     constexpr int EPV = RowView<BF16>::EPV;
-    const uint32_t NEG = BF16 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
     for (int j = 0; j < US; ++j) {
-        const int64_t vi = vbeg + (int64_t)j * WG + threadIdx.x;
-        const uint4 raw = (vi < rv.nvec) ? rv.vec[vi] : make_uint4(NEG, NEG, NEG, NEG);
+        const int vi = vbeg + j * WG + (int)threadIdx.x;
+        const uint4 raw = ld_plain(rv.vec + min(vi, rv.nvec - 1));
         unpack<BF16>(raw, f[j]);
-        if (rv.edge(vi)) {
+        if (vi >= rv.nvec || rv.edge(vi)) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                const int64_t x = rv.elem(vi, e);
+                const int x = rv.elem(vi, e);
                 if (x < 0 || x >= rv.V) f[j][e] = -INFINITY;
             }
         }
@@ -902,22 +1082,83 @@ __device__ __forceinline__ void load_sampler_chunk(const RowView<BF16> &rv, int6
     }
 }
 
+// Workgroup (b, c): merge request b's rows, run its accept scan (workgroup
+// c == 0 publishes the outputs), then for a request that draws a token,
+// reduce chunk c of the drawn row pair to fp64 (max, sum of exp2) per row; the
+// last chunk to finish combines the request's normalisers.
 template <bool BF16>
-__global__ __launch_bounds__(WG) void sampler_sums_kernel(Params P)
+__global__ __launch_bounds__(WG) void finish_kernel(Params P)
 {
     constexpr int EPV = RowView<BF16>::EPV;
+    extern __shared__ Stat rows_s[];   // [2K + 1] merged row statistics of request b
+    __shared__ double tab[EXP2_TAB];
+    __shared__ Stat stage[STAGE];
     __shared__ RedSmem sm;
+    __shared__ int sh_pre[NWAVE];
+    __shared__ ReqDesc sh_desc;
     __shared__ int sh_last;
-    const int b = blockIdx.y, c = blockIdx.x;
-    const ReqDesc desc = P.ws.req[b];
+    const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+    init_exp2_table(tab);
+
+    // first active row of request b: rows of the requests before it
+    int pre = 0;
+    for (int j = tid; j < b; j += WG) pre += plan_request(P, j).rows;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pre += __shfl_xor(pre, o, 64);
+    if (lane_id() == 0) sh_pre[wave_id()] = pre;
+    __syncthreads();
+    pre = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) pre += sh_pre[w];
+
+    const ReqPlan q = plan_request(P, b);
+    const int cpr = P.ws.meta[0];
+    const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF;
+    const double cs = lse ? (double)c32_of(q.kind, q.T) : 0.0;
+    const int grp = std::max(1, std::min(WG, STAGE / cpr));
+    for (int g0 = 0; g0 < q.rows; g0 += grp) {
+        const int gn = std::min(grp, q.rows - g0);
+        __syncthreads();
+        for (int i = tid; i < gn * cpr; i += WG) {
+            const int rr = i / cpr, jj = i - rr * cpr;
+            stage[i] = P.ws.part[(int64_t)(pre + g0 + rr) * P.cpr_max + jj];
+        }
+        __syncthreads();
+        if (tid < gn) rows_s[g0 + tid] = merge_chunks(stage + tid * cpr, cpr, lse, cs, tab);
+    }
+    __syncthreads();
+
+    if (P.mode == MODE_CONF) {
+        for (int k = tid; k < P.K; k += WG) {
+            float v;
+            if (q.kind == KIND_BAD) v = NAN;
+            else if (k >= q.d) v = 0.0f;
+            else v = stat_bad(rows_s[k], true) ? NAN : (float)(1.0 / rows_s[k].s);
+            P.conf[(int64_t)b * P.K + k] = v;
+        }
+        return;
+    }
+    if (wave_id() == 0) {
+        const ReqDesc d = scan_request(P, b, q.d, q.kind, q.T, rows_s, c == 0, tab);
+        if (lane_id() == 0) sh_desc = d;
+    }
+    __syncthreads();
+    const ReqDesc desc = sh_desc;
+    if (P.mode != MODE_SAMPLE) return;
+    if (c == 0 && tid == 0) {
+        P.ws.req[b] = desc;
+        P.ws.s2cnt[b] = 0u;
+    }
     if (desc.state == SREQ_NONE) return;
+
+    // fp64 normalisers of the drawn row pair (chunk c): local max, then
+    // sum exp2((v - max) * cd) with cd = log2(e)/T in double.
     const bool resid = desc.state == SREQ_RESID;
     const int K = P.K, V = P.V;
     const int64_t esz = BF16 ? 2 : 4;
-    const double invT = 1.0 / (double)desc.T;
+    const double cd = LOG2E / (double)desc.T;
     const RowView<BF16> rz((const char *)P.target + ((int64_t)b * (K + 1) + desc.n) * V * esz, V);
-    const int64_t vbeg = (int64_t)c * US * WG;
-
+    const int vbeg = c * US * WG;
     int flag = 0;
     float f[US][EPV];
     load_sampler_chunk<BF16>(rz, vbeg, f, flag);
@@ -932,7 +1173,7 @@ __global__ __launch_bounds__(WG) void sampler_sums_kernel(Params P)
 #pragma unroll
         for (int j = 0; j < US; ++j)
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) s += exp(((double)f[j][e] - (double)mz) * invT);
+            for (int e = 0; e < EPV; ++e) s += exp2_tab(((double)f[j][e] - (double)mz) * cd, tab);
     }
     const double sz = wg_sum(s, sm);
     float my = 0.0f;
@@ -952,118 +1193,122 @@ __global__ __launch_bounds__(WG) void sampler_sums_kernel(Params P)
 #pragma unroll
             for (int j = 0; j < US; ++j)
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) s += exp(((double)f[j][e] - (double)my) * invT);
+                for (int e = 0; e < EPV; ++e) s += exp2_tab(((double)f[j][e] - (double)my) * cd, tab);
         }
         sy = wg_sum(s, sm);
     }
     flag = wg_or(flag, sm);
 
-    if (threadIdx.x == 0) {
-        S1Part part = {mz, my, flag, 0, sz, sy};
-        P.ws.s1[(int64_t)b * P.cs + c] = part;
-        fence_release();
-        const uint32_t old = atomic_inc_agent(&P.ws.s1cnt[b]);
+    if (tid == 0) {
+        const S1Part part = {mz, my, flag, 0, sz, sy};
+        put_s1(P.ws.s1 + (int64_t)b * P.cs + c, part);
+        wait_stores();
+        const uint32_t old = count_in(&P.ws.s1cnt[b]);
         sh_last = (old == (uint32_t)(P.cs - 1));
     }
     __syncthreads();
     if (!sh_last || wave_id() != 0) return;
-    fence_acquire();
+    after_count();
     const S1Part *pp = P.ws.s1 + (int64_t)b * P.cs;
     float Mz = -INFINITY, My = -INFINITY;
     int bad = 0;
     for (int j = lane_id(); j < P.cs; j += 64) {
-        const S1Part q = pp[j];
-        Mz = fmaxf(Mz, q.mz);
-        My = fmaxf(My, q.my);
-        bad |= q.bad;
+        const S1Part x = get_s1(pp + j);
+        Mz = fmaxf(Mz, x.mz);
+        My = fmaxf(My, x.my);
+        bad |= x.bad;
     }
     Mz = wave_max(Mz);
     My = wave_max(My);
     double Sz = 0.0, Sy = 0.0;
     for (int j = lane_id(); j < P.cs; j += 64) {
-        const S1Part q = pp[j];
-        if (q.mz != -INFINITY) Sz += q.sz * exp(((double)q.mz - (double)Mz) * invT);
-        if (resid && q.my != -INFINITY) Sy += q.sy * exp(((double)q.my - (double)My) * invT);
+        const S1Part x = get_s1(pp + j);
+        if (x.mz != -INFINITY) Sz += x.sz * exp2_tab(((double)x.mz - (double)Mz) * cd, tab);
+        if (resid && x.my != -INFINITY) Sy += x.sy * exp2_tab(((double)x.my - (double)My) * cd, tab);
     }
     Sz = wave_sum(Sz);
     Sy = wave_sum(Sy);
     bad = wave_or(bad);
-    // only the bonus row is new to this call; residual rows were checked in
-    // the row pass, so `bad` can only come from target row d
+    // Residual rows were checked by the row pass; a flag here can only come
+    // from the bonus row (target row d), which only this draw reads.
     bad |= (Mz == -INFINITY || Mz == INFINITY || !(Sz > 0.0));
     if (resid) bad |= (My == -INFINITY || My == INFINITY || !(Sy > 0.0));
     if (lane_id() == 0) {
-        S1Part tot = {Mz, My, bad, 0, Sz, Sy};
+        const S1Part tot = {Mz, My, bad, 0, Sz, Sy};
         P.ws.s1tot[b] = tot;
-        store_zero_agent(&P.ws.s1cnt[b]);
     }
-    if (bad) mark_bad_request(P, b);
 }
 
-// Exclusive scan of one double per thread over the workgroup, in thread order.
-__device__ double wg_excl_scan(double v, double *sm4, double &total)
-{
-    const int lane = lane_id();
-    double incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
-    double excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0;
-    __syncthreads();
-    if (lane == 63) sm4[wave_id()] = incl;
-    __syncthreads();
-    double wb = 0.0, tot = 0.0;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-        if (w < wave_id()) wb += sm4[w];
-        tot += sm4[w];
-    }
-    total = tot;
-    return wb + excl;
-}
+// ---------------------------------------------------------------------------
+// Draw kernel (C): one token per sampled request from one row pair, in fp64.
+//   after a rejection at n: r = max(0, p_n - q_n)   (p_n if that has no mass)
+//   without one:            r = p_d
+// The draw compares u*R against prefix sums over V terms; fp32 terms would
+// move the drawn token for about one draw in a thousand.
+// ---------------------------------------------------------------------------
 
-// Sampler terms of one chunk, in fp64.  which: 0 = residual max(0, p - q),
-// 1 = target distribution p.  Values are written per (slot j, element e).
+// Sampler terms of one chunk.  which: 0 = residual max(0, p - q), 1 = p.
+// psum[j] receives the sum of p over slot j's elements, in element order.
 template <bool BF16>
-__device__ void sampler_terms(const Params &P, int b, const ReqDesc &desc, const S1Part &tot, int64_t vbeg,
-                              int which, double (&val)[US][RowView<BF16>::EPV])
+__device__ void sampler_terms(const Params &P, int b, const ReqDesc &desc, const S1Part &tot, int vbeg, int which,
+                              const double *tab, double (&val)[US][RowView<BF16>::EPV], double (&psum)[US])
 {
     constexpr int EPV = RowView<BF16>::EPV;
     const int K = P.K, V = P.V;
     const int64_t esz = BF16 ? 2 : 4;
-    const double invT = 1.0 / (double)desc.T;
+    const double cd = LOG2E / (double)desc.T;
     const double invSz = 1.0 / tot.sz;
     int flag = 0;
     float f[US][EPV];
     const RowView<BF16> rz((const char *)P.target + ((int64_t)b * (K + 1) + desc.n) * V * esz, V);
     load_sampler_chunk<BF16>(rz, vbeg, f, flag);
 #pragma unroll
-    for (int j = 0; j < US; ++j)
+    for (int j = 0; j < US; ++j) {
+        double ps = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) val[j][e] = exp(((double)f[j][e] - (double)tot.mz) * invT) * invSz;
+        for (int e = 0; e < EPV; ++e) {
+            val[j][e] = exp2_tab(((double)f[j][e] - (double)tot.mz) * cd, tab) * invSz;
+            ps += val[j][e];
+        }
+        psum[j] = ps;
+    }
     if (which == 0) {
         const double invSy = 1.0 / tot.sy;
-        const RowView<BF16> ry((const char *)P.draft + ((int64_t)b * K + desc.n) * V * esz, V);
-        load_sampler_chunk<BF16>(ry, vbeg, f, flag);
+        const char *yrow = (const char *)P.draft + ((int64_t)b * K + desc.n) * V * esz;
+        const RowView<BF16> ry(yrow, V);
+        if (ry.head == rz.head) {
+            load_sampler_chunk<BF16>(ry, vbeg, f, flag);   // same vector grid: same tokens per lane
+        } else {
+            // The two rows start at different offsets within a 16-byte vector
+            // (V * element size is not a multiple of 16): read the draft by
+            // token index on the target row's grid.
+#pragma unroll
+            for (int j = 0; j < US; ++j) {
+                const int vi = vbeg + j * WG + (int)threadIdx.x;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const int x = rz.elem(vi, e);
+                    f[j][e] = (x >= 0 && x < V) ? load_logit<BF16>(yrow, x) : -INFINITY;
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < US; ++j)
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                const double q = exp(((double)f[j][e] - (double)tot.my) * invT) * invSy;
-                const double dlt = val[j][e] - q;
+                const double qv = exp2_tab(((double)f[j][e] - (double)tot.my) * cd, tab) * invSy;
+                const double dlt = val[j][e] - qv;
                 val[j][e] = dlt > 0.0 ? dlt : 0.0;
             }
     }
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(WG) void sampler_draw_kernel(Params P)
+__global__ __launch_bounds__(WG) void draw_kernel(Params P)
 {
     constexpr int EPV = RowView<BF16>::EPV;
     constexpr int CS_LDS = 512;
+    __shared__ double tab[EXP2_TAB];
     __shared__ double sm4[NWAVE];
     __shared__ int sh_last;
     __shared__ S2Part parts[CS_LDS];
@@ -1074,54 +1319,47 @@ __global__ __launch_bounds__(WG) void sampler_draw_kernel(Params P)
     const ReqDesc desc = P.ws.req[b];
     if (desc.state == SREQ_NONE) return;
     const S1Part tot = P.ws.s1tot[b];
-    if (tot.bad) return;
+    if (tot.bad) {   // the bonus row holds NaN, +inf or nothing but -inf
+        if (c == 0 && wave_id() == 0) mark_bad_request(P, b);
+        return;
+    }
+    init_exp2_table(tab);
     const bool resid = desc.state == SREQ_RESID;
-    const int64_t vbeg_own = (int64_t)c * US * WG;
+    const int vbeg_own = c * US * WG;
 
     // chunk totals of r (and of p, for the all-zero-residual fallback)
-    double val[US][EPV];
+    // (summed in the same order as the rescan below, so the chunk located
+    // from these totals is the one the rescan walks)
+    double val[US][EPV], psum[US];
     double total_r = 0.0, total_p = 0.0;
-    {
-        sampler_terms<BF16>(P, b, desc, tot, vbeg_own, resid ? 0 : 1, val);
-        double carry = 0.0;
+    sampler_terms<BF16>(P, b, desc, tot, vbeg_own, resid ? 0 : 1, tab, val, psum);
 #pragma unroll
-        for (int j = 0; j < US; ++j) {
-            double vs = 0.0;
+    for (int j = 0; j < US; ++j) {
+        double vs = 0.0;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) vs += val[j][e];
-            double t;
-            (void)wg_excl_scan(vs, sm4, t);
-            carry += t;
+        for (int e = 0; e < EPV; ++e) vs += val[j][e];
+        double t;
+        (void)wg_excl_scan(vs, sm4, t);
+        total_r += t;
+        if (resid) {
+            (void)wg_excl_scan(psum[j], sm4, t);
+            total_p += t;
         }
-        total_r = carry;
     }
-    if (resid) {
-        sampler_terms<BF16>(P, b, desc, tot, vbeg_own, 1, val);
-        double carry = 0.0;
-#pragma unroll
-        for (int j = 0; j < US; ++j) {
-            double vs = 0.0;
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) vs += val[j][e];
-            double t;
-            (void)wg_excl_scan(vs, sm4, t);
-            carry += t;
-        }
-        total_p = carry;
-    }
+    if (!resid) total_p = total_r;   // the bonus draw's distribution is p itself
     if (threadIdx.x == 0) {
-        S2Part part = {total_r, total_p};
-        P.ws.s2[(int64_t)b * P.cs + c] = part;
-        fence_release();
-        const uint32_t old = atomic_inc_agent(&P.ws.s2cnt[b]);
+        const S2Part part = {total_r, total_p};
+        put_s2(P.ws.s2 + (int64_t)b * P.cs + c, part);
+        wait_stores();
+        const uint32_t old = count_in(&P.ws.s2cnt[b]);
         sh_last = (old == (uint32_t)(P.cs - 1));
     }
     __syncthreads();
     if (!sh_last) return;
-    fence_acquire();
+    after_count();
 
     // Last chunk of request b: locate u*R among the chunk totals.
-    for (int j = threadIdx.x; j < P.cs; j += WG) parts[j] = P.ws.s2[(int64_t)b * P.cs + j];
+    for (int j = threadIdx.x; j < P.cs; j += WG) parts[j] = get_s2(P.ws.s2 + (int64_t)b * P.cs + j);
     __syncthreads();
     if (threadIdx.x == 0) {
         double R = 0.0;
@@ -1152,17 +1390,16 @@ __global__ __launch_bounds__(WG) void sampler_draw_kernel(Params P)
     const int cs = sh_c;
     if (cs < 0) {   // no chunk holds positive mass (unreachable for valid statistics)
         if (threadIdx.x < 64) mark_bad_request(P, b);
-        if (threadIdx.x == 0) store_zero_agent(&P.ws.s2cnt[b]);
         return;
     }
     const double base = sh_base, target = sh_target;
     const int which = sh_which;
     const bool over = sh_over;
-    const int64_t vbeg = (int64_t)cs * US * WG;
+    const int vbeg = cs * US * WG;
 
     // Rescan chunk cs: first positive-mass element whose prefix exceeds
     // u*R; the chunk's last positive-mass element if none does.
-    sampler_terms<BF16>(P, b, desc, tot, vbeg, which, val);
+    sampler_terms<BF16>(P, b, desc, tot, vbeg, which, tab, val, psum);
     const RowView<BF16> rz((const char *)P.target + ((int64_t)b * (P.K + 1) + desc.n) * P.V * (BF16 ? 2 : 4), P.V);
     int first = 0x7fffffff, lastp = -1;
     double carry = 0.0;
@@ -1174,41 +1411,35 @@ __global__ __launch_bounds__(WG) void sampler_draw_kernel(Params P)
         double t;
         const double ex = wg_excl_scan(vs, sm4, t);
         const double slot0 = carry + ex;
-        const int64_t vi = vbeg + (int64_t)j * WG + threadIdx.x;
+        const int vi = vbeg + j * WG + (int)threadIdx.x;
         double part = 0.0;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             part += val[j][e];
-            const int64_t x = rz.elem(vi, e);
+            const int x = rz.elem(vi, e);
             if (val[j][e] > 0.0 && x >= 0 && x < P.V) {
-                if (x > lastp) lastp = (int)x;
-                if (first == 0x7fffffff && base + (slot0 + part) > target) first = (int)x;
+                if (x > lastp) lastp = x;
+                if (first == 0x7fffffff && base + (slot0 + part) > target) first = x;
             }
         }
         carry += t;
     }
-    // workgroup min of `first`, max of `lastp`
-    float dummy = 0.0f;
-    int fi = first;
+    int fi, lp;
     {
-        // min via argmax merge on negated index
-        float m = (fi == 0x7fffffff) ? -INFINITY : 0.0f;
-        int i = fi;
-        (void)dummy;
-        wg_argmax(m, i, sm);
+        float m = (first == 0x7fffffff) ? -INFINITY : 0.0f;
+        int i = first;
+        wg_argmax(m, i, sm);   // lowest index among threads holding a candidate
         fi = (m == -INFINITY) ? 0x7fffffff : i;
     }
-    int lp;
     {
         float m = (lastp < 0) ? -INFINITY : 0.0f;
         int i = (lastp < 0) ? 0x7fffffff : (0x7fffffff - lastp);
-        wg_argmax(m, i, sm);
+        wg_argmax(m, i, sm);   // highest index among threads holding one
         lp = (m == -INFINITY) ? -1 : (0x7fffffff - i);
     }
     if (threadIdx.x == 0) {
         const int tok = (!over && fi != 0x7fffffff) ? fi : lp;
         P.out_tokens[(int64_t)b * (P.K + 1) + desc.n] = tok;
-        store_zero_agent(&P.ws.s2cnt[b]);
     }
 }
 
@@ -1224,7 +1455,8 @@ __device__ __forceinline__ float sanitize_conf(float c)
 
 __device__ int block_sum_int(int v, int *sm32)
 {
-    v = __reduce_add_sync(0xffffffffffffffffull, v);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     __syncthreads();
     if (lane_id() == 0) sm32[wave_id()] = v;
     __syncthreads();
@@ -1252,59 +1484,65 @@ __device__ int block_excl_scan_int(int v, int *sm32)
     return wb + incl - v;
 }
 
+// keys[b*K + k]: 0 = not a candidate (k = 0, k >= K_b, invalid K_b), else the
+// float bits of the running product c_{b,k} plus 1 (the products lie in
+// [0, 1], so their bits order like their values).
 __global__ __launch_bounds__(DCUT_WG) void dcut_kernel(const float *conf, const int32_t *max_depth, int B, int K,
                                                       int budget, int32_t *depth_out)
 {
-    extern __shared__ uint32_t keys[];   // [B*K]: 0 = not a candidate, else float bits of c + 1
+    extern __shared__ uint32_t keys[];   // [B*K]
     __shared__ int hist[256];
     __shared__ int sm32[DCUT_WG / 64];
     __shared__ uint32_t sh_prefix;
     __shared__ int sh_kr;
-    const int per = (int)ceil_div(B, DCUT_WG);
-    const int b0 = threadIdx.x * per;
+    const int n = B * K;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < n; i += DCUT_WG) keys[i] = __float_as_uint(conf[i]);
+    __syncthreads();
     int floors = 0, cands = 0;
-    for (int j = 0; j < per; ++j) {
-        const int b = b0 + j;
-        if (b >= B) break;
+    for (int b = tid; b < B; b += DCUT_WG) {
         const int Kb = max_depth ? max_depth[b] : K;
         const bool valid = Kb >= 0 && Kb <= K;
         float c = 0.0f;
         for (int k = 0; k < K; ++k) {
             uint32_t key = 0;
             if (valid && k < Kb) {
-                const float s = sanitize_conf(conf[(int64_t)b * K + k]);
+                const float s = sanitize_conf(__uint_as_float(keys[b * K + k]));
                 c = (k == 0) ? s : c * s;
                 if (k >= 1) key = __float_as_uint(c) + 1u;
             }
-            keys[(int64_t)b * K + k] = key;
+            keys[b * K + k] = key;
         }
         if (valid) {
             floors += Kb > 0 ? 1 : 0;
             cands += Kb > 1 ? Kb - 1 : 0;
         }
     }
+    __syncthreads();
     floors = block_sum_int(floors, sm32);
     cands = block_sum_int(cands, sm32);
     int take = budget - floors;
     if (take > cands) take = cands;
     if (take < 0) take = 0;
 
+    // each thread owns the contiguous flat range [lo, hi)
+    const int per = (int)ceil_div(n, DCUT_WG);
+    const int lo = std::min(n, tid * per), hi = std::min(n, lo + per);
+
     // radix select of the take-th largest key, 8 bits at a time
     uint32_t prefix = 0;
     int kr = take;
     if (take > 0) {
         for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int i = threadIdx.x; i < 256; i += DCUT_WG) hist[i] = 0;
+            for (int i = tid; i < 256; i += DCUT_WG) hist[i] = 0;
             __syncthreads();
             const uint32_t hmask = (shift == 24) ? 0u : (0xffffffffu << (shift + 8));
-            for (int j = 0; j < per * K; ++j) {
-                const int64_t fi = (int64_t)b0 * K + j;
-                if (fi >= (int64_t)B * K) break;
-                const uint32_t key = keys[fi];
+            for (int i = lo; i < hi; ++i) {
+                const uint32_t key = keys[i];
                 if (key != 0 && (key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 255u], 1);
             }
             __syncthreads();
-            if (threadIdx.x == 0) {
+            if (tid == 0) {
                 int acc = 0, digit = 0;
                 for (int bin = 255; bin >= 0; --bin) {
                     if (acc + hist[bin] >= kr) { digit = bin; break; }
@@ -1319,31 +1557,29 @@ __global__ __launch_bounds__(DCUT_WG) void dcut_kernel(const float *conf, const 
             __syncthreads();
         }
     }
-    // entries above the threshold are taken; ties at the threshold go in
-    // flat-index order (threads own contiguous flat ranges)
-    const uint32_t thr = (take > 0) ? prefix : 0xffffffffu;
+    // Entries above the threshold are taken; ties at the threshold go in
+    // flat-index order.  Taken entries are marked 1 in place.
+    const uint32_t thr = prefix;
     int eq = 0;
-    for (int j = 0; j < per * K; ++j) {
-        const int64_t fi = (int64_t)b0 * K + j;
-        if (fi >= (int64_t)B * K) break;
-        eq += (keys[fi] == thr && take > 0);
-    }
+    if (take > 0)
+        for (int i = lo; i < hi; ++i) eq += (keys[i] == thr);
     int rank = block_excl_scan_int(eq, sm32);
-    for (int j = 0; j < per; ++j) {
-        const int b = b0 + j;
-        if (b >= B) break;
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t key = keys[i];
+        int taken = 0;
+        if (take > 0 && key != 0) {
+            if (key > thr) taken = 1;
+            else if (key == thr) taken = (rank++ < kr);
+        }
+        keys[i] = (uint32_t)taken;
+    }
+    __syncthreads();
+    for (int b = tid; b < B; b += DCUT_WG) {
         const int Kb = max_depth ? max_depth[b] : K;
         const bool valid = Kb >= 0 && Kb <= K;
         int dep = valid ? (Kb > 0 ? 1 : 0) : -1;
-        for (int k = 0; k < K; ++k) {
-            const uint32_t key = keys[(int64_t)b * K + k];
-            if (key == 0 || take == 0) continue;
-            if (key > thr) ++dep;
-            else if (key == thr) {
-                if (rank < kr) ++dep;
-                ++rank;
-            }
-        }
+        if (valid)
+            for (int k = 0; k < K; ++k) dep += (int)keys[b * K + k];
         depth_out[b] = dep;
     }
 }
@@ -1351,6 +1587,19 @@ __global__ __launch_bounds__(DCUT_WG) void dcut_kernel(const float *conf, const 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+
+thread_local char g_last_error[256] = "";
+
+sv_status hip_status(const char *what)
+{
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+        g_last_error[0] = 0;
+        return SV_OK;
+    }
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+    return SV_ERR_HIP;
+}
 
 constexpr int MAX_DEVICES = 64;
 std::atomic<int> g_cu_count[MAX_DEVICES];
@@ -1367,8 +1616,49 @@ int cu_count()
     return n;
 }
 
-// Workgroups of the persistent row pass per compute unit.
-int g_row_wgs_per_cu = 8;
+// Resident workgroups of the persistent row pass per compute unit (from the
+// occupancy calculator; the grid never exceeds what can run at once, so the
+// static task assignment stays balanced).
+int row_wgs_per_cu(bool bf16, size_t lds)
+{
+    static std::atomic<int> cache[2][64];
+    const int bucket = (int)std::min<size_t>(63, lds / 1024);
+    int n = cache[bf16][bucket].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        const void *fn = bf16 ? (const void *)row_pass_kernel<true> : (const void *)row_pass_kernel<false>;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, WG, (bucket + 1) * 1024) != hipSuccess || n <= 0)
+            n = 2;
+        cache[bf16][bucket].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The D-cut keys live in dynamic LDS (up to 128 KiB; gfx950 gives a
+// workgroup up to 160 KiB).  Checked against the device's limit, with the
+// kernel's dynamic-LDS ceiling raised once per device.
+bool dcut_lds_ok(size_t dyn)
+{
+    static std::atomic<int> limit[MAX_DEVICES];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return false;
+    int lim = limit[dev].load(std::memory_order_relaxed);
+    if (lim <= 0) {
+        if (hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lim <= 0)
+            lim = 65536;
+        lim -= 4096;   // the kernel's static LDS, with room to spare
+        if (hipFuncSetAttribute((const void *)dcut_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lim) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            lim = 65536 - 4096;
+        }
+        limit[dev].store(lim, std::memory_order_relaxed);
+    }
+    if (dyn > (size_t)lim) {
+        snprintf(g_last_error, sizeof g_last_error, "dcut_allocate: %zu bytes of keys exceed this device's LDS", dyn);
+        return false;
+    }
+    return true;
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -1385,30 +1675,30 @@ sv_status check_ws(void *ws, size_t ws_bytes, const Layout &L)
     return SV_OK;
 }
 
-sv_status launch_rows(Params &P, hipStream_t stream)
+// Row pass (A) then finish kernel (B) with grid.x = chunks (1 when nothing
+// is drawn), then, for sampled calls, the draw kernel (C).
+sv_status launch(Params &P, hipStream_t stream)
 {
     const int64_t nv = nvec_max(P.V, P.bf16 ? 8 : 4);
     const int64_t rows_max = (P.mode == MODE_SAMPLE) ? (int64_t)P.B * (2 * P.K + 1)
                            : (P.mode == MODE_GREEDY) ? (int64_t)P.B * (P.K + 1) : (int64_t)P.B * P.K;
-    int64_t grid = (int64_t)cu_count() * g_row_wgs_per_cu;
-    grid = std::min<int64_t>(grid, std::max<int64_t>(1, rows_max * ceil_div(nv, WG)));
-    const size_t lds = sizeof(int) * (size_t)(3 * P.B + 1);
-    if (P.bf16) hipLaunchKernelGGL(row_stats_kernel<true>, dim3((unsigned)grid), dim3(WG), lds, stream, P);
-    else hipLaunchKernelGGL(row_stats_kernel<false>, dim3((unsigned)grid), dim3(WG), lds, stream, P);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
-}
-
-sv_status launch_sampler(Params &P, hipStream_t stream)
-{
-    dim3 grid((unsigned)P.cs, (unsigned)P.B);
+    const size_t lds_a = sizeof(int) * (size_t)(3 * P.B + 1);
+    int64_t grid = (int64_t)cu_count() * row_wgs_per_cu(P.bf16, lds_a);
+    grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div(rows_max * ceil_div(nv, WVEC), NWAVE)));
+    const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1);
+    const dim3 grid_b((unsigned)(P.mode == MODE_SAMPLE ? P.cs : 1), (unsigned)P.B);
+    const dim3 grid_c((unsigned)P.cs, (unsigned)P.B);
+    (void)hipGetLastError();
     if (P.bf16) {
-        hipLaunchKernelGGL(sampler_sums_kernel<true>, grid, dim3(WG), 0, stream, P);
-        hipLaunchKernelGGL(sampler_draw_kernel<true>, grid, dim3(WG), 0, stream, P);
+        hipLaunchKernelGGL(row_pass_kernel<true>, dim3((unsigned)grid), dim3(WG), lds_a, stream, P);
+        hipLaunchKernelGGL(finish_kernel<true>, grid_b, dim3(WG), lds_b, stream, P);
+        if (P.mode == MODE_SAMPLE) hipLaunchKernelGGL(draw_kernel<true>, grid_c, dim3(WG), 0, stream, P);
     } else {
-        hipLaunchKernelGGL(sampler_sums_kernel<false>, grid, dim3(WG), 0, stream, P);
-        hipLaunchKernelGGL(sampler_draw_kernel<false>, grid, dim3(WG), 0, stream, P);
+        hipLaunchKernelGGL(row_pass_kernel<false>, dim3((unsigned)grid), dim3(WG), lds_a, stream, P);
+        hipLaunchKernelGGL(finish_kernel<false>, grid_b, dim3(WG), lds_b, stream, P);
+        if (P.mode == MODE_SAMPLE) hipLaunchKernelGGL(draw_kernel<false>, grid_c, dim3(WG), 0, stream, P);
     }
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return hip_status("kernel launch");
 }
 
 Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const Layout &L, void *ws)
@@ -1422,7 +1712,7 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
     P.mode = mode;
     P.cpr_max = L.cpr_max;
     P.cs = (int)ceil_div(nvec_max(V, P.bf16 ? 8 : 4), (int64_t)WG * US);
-    P.ws = carve(ws, L);
+    P.ws = carve(ws, L, B);
     return P;
 }
 
@@ -1431,6 +1721,8 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
 extern "C" {
 
 int32_t spec_verify_abi_version(void) { return 1; }
+
+const char *spec_verify_last_error(void) { return g_last_error; }
 
 const char *spec_verify_status_string(sv_status s)
 {
@@ -1470,7 +1762,7 @@ sv_status spec_verify_greedy(const void *target_logits, sv_dtype dt, const int32
     P.depth = depth;
     P.out_tokens = out_tokens;
     P.num_accepted = num_accepted;
-    return launch_rows(P, stream);
+    return launch(P, stream);
 }
 
 sv_status spec_verify_sample(const void *target_logits, const void *draft_logits, sv_dtype dt,
@@ -1500,8 +1792,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     P.num_accepted = num_accepted;
     P.p_draft = p_draft;
     P.q_draft = q_draft;
-    if ((st = launch_rows(P, stream)) != SV_OK) return st;
-    return launch_sampler(P, stream);
+    return launch(P, stream);
 }
 
 sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt, const int32_t *max_depth, int32_t B,
@@ -1521,7 +1812,7 @@ sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt, const int
     P.draft = draft_logits;
     P.max_depth = max_depth;
     P.conf = conf;
-    return launch_rows(P, stream);
+    return launch(P, stream);
 }
 
 sv_status dcut_allocate(const float *conf, const int32_t *max_depth, int32_t B, int32_t K, int32_t budget,
@@ -1532,15 +1823,10 @@ sv_status dcut_allocate(const float *conf, const int32_t *max_depth, int32_t B, 
     if (!depth_out || (K > 0 && !conf)) return SV_ERR_INVALID_ARG;
     if (budget < B) return SV_ERR_BUDGET;
     const size_t lds = sizeof(uint32_t) * (size_t)std::max<int64_t>(1, (int64_t)B * K);
-    static std::atomic<int> attr_set{0};
-    if (!attr_set.load()) {
-        if (hipFuncSetAttribute((const void *)dcut_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(sizeof(uint32_t) * DCUT_MAX)) != hipSuccess)
-            return SV_ERR_HIP;
-        attr_set.store(1);
-    }
+    if (!dcut_lds_ok(lds)) return SV_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
     hipLaunchKernelGGL(dcut_kernel, dim3(1), dim3(DCUT_WG), lds, stream, conf, max_depth, B, K, budget, depth_out);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return hip_status("dcut_kernel launch");
 }
 
 }  // extern "C"

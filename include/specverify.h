@@ -33,19 +33,21 @@
  *     returns SV_OK has only enqueued work.  Calls that share a workspace must
  *     be ordered (the same stream, or synchronised): their kernels use the
  *     workspace's counters.
- *   Workspace.  spec_verify_workspace_size(B, K, V) bytes, 256-byte aligned,
- *     ZERO-FILLED before its first use.  Every call leaves the counters it
- *     uses at zero when its kernels finish, so a workspace is reusable
- *     without clearing as long as every call on it ran to completion.
+ *   Workspace.  At least spec_verify_workspace_size(B, K, V) bytes,
+ *     256-byte aligned, contents arbitrary: each call's kernels clear the
+ *     counters they use before using them, so one workspace can serve calls
+ *     of any shape that fits it.  It holds per-call scratch (row partials,
+ *     counters, sampler partials) and nothing that outlives the call.
  *   Errors.  Arguments the host can check (null pointers, sizes, dtype,
  *     alignment, workspace size, budget) are rejected with a status before
  *     anything is enqueued.  Bad DATA is found on the device and reported per
  *     request as num_accepted[b] = -1 with out_tokens[b, :] = -1: a depth
- *     outside [0, K], a temperature that is negative or NaN, a drafted token
- *     outside [0, V), a uniform outside [0, 1), or a row that is read and
- *     holds a NaN or +inf, or only -inf.  -inf logits (masked tokens) are
- *     allowed otherwise.  No C++ exception crosses this interface.
- *   Limits.  1 <= B <= 4096, 0 <= K <= 1024, 1 <= V <= 2097152.
+ *     outside [0, K], a temperature that is not 0 and not a number in
+ *     [1e-6, 1e6] (so NaN, negatives and infinities), a drafted token outside
+ *     [0, V), a uniform outside [0, 1), or a row that is read and holds a NaN
+ *     or +inf, or only -inf.  -inf logits (masked tokens) are allowed
+ *     otherwise.  No C++ exception crosses this interface.
+ *   Limits.  1 <= B <= 4096, 0 <= K <= 1024, 1 <= V <= 2000000.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -75,6 +77,12 @@ int32_t spec_verify_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */
 const char *spec_verify_status_string(sv_status s);
+
+/* Detail of the last SV_ERR_HIP returned on the calling thread (the HIP
+ * error name and the launch that failed), or of a device limit behind an
+ * SV_ERR_UNSUPPORTED; "" when the last call on this thread that reached the
+ * device succeeded.  Thread-local storage. */
+const char *spec_verify_last_error(void);
 
 /* Bytes of workspace spec_verify_greedy, spec_verify_sample and
  * spec_draft_confidence need for a batch of this shape; 0 for sizes the
@@ -117,7 +125,7 @@ sv_status spec_verify_greedy(const void *target_logits, sv_dtype dt,
  *   "Qu'est-ce que le speculative decoding"; [Remio], section "Cosa non
  *   dimostrano i numeri di AngelSpec").
  *   draft_logits  [B, K, V] of dt (read: rows 0..d-1 of requests with T > 0)
- *   temperature   [B] float >= 0
+ *   temperature   [B] float: 0 (greedy rule) or in [1e-6, 1e6]
  *   u_accept      [B, K] float in [0, 1);  u_sample [B] float in [0, 1)
  *   p_draft, q_draft  [B, K] float or NULL  out: p_k(x_k), q_k(x_k) for every
  *     k < d of requests with T > 0; 0 elsewhere.
@@ -158,7 +166,10 @@ sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt,
  *   request with K_b outside [0, K] gets -1 and takes nothing.  The result is
  *   a prefix per request, sum(depth_out) = min(budget, sum of valid K_b).
  *   conf [B, K] float, max_depth [B] int32 or NULL, depth_out [B] int32.
- *   Limits: B*K <= 32768.  budget < B -> SV_ERR_BUDGET. */
+ *   Limits: B*K <= 32768 (the 4*B*K bytes of keys are held in one
+ *   workgroup's LDS; a device that gives a workgroup less LDS than that
+ *   returns SV_ERR_UNSUPPORTED, with the reason in spec_verify_last_error).
+ *   budget < B -> SV_ERR_BUDGET. */
 sv_status dcut_allocate(const float *conf, const int32_t *max_depth,
                         int32_t B, int32_t K, int32_t budget, int32_t *depth_out,
                         hipStream_t stream);

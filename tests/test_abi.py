@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -112,3 +112,10 @@ def test_confidence_and_dcut_host_errors():
     assert L.dcut_allocate(NULL, NULL, 4, 3, 8, FAKE, NULL) == 1
     assert L.dcut_allocate(FAKE, NULL, 4, 3, 8, NULL, NULL) == 1
     assert L.dcut_allocate(FAKE, NULL, 4096, 16, 9000, FAKE, NULL) == 2  # B*K > 32768
+
+
+def test_binding_shares_torch_hip_runtime():
+    # exactly one HIP runtime in the process, the one torch loaded
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs

@@ -234,7 +234,7 @@ def test_mixed_fp32_pipeline_full_size():
 def test_determinism_and_workspace_reuse():
     note("determinism: repeated calls, shared workspace across shapes")
     import draft_verification_verify_amd as sv
-    ws = torch.zeros(sv.workspace_size(64, 16, 152064), dtype=torch.uint8, device="cuda")
+    ws = torch.full((sv.workspace_size(64, 16, 152064),), 0xA5, dtype=torch.uint8, device="cuda")  # garbage
     a = synth.block_code(3, T=1.0, B=6, V=50000)
     b = synth.tiny(4, T=1.0)
     args = lambda w: (dev(w.target), dev(w.draft), dev(w.tokens), dev(w.temperature), dev(w.u_accept),
@@ -249,7 +249,6 @@ def test_determinism_and_workspace_reuse():
         for x, y in zip(ra[0], r):
             assert np.array_equal(x, y)
     assert np.array_equal(g1, g2)
-    assert np.all(host(ws) == 0)           # counters are left at zero
     compare_sample(b, *rb).assert_ok("reuse")
 
 
