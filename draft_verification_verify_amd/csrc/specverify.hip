@@ -58,9 +58,11 @@ constexpr int WG = 256;           // threads per workgroup
 constexpr int NWAVE = WG / 64;    // wave64
 constexpr int UW = 4;             // 16-byte loads per lane per row-pass batch
 constexpr int WVEC = UW * 64;     // vectors per wave batch
-constexpr int US = 4;             // 16-byte loads per thread per sampler chunk
+constexpr int UNIT_E = 2048;      // logits of a row in one sampler unit (one wave)
+constexpr int SE = 16;            // logits per lane per step of a unit
+constexpr int SUB = UNIT_E / (64 * SE);   // steps per unit
+constexpr int UNITS_MAX = 1024;   // sampler units per row, at most
 constexpr int CPR_CAP = 256;      // chunks per row, at most
-constexpr int STAGE = 1024;       // partials staged in LDS at a time (finish kernel)
 constexpr int B_MAX = 4096;
 constexpr int K_MAX = 1024;
 constexpr int V_MAX = 2000000;
@@ -70,7 +72,8 @@ constexpr int EXP2_TAB = 512;     // table entries of the fp64 exp2
 
 enum : int { MODE_GREEDY = 0, MODE_SAMPLE = 1, MODE_CONF = 2 };
 enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3 };
-enum : int { SREQ_NONE = 0, SREQ_RESID = 1, SREQ_BONUS = 2 };
+// outcome of a request's accept scan
+enum : int { SREQ_BAD = 0, SREQ_GREEDY = 1, SREQ_RESID = 2, SREQ_BONUS = 3 };
 
 constexpr double LOG2E = 1.4426950408889634;
 constexpr double LN2 = 0.6931471805599453;
@@ -84,36 +87,44 @@ struct alignas(16) Stat {
     double s;
 };
 
-struct alignas(16) ReqDesc {
+struct ReqDesc {
     int32_t state;   // SREQ_*
-    int32_t n;       // accepted length = row the sampler reads
-    int32_t pad;
+    int32_t n;       // accepted length (the row pair a draw reads)
+    int32_t emit;    // greedy: the emitted token
     float T;
 };
 
-struct alignas(16) S1Part {
-    float mz, my;
-    int32_t bad, pad;
-    double sz, sy;
+// One sampler chunk's fp64 sums over the drawn row pair, all in units of
+// 2^((v - max) * log2(e)/T):
+//   residual draw: d = sum over {P > rho_hat Q} of (P - rho_hat Q), bq = sum of
+//   Q over the same set, sz = sum P, sy = sum Q (P, Q: target and draft terms
+//   relative to their row maxima, rho_hat an estimate of sz/sy);
+//   bonus draw: m = the chunk's maximum, sz = sum of P relative to m.
+struct alignas(16) ChunkPart {
+    double d, bq, sz, sy;
+    float m;
+    int32_t bad;
+    int32_t pad[2];
 };
 
-struct alignas(16) S2Part {
-    double r, p;
+// What the draw kernel needs to know of a request (written by the finish
+// kernel): the scan's outcome and the drawn row pair's statistics.
+struct alignas(16) DrawRec {
+    int32_t state, n;
+    float T, mz;
+    float my, pad;
+    double rho_hat;
 };
 
 struct Ws {
     int32_t *meta;       // [4]: chunks per row and batches per chunk of the row pass
-    uint32_t *s1cnt;     // [B]  (cleared by the row pass)
-    uint32_t *s2cnt;     // [B]  (cleared by the finish kernel)
     Stat *part;          // [R_max * cpr_max] row-pass chunk partials
-    ReqDesc *req;        // [B]
-    S1Part *s1;          // [B * cs_max]
-    S1Part *s1tot;       // [B]
-    S2Part *s2;          // [B * cs_max]
+    ChunkPart *cp;       // [B * cs_max] sampler chunk sums
+    DrawRec *rec;        // [B]
 };
 
 struct Layout {
-    size_t off[6];
+    size_t off[4];
     size_t total;
     int64_t r_max;
     int cpr_max;
@@ -134,17 +145,16 @@ bool make_layout(int B, int K, int V, Layout &L)
     const int64_t nv = nvec_max(V, 4);   // fp32 is the worst case
     L.r_max = (int64_t)B * (2 * K + 1);
     L.cpr_max = (int)std::min<int64_t>(CPR_CAP, ceil_div(nv, WVEC));
-    L.cs_max = (int)ceil_div(nv, (int64_t)WG * US);
-    const size_t sz[6] = {
-        sizeof(int32_t) * 4 + sizeof(uint32_t) * 2 * (size_t)B,
+    L.cs_max = (int)std::max(ceil_div(nv, (int64_t)UNIT_E / 4), ceil_div(nvec_max(V, 8), (int64_t)UNIT_E / 8));
+    if (L.cs_max > UNITS_MAX) return false;
+    const size_t sz[4] = {
+        sizeof(int32_t) * 4,
         sizeof(Stat) * (size_t)L.r_max * (size_t)L.cpr_max,
-        sizeof(ReqDesc) * (size_t)B,
-        sizeof(S1Part) * (size_t)B * (size_t)L.cs_max,
-        sizeof(S1Part) * (size_t)B,
-        sizeof(S2Part) * (size_t)B * (size_t)L.cs_max,
+        sizeof(ChunkPart) * (size_t)B * (size_t)L.cs_max,
+        sizeof(DrawRec) * (size_t)B,
     };
     size_t o = 0;
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 4; ++i) {
         L.off[i] = o;
         o += align256(sz[i]);
     }
@@ -157,13 +167,10 @@ Ws carve(void *base, const Layout &L, int B)
     char *p = (char *)base;
     Ws w;
     w.meta = (int32_t *)(p + L.off[0]);
-    w.s1cnt = (uint32_t *)(p + L.off[0] + 16);
-    w.s2cnt = w.s1cnt + B;
     w.part = (Stat *)(p + L.off[1]);
-    w.req = (ReqDesc *)(p + L.off[2]);
-    w.s1 = (S1Part *)(p + L.off[3]);
-    w.s1tot = (S1Part *)(p + L.off[4]);
-    w.s2 = (S2Part *)(p + L.off[5]);
+    w.cp = (ChunkPart *)(p + L.off[2]);
+    w.rec = (DrawRec *)(p + L.off[3]);
+    (void)B;
     return w;
 }
 
@@ -185,7 +192,8 @@ struct Params {
     int32_t bf16;      // logits dtype: 1 bf16, 0 fp32
     int32_t mode;
     int32_t cpr_max;
-    int32_t cs;        // sampler chunks per row (this call's dtype)
+    int32_t cs;        // sampler units per row (this call's dtype)
+    int32_t aligned;   // V * element size is a multiple of 16: every row starts 16-byte aligned
     Ws ws;
 };
 
@@ -242,72 +250,6 @@ __device__ __forceinline__ uint4 ld_stream(gvec_t p)
     typedef unsigned int u4v __attribute__((ext_vector_type(4)));
     const u4v w = __builtin_nontemporal_load((const __attribute__((address_space(1))) u4v *)p);
     return make_uint4(w.x, w.y, w.z, w.w);
-}
-
-// Cross-workgroup hand-off inside a kernel, without cache maintenance.  Data
-// another workgroup will read is written with device-scope (sc1) atomic
-// stores, which complete at the device coherence point; an s_waitcnt waits
-// for them to complete before the counter's atomic increment is issued, and
-// the workgroup that sees the final count reads the data back with
-// device-scope atomic loads, which never return stale cache lines.  (An
-// agent-scope release/acquire fence would instead write back and invalidate
-// the XCD's whole L2.)
-__device__ __forceinline__ void st_dev(uint64_t *p, uint64_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_dev(const uint64_t *p)
-{
-    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores()
-{
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-__device__ __forceinline__ uint32_t count_in(uint32_t *p)
-{
-    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void after_count() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
-
-__device__ __forceinline__ uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x); }
-__device__ __forceinline__ double bitsd(uint64_t x) { return __longlong_as_double((long long)x); }
-
-__device__ __forceinline__ void put_s1(S1Part *p, const S1Part &v)
-{
-    st_dev((uint64_t *)p, (uint64_t)__float_as_uint(v.mz) | ((uint64_t)__float_as_uint(v.my) << 32));
-    st_dev((uint64_t *)p + 1, (uint64_t)(uint32_t)v.bad);
-    st_dev((uint64_t *)p + 2, dbits(v.sz));
-    st_dev((uint64_t *)p + 3, dbits(v.sy));
-}
-
-__device__ __forceinline__ S1Part get_s1(const S1Part *p)
-{
-    const uint64_t w0 = ld_dev((const uint64_t *)p), w1 = ld_dev((const uint64_t *)p + 1);
-    S1Part v;
-    v.mz = __uint_as_float((uint32_t)w0);
-    v.my = __uint_as_float((uint32_t)(w0 >> 32));
-    v.bad = (int32_t)w1;
-    v.pad = 0;
-    v.sz = bitsd(ld_dev((const uint64_t *)p + 2));
-    v.sy = bitsd(ld_dev((const uint64_t *)p + 3));
-    return v;
-}
-
-__device__ __forceinline__ void put_s2(S2Part *p, const S2Part &v)
-{
-    st_dev((uint64_t *)p, dbits(v.r));
-    st_dev((uint64_t *)p + 1, dbits(v.p));
-}
-
-__device__ __forceinline__ S2Part get_s2(const S2Part *p)
-{
-    S2Part v;
-    v.r = bitsd(ld_dev((const uint64_t *)p));
-    v.p = bitsd(ld_dev((const uint64_t *)p + 1));
-    return v;
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -430,11 +372,13 @@ __device__ double wg_excl_scan(double v, double *sm4, double &total)
     return wb + excl;
 }
 
-// fp64 2^x for x <= 0: x = k/512 + r with k = rint(512 x) and |r| <= 1/1024;
+// fp64 2^x for x <= 0, within 1e-14 relative (the sampler needs per-term
+// accuracy far below 1e-10, not correct rounding).  x = k/512 + r with k = round(512 x)
+// taken from the low word of x*512 + 1.5*2^52, |r| <= 1/1024;
 // 2^(k/512) = 2^(k >> 9) * T[k & 511] with T[j] = 2^(j/512) tabulated in LDS
-// at kernel start, and 2^r = exp(r ln2) by its Taylor polynomial of degree 4
-// (truncation below 2e-18 relative).  Total error about 2 ulp.  Arguments at
-// or below -1070 give 0; NaN propagates.
+// at kernel start, and 2^r by its Taylor polynomial of degree 3 (truncation
+// below 1e-14 relative).  Arguments below -2000 (and -inf) give exactly 0
+// through ldexp's underflow; NaN propagates.
 __device__ void init_exp2_table(double *tab)
 {
     for (int j = threadIdx.x; j < EXP2_TAB; j += blockDim.x) tab[j] = exp2((double)j / EXP2_TAB);
@@ -443,14 +387,15 @@ __device__ void init_exp2_table(double *tab)
 
 __device__ __forceinline__ double exp2_tab(double x, const double *tab)
 {
-    if (!(x > -1070.0)) return (x != x) ? x : 0.0;
-    const double kd = rint(x * EXP2_TAB);
-    const int k = (int)kd;
-    const double t = fma(kd, -1.0 / EXP2_TAB, x) * LN2;
-    double p = fma(t, 1.0 / 24.0, 1.0 / 6.0);
-    p = fma(t, p, 0.5);
-    p = fma(t, p, 1.0);
-    p = fma(t, p, 1.0);
+    constexpr double SHIFT = 6755399441055744.0;   // 1.5 * 2^52
+    constexpr double C1 = LN2, C2 = LN2 * LN2 / 2.0, C3 = LN2 * LN2 * LN2 / 6.0;
+    x = (x < -2000.0) ? -2000.0 : x;
+    const double kb = fma(x, (double)EXP2_TAB, SHIFT);
+    const int k = (int)(uint32_t)(uint64_t)__double_as_longlong(kb);
+    const double r = fma(kb - SHIFT, -1.0 / EXP2_TAB, x);
+    double p = fma(r, C3, C2);
+    p = fma(r, p, C1);
+    p = fma(r, p, 1.0);
     return ldexp(tab[k & (EXP2_TAB - 1)] * p, k >> 9);
 }
 
@@ -824,13 +769,9 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int64_t nwaves = (int64_t)gridDim.x * NWAVE;
     int cpr, nb;
     row_chunking(R, P.V, BF16, nwaves, cpr, nb);
-    if (blockIdx.x == 0) {
-        if (threadIdx.x == 0) {
-            P.ws.meta[0] = cpr;
-            P.ws.meta[1] = nb;
-        }
-        if (P.mode == MODE_SAMPLE)
-            for (int i = threadIdx.x; i < P.B; i += WG) P.ws.s1cnt[i] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        P.ws.meta[0] = cpr;
+        P.ws.meta[1] = nb;
     }
 
     // Static assignment: wave w takes tasks w, w + nwaves, ...  The next
@@ -883,19 +824,6 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 // the drafted positions), from the request's merged row statistics.
 // ---------------------------------------------------------------------------
 
-__device__ void mark_bad_request(const Params &P, int b)
-{
-    const int K = P.K;
-    for (int k = lane_id(); k <= K; k += 64) P.out_tokens[(int64_t)b * (K + 1) + k] = -1;
-    if (P.mode == MODE_SAMPLE) {
-        for (int k = lane_id(); k < K; k += 64) {
-            if (P.p_draft) P.p_draft[(int64_t)b * K + k] = 0.0f;
-            if (P.q_draft) P.q_draft[(int64_t)b * K + k] = 0.0f;
-        }
-    }
-    if (lane_id() == 0) P.num_accepted[b] = -1;
-}
-
 // Unusable row statistics: NaN or +inf present (m = NaN or +inf), nothing
 // but -inf (m = -inf), or a normaliser that is not a positive finite number.
 __device__ __forceinline__ bool stat_bad(const Stat &s, bool lse)
@@ -908,22 +836,18 @@ __device__ __forceinline__ bool stat_bad(const Stat &s, bool lse)
 __device__ __forceinline__ bool unif_ok(float u) { return u >= 0.0f && u < 1.0f; }
 
 // rows: target rows 0..d (greedy) or target rows 0..d-1 then draft rows
-// 0..d-1 (sampled), in LDS.  Only the workgroup with `write` set publishes
-// the outputs; every caller gets the sampler descriptor.
-__device__ ReqDesc scan_request(const Params &P, int b, int d, int kind, float T, const Stat *rows, bool write,
+// 0..d-1 (sampled), in LDS.  For a sampled request pq[k] receives
+// (p_k(x_k), q_k(x_k)) for k < d.  Writes nothing to global memory.
+__device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const Stat *rows, float2 *pq,
                                 const double *tab)
 {
-    const int K = P.K;
+    const int K = P.K, d = q.d;
     const int lane = lane_id();
-    const int64_t ob = (int64_t)b * (K + 1);
     const int64_t tb = (int64_t)b * K;
-    ReqDesc desc = {SREQ_NONE, 0, 0, T};
+    ReqDesc desc = {SREQ_BAD, 0, -1, q.T};
+    if (q.kind == KIND_BAD) return desc;
 
-    if (kind == KIND_BAD) {
-        if (write) mark_bad_request(P, b);
-        return desc;
-    }
-    if (kind == KIND_GREEDY) {
+    if (q.kind == KIND_GREEDY) {
         // accept k iff x_k == argmax of target row k; emit argmax of row n
         int n = d;
         int bad = 0;
@@ -942,22 +866,7 @@ __device__ ReqDesc scan_request(const Params &P, int b, int d, int kind, float T
             const uint64_t mm = __ballot(mism);
             if (mm && n == d) n = k0 + __builtin_ctzll(mm);
         }
-        bad = wave_or(bad);
-        if (!write) return desc;
-        if (bad) {
-            mark_bad_request(P, b);
-        } else {
-            const int emit = rows[n].idx;
-            for (int k = lane; k <= K; k += 64)
-                P.out_tokens[ob + k] = (k < n) ? P.tokens[tb + k] : (k == n ? emit : -1);
-            if (P.mode == MODE_SAMPLE) {
-                for (int k = lane; k < K; k += 64) {
-                    if (P.p_draft) P.p_draft[tb + k] = 0.0f;
-                    if (P.q_draft) P.q_draft[tb + k] = 0.0f;
-                }
-            }
-            if (lane == 0) P.num_accepted[b] = n;
-        }
+        if (!wave_or(bad)) desc = {SREQ_GREEDY, n, rows[n].idx, q.T};
         return desc;
     }
 
@@ -966,18 +875,18 @@ __device__ ReqDesc scan_request(const Params &P, int b, int d, int kind, float T
     // exponent scale c32 as the statistics.
     int bad = unif_ok(P.u_sample[b]) ? 0 : 1;
     int n = d;
-    const double c2 = (double)c32_of(kind, T);
+    const double c2 = (double)c32_of(q.kind, q.T);
     const int64_t V = P.V;
     for (int k0 = 0; k0 < d; k0 += 64) {
         const int k = k0 + lane;
         const bool active = k < d;
         bool rej = false;
-        double a = 0.0, c = 0.0;
         if (active) {
             const int x = P.tokens[tb + k];
             const float ua = P.u_accept[tb + k];
             const Stat st = rows[k], sd = rows[d + k];
             const bool lb = (x < 0 || x >= P.V) || !unif_ok(ua) || stat_bad(st, true) || stat_bad(sd, true);
+            double a = 0.0, c = 0.0;
             if (!lb) {
                 const float zx = load_logit_dt(P.target, P.bf16, ((int64_t)b * (K + 1) + k) * V + x);
                 const float yx = load_logit_dt(P.draft, P.bf16, (tb + k) * V + x);
@@ -987,116 +896,277 @@ __device__ ReqDesc scan_request(const Params &P, int b, int d, int kind, float T
                 rej = !((double)ua < ratio);
             }
             bad |= lb;
-        }
-        if (write && active) {
-            if (P.p_draft) P.p_draft[tb + k] = (float)a;
-            if (P.q_draft) P.q_draft[tb + k] = (float)c;
+            pq[k] = make_float2((float)a, (float)c);
         }
         const uint64_t rm = __ballot(active && rej);
         if (rm && n == d) n = k0 + __builtin_ctzll(rm);
     }
-    bad = wave_or(bad);
-    if (bad) {
-        if (write) mark_bad_request(P, b);
-        return desc;
-    }
-    desc.state = (n == d) ? SREQ_BONUS : SREQ_RESID;
-    desc.n = n;
-    if (write) {
-        for (int k = d + lane; k < K; k += 64) {
-            if (P.p_draft) P.p_draft[tb + k] = 0.0f;
-            if (P.q_draft) P.q_draft[tb + k] = 0.0f;
-        }
-        // the emitted token at position n is written by the draw kernel
-        for (int k = lane; k <= K; k += 64) P.out_tokens[ob + k] = (k < n) ? P.tokens[tb + k] : -1;
-        if (lane == 0) P.num_accepted[b] = n;
-    }
+    if (!wave_or(bad)) desc = {n == d ? SREQ_BONUS : SREQ_RESID, n, -1, q.T};
     return desc;
 }
 
-// ---------------------------------------------------------------------------
-// Finish kernel (B)
-// ---------------------------------------------------------------------------
-
-// s_i (relative to m_i, exponent scale cs) rescaled to M; unusable partials
-// (NaN) poison the sum.
-__device__ __forceinline__ double rescale(float m_i, double s_i, float M, double cs, const double *tab)
+// One wave writes request b's outputs: the accepted prefix, the emitted token
+// at position n, -1 after it, num_accepted, and (sampled calls) p/q at the
+// drafted tokens.  A bad request gets -1 everywhere and zero probabilities.
+__device__ void write_outputs(const Params &P, int b, int d, const ReqDesc &desc, const float2 *pq, int token)
 {
-    if (m_i == -INFINITY) return (s_i != s_i) ? s_i : 0.0;
-    return s_i * exp2_tab(((double)m_i - (double)M) * cs, tab);
+    const int K = P.K, lane = lane_id();
+    const int64_t ob = (int64_t)b * (K + 1), tb = (int64_t)b * K;
+    const bool bad = desc.state == SREQ_BAD;
+    const int n = desc.n;
+    for (int k = lane; k <= K; k += 64)
+        P.out_tokens[ob + k] = bad ? -1 : (k < n ? P.tokens[tb + k] : (k == n ? token : -1));
+    if (P.mode == MODE_SAMPLE) {
+        const bool sampled = desc.state == SREQ_RESID || desc.state == SREQ_BONUS;
+        for (int k = lane; k < K; k += 64) {
+            const float2 v = (sampled && k < d) ? pq[k] : make_float2(0.0f, 0.0f);
+            if (P.p_draft) P.p_draft[tb + k] = v.x;
+            if (P.q_draft) P.q_draft[tb + k] = v.y;
+        }
+    }
+    if (lane == 0) P.num_accepted[b] = bad ? -1 : n;
 }
 
-// Merge n chunk partials of one row (one thread, from LDS).
-__device__ Stat merge_chunks(const Stat *q, int n, bool lse, double cs, const double *tab)
+// ---------------------------------------------------------------------------
+// Finish kernel: merge, accept scan, sampler chunk sums.
+// ---------------------------------------------------------------------------
+
+// Merge of two partial statistics of one row: (max, lowest argmax) with NaN
+// propagated, or (max, sum relative to the max) rescaled to the larger max.
+__device__ __forceinline__ Stat merge2(Stat a, Stat b, bool lse, double cs, const double *tab)
 {
-    Stat st;
     if (!lse) {
-        float m = -INFINITY;
-        int i = 0x7fffffff, nanf = 0;
-        for (int j = 0; j < n; ++j) {
-            const Stat p = q[j];
-            if (!(p.m == p.m)) nanf = 1;
-            else argmax_merge(m, i, p.m, p.idx);
-        }
-        st.m = nanf ? NAN : m;
-        st.idx = i;
-        st.s = 0.0;
-    } else {
-        float M = -INFINITY;
-        double S = 0.0;
-        for (int j = 0; j < n; ++j) {
-            const Stat p = q[j];
-            if (p.m > M) {
-                S = rescale(M, S, p.m, cs, tab) + p.s;
-                M = p.m;
-            } else {
-                S += rescale(p.m, p.s, M, cs, tab);
-            }
-        }
-        st.m = M;
-        st.idx = 0;
-        st.s = S;
+        if (!(a.m == a.m)) return a;
+        if (!(b.m == b.m)) return b;
+        argmax_merge(a.m, a.idx, b.m, b.idx);
+        return a;
     }
-    return st;
+    if (b.m > a.m) {
+        const Stat t = a;
+        a = b;
+        b = t;
+    }
+    if (b.m == -INFINITY) a.s += (b.s != b.s) ? b.s : 0.0;   // empty (or NaN-poisoned) partial
+    else a.s += b.s * exp2_tab(((double)b.m - (double)a.m) * cs, tab);
+    return a;
 }
 
-template <bool BF16>
-__device__ __forceinline__ void load_sampler_chunk(const RowView<BF16> &rv, int vbeg, float (&f)[US][RowView<BF16>::EPV],
-                                                   int &flag)
+// Merges the row-pass partials of request b's rows into rows_s (all threads;
+// tpr threads per row, each folding every tpr-th partial, then a butterfly
+// over the tpr lanes).  Every workgroup of a request performs the same
+// operations in the same order, so all of them hold identical statistics.
+__device__ void merge_rows(const Params &P, int pre, int rows, int cpr, bool lse, double cs, const double *tab,
+                           Stat *rows_s)
 {
-    constexpr int EPV = RowView<BF16>::EPV;
-#pragma unroll
-    for (int j = 0; j < US; ++j) {
-        const int vi = vbeg + j * WG + (int)threadIdx.x;
-        const uint4 raw = ld_plain(rv.vec + min(vi, rv.nvec - 1));
-        unpack<BF16>(raw, f[j]);
-        if (vi >= rv.nvec || rv.edge(vi)) {
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const int x = rv.elem(vi, e);
-                if (x < 0 || x >= rv.V) f[j][e] = -INFINITY;
-            }
+    const int tid = threadIdx.x;
+    int tpr = 1;
+    while (tpr < 64 && tpr < cpr && 2 * tpr * rows <= WG) tpr <<= 1;
+    const int G = WG / tpr;
+    const Stat ident = {-INFINITY, 0x7fffffff, 0.0};
+    for (int g0 = 0; g0 < rows; g0 += G) {
+        const int r = g0 + tid / tpr, l = tid & (tpr - 1);
+        Stat acc = ident;
+        if (r < rows) {
+            const Stat *pp = P.ws.part + (int64_t)(pre + r) * P.cpr_max;
+            for (int j = l; j < cpr; j += tpr) acc = merge2(acc, pp[j], lse, cs, tab);
         }
+        for (int o = tpr >> 1; o > 0; o >>= 1) {
+            Stat other;
+            other.m = __shfl_xor(acc.m, o, 64);
+            other.idx = __shfl_xor(acc.idx, o, 64);
+            other.s = __shfl_xor(acc.s, o, 64);
+            acc = merge2(acc, other, lse, cs, tab);
+        }
+        if (r < rows && l == 0) rows_s[r] = acc;
+    }
+    __syncthreads();
+}
+
+// Sampler units: a wave's contiguous run of UNIT_E logits of the drawn row
+// pair (UNIT_V 16-byte vectors), read in SUB steps of NV vectors per lane;
+// step s, slot j, lane l reads vector (s*NV + j)*64 + l of the unit, so every
+// load instruction covers 64 consecutive vectors.
+template <bool BF16>
+constexpr int unit_v() { return UNIT_E / RowView<BF16>::EPV; }
+template <bool BF16>
+constexpr int sampler_nv() { return SE / RowView<BF16>::EPV; }
+
+// Branch-free loads (clamped index) of vectors v0 + j*stride, j < N.
+template <bool BF16, int N>
+__device__ __forceinline__ void issue_vecs(const RowView<BF16> &rv, int v0, int stride, uint4 (&raw)[N])
+{
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) flag |= (!(f[j][e] == f[j][e]) || f[j][e] == INFINITY);
+    for (int j = 0; j < N; ++j) raw[j] = ld_plain(rv.vec + min(v0 + j * stride, rv.nvec - 1));
+}
+
+// Elements of vector vi as fp32, -inf outside the row (selects, no branch);
+// NaN / +inf flagged.
+template <bool BF16>
+__device__ __forceinline__ void chunk_vec(const RowView<BF16> &rv, int vi, const uint4 &raw,
+                                          float (&f)[RowView<BF16>::EPV], int &flag)
+{
+    unpack<BF16>(raw, f);
+#pragma unroll
+    for (int e = 0; e < RowView<BF16>::EPV; ++e) {
+        const int x = rv.elem(vi, e);
+        f[e] = ((unsigned)x < (unsigned)rv.V) ? f[e] : -INFINITY;
+        flag |= (!(f[e] == f[e]) || f[e] == INFINITY);
     }
 }
 
-// Workgroup (b, c): merge request b's rows, run its accept scan (workgroup
-// c == 0 publishes the outputs), then for a request that draws a token,
-// reduce chunk c of the drawn row pair to fp64 (max, sum of exp2) per row; the
-// last chunk to finish combines the request's normalisers.
+// Draft logits on the target row's vector grid.  With ALIGNED (V * element
+// size a multiple of 16) every row starts on a vector boundary and that is
+// the draft row's own grid; otherwise the draft row is read by token index.
 template <bool BF16>
+struct DraftChunk {
+    RowView<BF16> ry;
+    const char *yrow;
+};
+
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ void draft_vec(const DraftChunk<BF16> &dc, const RowView<BF16> &rz, int vi,
+                                          const uint4 &raw, float (&g)[RowView<BF16>::EPV])
+{
+    int fl = 0;
+    if constexpr (ALIGNED) {
+        chunk_vec<BF16>(dc.ry, vi, raw, g, fl);
+    } else {
+#pragma unroll
+        for (int e = 0; e < RowView<BF16>::EPV; ++e) {
+            const int x = rz.elem(vi, e);
+            const float v = load_logit<BF16>(dc.yrow, min(max(x, 0), rz.V - 1));   // branch-free
+            g[e] = (x >= 0 && x < rz.V) ? v : -INFINITY;
+        }
+    }
+}
+
+// Drawn row pair of a request: target row n (and draft row n for a residual
+// draw), with the exponent constants of P = 2^((z - Mz) cd), Q = 2^((y - My) cd).
+template <bool BF16>
+struct DrawRows {
+    RowView<BF16> rz;
+    DraftChunk<BF16> dc;
+    double cd, mzc, myc;
+};
+
+template <bool BF16>
+__device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int b, const ReqDesc &desc, float Mz, float My)
+{
+    DrawRows<BF16> r;
+    const int64_t esz = BF16 ? 2 : 4;
+    r.rz = RowView<BF16>((const char *)P.target + ((int64_t)b * (P.K + 1) + desc.n) * P.V * esz, P.V);
+    r.dc.yrow = (const char *)P.draft + ((int64_t)b * P.K + desc.n) * P.V * esz;
+    r.dc.ry = RowView<BF16>(r.dc.yrow, P.V);
+    r.cd = LOG2E / (double)desc.T;
+    r.mzc = (double)Mz * r.cd;
+    r.myc = (double)My * r.cd;
+    return r;
+}
+
+// One wave's unit of the drawn row pair (vectors vu .. vu + UNIT_V - 1).
+// Residual draw: the sums d, bq, sz, sy (rho_hat from the row pass).  Bonus
+// draw: the unit's maximum and the sum of P relative to it (each lane keeps a
+// running maximum; the wave rescales to the unit's).
+template <bool BF16, bool ALIGNED>
+__device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_hat, int vu, const double *tab)
+{
+    constexpr int EPV = RowView<BF16>::EPV, NV = sampler_nv<BF16>();
+    const int lane = lane_id();
+    ChunkPart part;
+    part.pad[0] = part.pad[1] = 0;
+    int flag = 0;
+    if (resid) {
+        double dsum = 0.0, bq = 0.0, sz = 0.0, sy = 0.0;
+#pragma unroll 1
+        for (int u = 0; u < SUB; ++u) {
+            const int v0 = vu + u * NV * 64 + lane;
+            uint4 rz[NV], ry[NV];
+            issue_vecs<BF16, NV>(dr.rz, v0, 64, rz);
+            if (ALIGNED) issue_vecs<BF16, NV>(dr.dc.ry, v0, 64, ry);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int vi = v0 + j * 64;
+                float f[EPV], g[EPV];
+                // one vector at a time: unbounded interleaving of the fp64
+                // exponentials would cost occupancy
+                __builtin_amdgcn_sched_barrier(0);
+                chunk_vec<BF16>(dr.rz, vi, rz[j], f, flag);
+                draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry[j], g);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const double p = exp2_tab(fma((double)f[e], dr.cd, -dr.mzc), tab);
+                    const double q = exp2_tab(fma((double)g[e], dr.cd, -dr.myc), tab);
+                    sz += p;
+                    sy += q;
+                    const double t = fma(-rho_hat, q, p);
+                    if (t > 0.0) {
+                        dsum += t;
+                        bq += q;
+                    }
+                }
+            }
+        }
+        part.d = wave_sum(dsum);
+        part.bq = wave_sum(bq);
+        part.sz = wave_sum(sz);
+        part.sy = wave_sum(sy);
+        part.m = 0.0f;
+        part.bad = 0;   // the residual rows were checked by the row pass
+    } else {
+        float m = -INFINITY;
+        double s = 0.0;
+#pragma unroll 1
+        for (int u = 0; u < SUB; ++u) {
+            const int v0 = vu + u * NV * 64 + lane;
+            uint4 rz[NV];
+            issue_vecs<BF16, NV>(dr.rz, v0, 64, rz);
+            float f[NV][EPV];
+            float ml = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                chunk_vec<BF16>(dr.rz, v0 + j * 64, rz[j], f[j], flag);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) ml = fmaxf(ml, f[j][e]);
+            }
+            if (ml > m) {
+                if (m != -INFINITY) s *= exp2_tab(((double)m - (double)ml) * dr.cd, tab);
+                m = ml;
+            }
+            if (m != -INFINITY && m != INFINITY) {
+                const double mc = (double)m * dr.cd;
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) s += exp2_tab(fma((double)f[j][e], dr.cd, -mc), tab);
+            }
+        }
+        const float M = wave_max(m);
+        if (m != -INFINITY && M != INFINITY) s *= exp2_tab(((double)m - (double)M) * dr.cd, tab);
+        else s = 0.0;
+        part.d = part.bq = part.sy = 0.0;
+        part.sz = wave_sum(s);
+        part.m = M;
+        part.bad = wave_or(flag);
+    }
+    return part;
+}
+
+// Workgroup (c, b):
+//  1. merges request b's row statistics from the row-pass partials (every
+//     workgroup of the request does this itself, so none waits on another);
+//  2. wave 0 runs the accept test and first-rejection scan; workgroup c = 0
+//     writes the request's outputs (the drawn token, if any, comes from the
+//     draw kernel) and the record the draw kernel reads;
+//  3. for a request that draws a token (sampled calls), each wave sums one
+//     unit of the drawn row pair in fp64 (unit 4c + wave).
+template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(WG) void finish_kernel(Params P)
 {
-    constexpr int EPV = RowView<BF16>::EPV;
-    extern __shared__ Stat rows_s[];   // [2K + 1] merged row statistics of request b
+    extern __shared__ Stat rows_s[];   // [2K + 1] merged row statistics, then [K] (p, q) pairs
     __shared__ double tab[EXP2_TAB];
-    __shared__ Stat stage[STAGE];
-    __shared__ RedSmem sm;
     __shared__ int sh_pre[NWAVE];
     __shared__ ReqDesc sh_desc;
-    __shared__ int sh_last;
+    float2 *pq_s = (float2 *)(rows_s + 2 * P.K + 1);
     const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
     init_exp2_table(tab);
 
@@ -1112,21 +1182,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     for (int w = 0; w < NWAVE; ++w) pre += sh_pre[w];
 
     const ReqPlan q = plan_request(P, b);
-    const int cpr = P.ws.meta[0];
     const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF;
-    const double cs = lse ? (double)c32_of(q.kind, q.T) : 0.0;
-    const int grp = std::max(1, std::min(WG, STAGE / cpr));
-    for (int g0 = 0; g0 < q.rows; g0 += grp) {
-        const int gn = std::min(grp, q.rows - g0);
-        __syncthreads();
-        for (int i = tid; i < gn * cpr; i += WG) {
-            const int rr = i / cpr, jj = i - rr * cpr;
-            stage[i] = P.ws.part[(int64_t)(pre + g0 + rr) * P.cpr_max + jj];
-        }
-        __syncthreads();
-        if (tid < gn) rows_s[g0 + tid] = merge_chunks(stage + tid * cpr, cpr, lse, cs, tab);
-    }
-    __syncthreads();
+    merge_rows(P, pre, q.rows, P.ws.meta[0], lse, lse ? (double)c32_of(q.kind, q.T) : 0.0, tab, rows_s);
 
     if (P.mode == MODE_CONF) {
         for (int k = tid; k < P.K; k += WG) {
@@ -1139,285 +1196,225 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
         return;
     }
     if (wave_id() == 0) {
-        const ReqDesc d = scan_request(P, b, q.d, q.kind, q.T, rows_s, c == 0, tab);
-        if (lane_id() == 0) sh_desc = d;
+        const ReqDesc dsc = scan_request(P, b, q, rows_s, pq_s, tab);
+        if (lane_id() == 0) sh_desc = dsc;
     }
     __syncthreads();
     const ReqDesc desc = sh_desc;
-    if (P.mode != MODE_SAMPLE) return;
-    if (c == 0 && tid == 0) {
-        P.ws.req[b] = desc;
-        P.ws.s2cnt[b] = 0u;
-    }
-    if (desc.state == SREQ_NONE) return;
-
-    // fp64 normalisers of the drawn row pair (chunk c): local max, then
-    // sum exp2((v - max) * cd) with cd = log2(e)/T in double.
+    const bool draw = desc.state == SREQ_RESID || desc.state == SREQ_BONUS;
     const bool resid = desc.state == SREQ_RESID;
-    const int K = P.K, V = P.V;
-    const int64_t esz = BF16 ? 2 : 4;
-    const double cd = LOG2E / (double)desc.T;
-    const RowView<BF16> rz((const char *)P.target + ((int64_t)b * (K + 1) + desc.n) * V * esz, V);
-    const int vbeg = c * US * WG;
-    int flag = 0;
-    float f[US][EPV];
-    load_sampler_chunk<BF16>(rz, vbeg, f, flag);
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < US; ++j)
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) m = fmaxf(m, f[j][e]);
-    const float mz = wg_max(m, sm);
-    double s = 0.0;
-    if (mz != -INFINITY && mz != INFINITY) {
-#pragma unroll
-        for (int j = 0; j < US; ++j)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) s += exp2_tab(((double)f[j][e] - (double)mz) * cd, tab);
-    }
-    const double sz = wg_sum(s, sm);
-    float my = 0.0f;
-    double sy = 0.0;
-    if (resid) {
-        const RowView<BF16> ry((const char *)P.draft + ((int64_t)b * K + desc.n) * V * esz, V);
-        int fy = 0;
-        load_sampler_chunk<BF16>(ry, vbeg, f, fy);
-        m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < US; ++j)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) m = fmaxf(m, f[j][e]);
-        my = wg_max(m, sm);
-        s = 0.0;
-        if (my != -INFINITY && my != INFINITY) {
-#pragma unroll
-            for (int j = 0; j < US; ++j)
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) s += exp2_tab(((double)f[j][e] - (double)my) * cd, tab);
+    const int d = q.d;
+    const Stat sz_row = rows_s[draw ? desc.n : 0];
+    const Stat sy_row = resid ? rows_s[d + desc.n] : sz_row;
+    const double rho_hat = resid ? sz_row.s / sy_row.s : 0.0;
+    if (c == 0 && wave_id() == 0) {
+        write_outputs(P, b, d, desc, pq_s, desc.state == SREQ_GREEDY ? desc.emit : -1);
+        if (P.mode == MODE_SAMPLE && lane_id() == 0) {
+            DrawRec r;
+            r.state = desc.state;
+            r.n = desc.n;
+            r.T = desc.T;
+            r.mz = resid ? sz_row.m : 0.0f;
+            r.my = resid ? sy_row.m : 0.0f;
+            r.pad = 0.0f;
+            r.rho_hat = rho_hat;
+            P.ws.rec[b] = r;
         }
-        sy = wg_sum(s, sm);
     }
-    flag = wg_or(flag, sm);
-
-    if (tid == 0) {
-        const S1Part part = {mz, my, flag, 0, sz, sy};
-        put_s1(P.ws.s1 + (int64_t)b * P.cs + c, part);
-        wait_stores();
-        const uint32_t old = count_in(&P.ws.s1cnt[b]);
-        sh_last = (old == (uint32_t)(P.cs - 1));
-    }
-    __syncthreads();
-    if (!sh_last || wave_id() != 0) return;
-    after_count();
-    const S1Part *pp = P.ws.s1 + (int64_t)b * P.cs;
-    float Mz = -INFINITY, My = -INFINITY;
-    int bad = 0;
-    for (int j = lane_id(); j < P.cs; j += 64) {
-        const S1Part x = get_s1(pp + j);
-        Mz = fmaxf(Mz, x.mz);
-        My = fmaxf(My, x.my);
-        bad |= x.bad;
-    }
-    Mz = wave_max(Mz);
-    My = wave_max(My);
-    double Sz = 0.0, Sy = 0.0;
-    for (int j = lane_id(); j < P.cs; j += 64) {
-        const S1Part x = get_s1(pp + j);
-        if (x.mz != -INFINITY) Sz += x.sz * exp2_tab(((double)x.mz - (double)Mz) * cd, tab);
-        if (resid && x.my != -INFINITY) Sy += x.sy * exp2_tab(((double)x.my - (double)My) * cd, tab);
-    }
-    Sz = wave_sum(Sz);
-    Sy = wave_sum(Sy);
-    bad = wave_or(bad);
-    // Residual rows were checked by the row pass; a flag here can only come
-    // from the bonus row (target row d), which only this draw reads.
-    bad |= (Mz == -INFINITY || Mz == INFINITY || !(Sz > 0.0));
-    if (resid) bad |= (My == -INFINITY || My == INFINITY || !(Sy > 0.0));
-    if (lane_id() == 0) {
-        const S1Part tot = {Mz, My, bad, 0, Sz, Sy};
-        P.ws.s1tot[b] = tot;
-    }
+    if (!draw) return;
+    // this wave's unit of the drawn row pair (no workgroup barrier after here)
+    const int unit = c * NWAVE + wave_id();
+    if (unit >= P.cs) return;
+    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, resid ? sz_row.m : 0.0f, resid ? sy_row.m : 0.0f);
+    const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rho_hat, unit * unit_v<BF16>(), tab);
+    if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
 }
 
 // ---------------------------------------------------------------------------
-// Draw kernel (C): one token per sampled request from one row pair, in fp64.
-//   after a rejection at n: r = max(0, p_n - q_n)   (p_n if that has no mass)
-//   without one:            r = p_d
-// The draw compares u*R against prefix sums over V terms; fp32 terms would
-// move the drawn token for about one draw in a thousand.
+// Draw kernel: one workgroup per request that draws a token.
+//
+// After a rejection at n:  r = max(0, p_n - q_n), or p_n if that has no mass;
+// without one: r = p_d (target row d).  In units of P and Q (terms relative to
+// the row maxima), r = max(0, P - rho Q)/Sz with rho = Sz/Sy, which needs the
+// row sums before any term; the chunk pass therefore split the terms with an
+// estimate rho_hat of rho (from the row pass): D = sum over {P > rho_hat Q} of
+// (P - rho_hat Q) and Bq = sum of Q over the same set, so that
+// R_c = D + (rho_hat - rho) Bq is chunk c's residual mass.  The two sets
+// differ only on terms where P and rho Q agree to within the estimate's
+// relative error (about 1e-7), whose residual mass is negligible.  The draw
+// compares u*R with prefix sums in token order: the first token whose
+// inclusive prefix exceeds u*R, or the last token with mass if rounding
+// leaves none.
 // ---------------------------------------------------------------------------
 
-// Sampler terms of one chunk.  which: 0 = residual max(0, p - q), 1 = p.
-// psum[j] receives the sum of p over slot j's elements, in element order.
-template <bool BF16>
-__device__ void sampler_terms(const Params &P, int b, const ReqDesc &desc, const S1Part &tot, int vbeg, int which,
-                              const double *tab, double (&val)[US][RowView<BF16>::EPV], double (&psum)[US])
+// Terms of the chosen distribution at the elements of vector vi (rescan):
+//   which 0: residual max(0, P - rho Q);  which 1: P.
+template <bool BF16, bool ALIGNED>
+__device__ __forceinline__ void slot_terms(const DrawRows<BF16> &dr, int which, double rho, int vi, const uint4 &rz,
+                                           const uint4 &ry, const double *tab, double (&val)[RowView<BF16>::EPV])
 {
     constexpr int EPV = RowView<BF16>::EPV;
-    const int K = P.K, V = P.V;
-    const int64_t esz = BF16 ? 2 : 4;
-    const double cd = LOG2E / (double)desc.T;
-    const double invSz = 1.0 / tot.sz;
     int flag = 0;
-    float f[US][EPV];
-    const RowView<BF16> rz((const char *)P.target + ((int64_t)b * (K + 1) + desc.n) * V * esz, V);
-    load_sampler_chunk<BF16>(rz, vbeg, f, flag);
+    float f[EPV], g[EPV];
+    chunk_vec<BF16>(dr.rz, vi, rz, f, flag);
+    if (which == 0) draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry, g);
 #pragma unroll
-    for (int j = 0; j < US; ++j) {
-        double ps = 0.0;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            val[j][e] = exp2_tab(((double)f[j][e] - (double)tot.mz) * cd, tab) * invSz;
-            ps += val[j][e];
-        }
-        psum[j] = ps;
-    }
-    if (which == 0) {
-        const double invSy = 1.0 / tot.sy;
-        const char *yrow = (const char *)P.draft + ((int64_t)b * K + desc.n) * V * esz;
-        const RowView<BF16> ry(yrow, V);
-        if (ry.head == rz.head) {
-            load_sampler_chunk<BF16>(ry, vbeg, f, flag);   // same vector grid: same tokens per lane
+    for (int e = 0; e < EPV; ++e) {
+        const double p = exp2_tab(fma((double)f[e], dr.cd, -dr.mzc), tab);
+        if (which == 0) {
+            const double q = exp2_tab(fma((double)g[e], dr.cd, -dr.myc), tab);
+            const double t = fma(-rho, q, p);
+            val[e] = t > 0.0 ? t : 0.0;
         } else {
-            // The two rows start at different offsets within a 16-byte vector
-            // (V * element size is not a multiple of 16): read the draft by
-            // token index on the target row's grid.
-#pragma unroll
-            for (int j = 0; j < US; ++j) {
-                const int vi = vbeg + j * WG + (int)threadIdx.x;
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const int x = rz.elem(vi, e);
-                    f[j][e] = (x >= 0 && x < V) ? load_logit<BF16>(yrow, x) : -INFINITY;
-                }
-            }
+            val[e] = p;
         }
-#pragma unroll
-        for (int j = 0; j < US; ++j)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const double qv = exp2_tab(((double)f[j][e] - (double)tot.my) * cd, tab) * invSy;
-                const double dlt = val[j][e] - qv;
-                val[j][e] = dlt > 0.0 ? dlt : 0.0;
-            }
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(WG) void draw_kernel(Params P)
 {
-    constexpr int EPV = RowView<BF16>::EPV;
-    constexpr int CS_LDS = 512;
+    constexpr int EPV = RowView<BF16>::EPV, UV = unit_v<BF16>(), UPT = UNITS_MAX / WG;
     __shared__ double tab[EXP2_TAB];
-    __shared__ double sm4[NWAVE];
-    __shared__ int sh_last;
-    __shared__ S2Part parts[CS_LDS];
-    __shared__ double sh_base, sh_target;
-    __shared__ int sh_c, sh_which, sh_over;
     __shared__ RedSmem sm;
-    const int b = blockIdx.y, c = blockIdx.x;
-    const ReqDesc desc = P.ws.req[b];
-    if (desc.state == SREQ_NONE) return;
-    const S1Part tot = P.ws.s1tot[b];
-    if (tot.bad) {   // the bonus row holds NaN, +inf or nothing but -inf
-        if (c == 0 && wave_id() == 0) mark_bad_request(P, b);
-        return;
-    }
+    __shared__ double sm4[NWAVE];
+    __shared__ double sh_base;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const DrawRec rec = P.ws.rec[b];
+    if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
     init_exp2_table(tab);
-    const bool resid = desc.state == SREQ_RESID;
-    const int vbeg_own = c * US * WG;
+    const bool resid = rec.state == SREQ_RESID;
+    const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
+    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
 
-    // chunk totals of r (and of p, for the all-zero-residual fallback)
-    // (summed in the same order as the rescan below, so the chunk located
-    // from these totals is the one the rescan walks)
-    double val[US][EPV], psum[US];
-    double total_r = 0.0, total_p = 0.0;
-    sampler_terms<BF16>(P, b, desc, tot, vbeg_own, resid ? 0 : 1, tab, val, psum);
+    // combine the unit sums; thread t holds units t*per .. t*per + per - 1
+    const ChunkPart *cp = P.ws.cp + (int64_t)b * P.cs;
+    const int ncs = P.cs;
+    const int per = (int)ceil_div(ncs, WG);   // <= UPT
+    const int u0 = tid * per;
+    ChunkPart pa[UPT];
 #pragma unroll
-    for (int j = 0; j < US; ++j) {
-        double vs = 0.0;
+    for (int h = 0; h < UPT; ++h) {
+        const int j = u0 + h;
+        if (h < per && j < ncs) pa[h] = cp[j];
+        else pa[h] = ChunkPart{0.0, 0.0, 0.0, 0.0, -INFINITY, 0, {0, 0}};
+    }
+    double tot[UPT];
+    double rho = 0.0;
+    int which = 1;
+    float Mb = 0.0f;
+    bool bad = false;
+    if (resid) {
+        double lz = 0.0, ly = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) vs += val[j][e];
-        double t;
-        (void)wg_excl_scan(vs, sm4, t);
-        total_r += t;
-        if (resid) {
-            (void)wg_excl_scan(psum[j], sm4, t);
-            total_p += t;
+        for (int h = 0; h < UPT; ++h) {
+            lz += pa[h].sz;
+            ly += pa[h].sy;
         }
-    }
-    if (!resid) total_p = total_r;   // the bonus draw's distribution is p itself
-    if (threadIdx.x == 0) {
-        const S2Part part = {total_r, total_p};
-        put_s2(P.ws.s2 + (int64_t)b * P.cs + c, part);
-        wait_stores();
-        const uint32_t old = count_in(&P.ws.s2cnt[b]);
-        sh_last = (old == (uint32_t)(P.cs - 1));
-    }
-    __syncthreads();
-    if (!sh_last) return;
-    after_count();
-
-    // Last chunk of request b: locate u*R among the chunk totals.
-    for (int j = threadIdx.x; j < P.cs; j += WG) parts[j] = get_s2(P.ws.s2 + (int64_t)b * P.cs + j);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double R = 0.0;
-        for (int j = 0; j < P.cs; ++j) R += parts[j].r;
-        int which = resid ? 0 : 1;
-        if (resid && R == 0.0) {   // no residual mass: fall back to p
-            which = 1;
-            R = 0.0;
-            for (int j = 0; j < P.cs; ++j) R += parts[j].p;
+        const double Sz = wg_sum(lz, sm);
+        const double Sy = wg_sum(ly, sm);
+        bad = !(Sz > 0.0) || !(Sy > 0.0);
+        rho = bad ? 0.0 : Sz / Sy;
+        double lr = 0.0;
+#pragma unroll
+        for (int h = 0; h < UPT; ++h) {
+            tot[h] = fmax(0.0, fma(rec.rho_hat - rho, pa[h].bq, pa[h].d));
+            lr += tot[h];
         }
-        const double target = (double)P.u_sample[b] * R;
-        double cum = 0.0, base = 0.0;
-        int cstar = -1, lastpos = -1;
-        for (int j = 0; j < P.cs; ++j) {
-            const double t = which == 0 ? parts[j].r : parts[j].p;
-            if (t > 0.0) lastpos = j;
-            const double nc = cum + t;
-            if (cstar < 0 && nc > target) { cstar = j; base = cum; }
-            cum = nc;
+        if (wg_sum(lr, sm) > 0.0) {
+            which = 0;
+        } else {   // no residual mass: draw from p
+#pragma unroll
+            for (int h = 0; h < UPT; ++h) tot[h] = pa[h].sz;
         }
-        sh_over = cstar < 0;
-        sh_c = cstar < 0 ? lastpos : cstar;
-        sh_base = base;
-        sh_target = target;
-        sh_which = which;
+    } else {
+        float lm = -INFINITY;
+        int lb = 0;
+#pragma unroll
+        for (int h = 0; h < UPT; ++h) {
+            lm = fmaxf(lm, pa[h].m);
+            lb |= pa[h].bad;
+        }
+        Mb = wg_max(lm, sm);
+        bad = wg_or(lb, sm) != 0;
+        bad |= (Mb == -INFINITY || Mb == INFINITY);
+#pragma unroll
+        for (int h = 0; h < UPT; ++h)
+            tot[h] = (pa[h].m == -INFINITY || bad) ? 0.0
+                                                    : pa[h].sz * exp2_tab(((double)pa[h].m - (double)Mb) * dr.cd, tab);
     }
-    __syncthreads();
-    const int cs = sh_c;
-    if (cs < 0) {   // no chunk holds positive mass (unreachable for valid statistics)
-        if (threadIdx.x < 64) mark_bad_request(P, b);
+    // exclusive prefix of the unit totals in unit order; the total R
+    double lsum = 0.0;
+#pragma unroll
+    for (int h = 0; h < UPT; ++h) lsum += tot[h];
+    double Rt;
+    const double base0 = wg_excl_scan(lsum, sm4, Rt);
+    if (!(Rt > 0.0)) bad = true;
+    const double target = (double)P.u_sample[b] * Rt;
+    // first unit whose inclusive prefix exceeds u*R; last unit with mass
+    int cand = 0x7fffffff, lastc = -1;
+    double run = base0, cbase = 0.0;
+#pragma unroll
+    for (int h = 0; h < UPT; ++h) {
+        const int j = u0 + h;
+        if (cand == 0x7fffffff && h < per && j < ncs && run + tot[h] > target) {
+            cand = j;
+            cbase = run;
+        }
+        if (tot[h] > 0.0) lastc = j;
+        run += tot[h];
+    }
+    {
+        float m = (cand == 0x7fffffff) ? -INFINITY : 0.0f;
+        int i = cand;
+        wg_argmax(m, i, sm);
+        const int cw = (m == -INFINITY) ? 0x7fffffff : i;
+        if (cw != 0x7fffffff && cw == cand) sh_base = cbase;
+        cand = cw;
+        float m2 = (lastc < 0) ? -INFINITY : 0.0f;
+        int i2 = (lastc < 0) ? 0x7fffffff : (0x7fffffff - lastc);
+        wg_argmax(m2, i2, sm);   // contains a barrier: sh_base is visible after it
+        lastc = (m2 == -INFINITY) ? -1 : (0x7fffffff - i2);
+    }
+    const bool over = cand == 0x7fffffff;
+    const int cstar = over ? lastc : cand;
+    if (bad || cstar < 0) {   // the bonus row holds NaN, +inf or nothing but -inf
+        if (wave_id() == 0) {
+            const ReqDesc bd = {SREQ_BAD, 0, -1, rec.T};
+            write_outputs(P, b, 0, bd, nullptr, -1);
+        }
         return;
     }
-    const double base = sh_base, target = sh_target;
-    const int which = sh_which;
-    const bool over = sh_over;
-    const int vbeg = cs * US * WG;
+    const double base = over ? 0.0 : sh_base;
 
-    // Rescan chunk cs: first positive-mass element whose prefix exceeds
-    // u*R; the chunk's last positive-mass element if none does.
-    sampler_terms<BF16>(P, b, desc, tot, vbeg, which, tab, val, psum);
-    const RowView<BF16> rz((const char *)P.target + ((int64_t)b * (P.K + 1) + desc.n) * P.V * (BF16 ? 2 : 4), P.V);
+    // rescan unit cstar in token order: thread t takes vectors k*WG + t
+    DrawRows<BF16> dr2 = dr;
+    if (!resid) dr2.mzc = (double)Mb * dr.cd;
+    const int wsel = resid ? which : 1;
     int first = 0x7fffffff, lastp = -1;
     double carry = 0.0;
+    uint4 rz[UV / WG], ry[UV / WG];
+    issue_vecs<BF16, UV / WG>(dr2.rz, cstar * UV + tid, WG, rz);
+    // the draft row exists only for a residual draw (a bonus draw reads
+    // target row d; draft row d may lie past the draft logits)
+    if (wsel == 0 && ALIGNED) issue_vecs<BF16, UV / WG>(dr2.dc.ry, cstar * UV + tid, WG, ry);
 #pragma unroll
-    for (int j = 0; j < US; ++j) {
+    for (int k = 0; k < UV / WG; ++k) {
+        const int vi = cstar * UV + k * WG + tid;
+        double val[EPV];
+        slot_terms<BF16, ALIGNED>(dr2, wsel, rho, vi, rz[k], ry[k], tab, val);
         double vs = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) vs += val[j][e];
+        for (int e = 0; e < EPV; ++e) vs += val[e];
         double t;
         const double ex = wg_excl_scan(vs, sm4, t);
         const double slot0 = carry + ex;
-        const int vi = vbeg + j * WG + (int)threadIdx.x;
         double part = 0.0;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-            part += val[j][e];
-            const int x = rz.elem(vi, e);
-            if (val[j][e] > 0.0 && x >= 0 && x < P.V) {
+            part += val[e];
+            const int x = dr.rz.elem(vi, e);
+            if (val[e] > 0.0 && x >= 0 && x < P.V) {
                 if (x > lastp) lastp = x;
                 if (first == 0x7fffffff && base + (slot0 + part) > target) first = x;
             }
@@ -1428,18 +1425,21 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
     {
         float m = (first == 0x7fffffff) ? -INFINITY : 0.0f;
         int i = first;
-        wg_argmax(m, i, sm);   // lowest index among threads holding a candidate
+        wg_argmax(m, i, sm);   // lowest token among threads holding a crossing
         fi = (m == -INFINITY) ? 0x7fffffff : i;
     }
     {
         float m = (lastp < 0) ? -INFINITY : 0.0f;
         int i = (lastp < 0) ? 0x7fffffff : (0x7fffffff - lastp);
-        wg_argmax(m, i, sm);   // highest index among threads holding one
+        wg_argmax(m, i, sm);   // highest token with mass
         lp = (m == -INFINITY) ? -1 : (0x7fffffff - i);
     }
-    if (threadIdx.x == 0) {
-        const int tok = (!over && fi != 0x7fffffff) ? fi : lp;
-        P.out_tokens[(int64_t)b * (P.K + 1) + desc.n] = tok;
+    const int tok = (!over && fi != 0x7fffffff) ? fi : lp;
+    if (tok >= 0) {
+        if (tid == 0) P.out_tokens[(int64_t)b * (P.K + 1) + rec.n] = tok;
+    } else if (wave_id() == 0) {
+        const ReqDesc bd = {SREQ_BAD, 0, -1, rec.T};
+        write_outputs(P, b, 0, bd, nullptr, -1);
     }
 }
 
@@ -1675,8 +1675,8 @@ sv_status check_ws(void *ws, size_t ws_bytes, const Layout &L)
     return SV_OK;
 }
 
-// Row pass (A) then finish kernel (B) with grid.x = chunks (1 when nothing
-// is drawn), then, for sampled calls, the draw kernel (C).
+// Row pass, then the finish kernel with grid.x = sampler units / 4 (1 when
+// nothing is drawn), then for sampled calls the draw kernel.
 sv_status launch(Params &P, hipStream_t stream)
 {
     const int64_t nv = nvec_max(P.V, P.bf16 ? 8 : 4);
@@ -1685,19 +1685,24 @@ sv_status launch(Params &P, hipStream_t stream)
     const size_t lds_a = sizeof(int) * (size_t)(3 * P.B + 1);
     int64_t grid = (int64_t)cu_count() * row_wgs_per_cu(P.bf16, lds_a);
     grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div(rows_max * ceil_div(nv, WVEC), NWAVE)));
-    const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1);
-    const dim3 grid_b((unsigned)(P.mode == MODE_SAMPLE ? P.cs : 1), (unsigned)P.B);
-    const dim3 grid_c((unsigned)P.cs, (unsigned)P.B);
+    const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1) + sizeof(float2) * (size_t)P.K;
+    const bool sample = P.mode == MODE_SAMPLE;
+    const dim3 grid_b((unsigned)(sample ? ceil_div(P.cs, NWAVE) : 1), (unsigned)P.B);
     (void)hipGetLastError();
+#define SV_LAUNCH_PATH(BF, AL)                                                                              \
+    do {                                                                                                    \
+        hipLaunchKernelGGL(row_pass_kernel<BF>, dim3((unsigned)grid), dim3(WG), lds_a, stream, P);           \
+        hipLaunchKernelGGL((finish_kernel<BF, AL>), grid_b, dim3(WG), lds_b, stream, P);                    \
+        if (sample) hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P); \
+    } while (0)
     if (P.bf16) {
-        hipLaunchKernelGGL(row_pass_kernel<true>, dim3((unsigned)grid), dim3(WG), lds_a, stream, P);
-        hipLaunchKernelGGL(finish_kernel<true>, grid_b, dim3(WG), lds_b, stream, P);
-        if (P.mode == MODE_SAMPLE) hipLaunchKernelGGL(draw_kernel<true>, grid_c, dim3(WG), 0, stream, P);
+        if (P.aligned) SV_LAUNCH_PATH(true, true);
+        else SV_LAUNCH_PATH(true, false);
     } else {
-        hipLaunchKernelGGL(row_pass_kernel<false>, dim3((unsigned)grid), dim3(WG), lds_a, stream, P);
-        hipLaunchKernelGGL(finish_kernel<false>, grid_b, dim3(WG), lds_b, stream, P);
-        if (P.mode == MODE_SAMPLE) hipLaunchKernelGGL(draw_kernel<false>, grid_c, dim3(WG), 0, stream, P);
+        if (P.aligned) SV_LAUNCH_PATH(false, true);
+        else SV_LAUNCH_PATH(false, false);
     }
+#undef SV_LAUNCH_PATH
     return hip_status("kernel launch");
 }
 
@@ -1711,7 +1716,8 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
     P.bf16 = dt == SV_BF16;
     P.mode = mode;
     P.cpr_max = L.cpr_max;
-    P.cs = (int)ceil_div(nvec_max(V, P.bf16 ? 8 : 4), (int64_t)WG * US);
+    P.cs = (int)ceil_div(nvec_max(V, P.bf16 ? 8 : 4), (int64_t)UNIT_E / (P.bf16 ? 8 : 4));
+    P.aligned = ((int64_t)V * (P.bf16 ? 2 : 4)) % 16 == 0;
     P.ws = carve(ws, L, B);
     return P;
 }
