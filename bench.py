@@ -1,23 +1,37 @@
 """Benchmark of batched draft verification on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
 
 One step = one spec_verify_sample call (row statistics, accept test,
 first-rejection scan, residual/bonus draw, output assembly) over the dense
 D-cut workload at full depth: B=64 requests, K=16 drafted tokens, V=128000,
-bf16 logits, T=1, every request verified at depth 16 (B*(K+1) = 1088 target
-rows and 1024 draft rows per step).  Inputs are seeded synthetic logits
-already resident in HBM; input copies are rotated so the 256 MB
-memory-side cache cannot serve a step from the previous one.
+bf16 logits, T=1, every request verified at depth 16 (B*(K+1) = 1088 verified
+target rows, 1024 draft rows).  Inputs are seeded synthetic logits already
+resident in HBM; input copies are rotated so the 256 MB memory-side cache
+cannot serve a step from the previous one.
 
 Printed: one JSON line with the verified-rows/s metric, the roofline of the
-dominant kernel (HIP events on the launch stream), the oracle CPU baseline on
-a bounded sample, and secondary measurements (greedy, K=3 chat shape, and
-the D-cut pipeline: confidence + dcut_allocate(384) + ragged verify).
+dominant kernel (the row-statistics pass; its duration from HIP events that
+the library records on the launch stream around each kernel of every timed
+call), the oracle CPU baseline on a bounded sample, and secondary
+measurements (greedy, the K=3 chat shape, the D-cut pipeline, the mixed fp32
+batch).
+
+Profiling helpers (run under rocprofv3; see the summaries under profiles/):
+    python bench.py --pmc-pass            a few headline steps, then a plain
+                                          device copy of 512 MiB (counter
+                                          calibration); prints the kernel names
+    python bench.py --pmc-summary DIR...  reads rocprofv3 counter CSVs from the
+                                          given directories (one FETCH_SIZE run,
+                                          one WRITE_SIZE run; no GPU needed) and
+                                          prints the scaled per-launch traffic
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,25 +40,105 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "draft_verification_verify_amd", "csrc", "specverify.hip")
+ROW_PASS_KERNEL = "row_pass_kernel"
+CALIB_BYTES = 512 * 2**20          # fp32 elements read once and written once by the calibration copy
+CALIB_KERNEL = "neg_kernel"
+
+# HBM traffic of one row-statistics launch on the headline workload (bytes),
+# from two rocprofv3 --pmc runs of `bench.py --pmc-pass` (FETCH_SIZE, then
+# WRITE_SIZE), each scaled by what the same counter reads for the calibration
+# copy in that run.  It describes the kernel source with this SHA-256 only;
+# for any other source it is reported as null.
+ROW_PASS_TRAFFIC = {"source_sha256": "74d91a599549029b4754d69f3c1c1ea908f04f703f7f320ae97fb0c37d10f3f9",
+                    "fetch_bytes": 540079945, "write_bytes": 527460}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR")
     return ap.parse_args()
 
 
+def source_sha256() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def row_pass_rows(w, mode: str, depth=None) -> int:
+    """Logit rows the row-statistics kernel reads: target rows 0..d_b of a
+    request verified by the greedy rule; target rows 0..d_b-1 and draft rows
+    0..d_b-1 of a sampled request (its target row d_b is read only by a bonus
+    draw, in the sampler)."""
+    d = np.full(w.B, w.K) if depth is None else np.asarray(depth)
+    if mode == "greedy":
+        return int(np.sum(d + 1))
+    return int(np.sum(np.where(w.temperature > 0, 2 * d, d + 1)))
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- pmc summary
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    out = []
+    for f in files:
+        with open(f, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def pmc_summary(dirs):
+    """Per-kernel mean of each counter (KiB per dispatch as rocprofv3 reports
+    FETCH_SIZE / WRITE_SIZE), the calibration factor from the plain copy, and
+    the scaled bytes per launch of the row-statistics kernel."""
+    per = {}
+    for d in dirs:
+        for r in _counter_rows(d):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            ctr = r.get("Counter_Name") or r.get("Counter-Name")
+            val = float(r.get("Counter_Value") or r.get("Counter-Value") or 0.0)
+            disp = r.get("Dispatch_Id") or r.get("Dispatch-Id") or r.get("Correlation_Id")
+            per.setdefault(ctr, {}).setdefault(name, {}).setdefault(disp, 0.0)
+            per[ctr][name][disp] += val       # sum over the rows of one dispatch
+    res = {"counters": {}}
+    for ctr, kernels in per.items():
+        row = [v for n, v in kernels.items() if ROW_PASS_KERNEL in n]
+        cal = [v for n, v in kernels.items() if CALIB_KERNEL in n]
+        if not row or not cal:
+            continue
+        row_kib = float(np.mean([x for v in row for x in v.values()]))
+        cal_kib = float(np.mean([x for v in cal for x in v.values()]))
+        factor = CALIB_BYTES / (cal_kib * 1024.0)
+        res["counters"][ctr] = {"row_pass_kib_per_dispatch": row_kib, "copy_kib_per_dispatch": cal_kib,
+                                "copy_known_bytes": CALIB_BYTES, "scale": factor,
+                                "row_pass_bytes_per_launch": row_kib * 1024.0 * factor}
+    res["source_sha256"] = source_sha256()
+    print(json.dumps(res, indent=1))
+
+
+# --------------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU; multi-GPU runs are not part of "
-                                   "this build (requests shard with no exchange; see the design notes)",
+        print(json.dumps({"error": "this benchmark measures one GPU: the verification path has no "
+                                   "multi-GPU part in this library (requests shard with no exchange)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -61,18 +155,16 @@ def main():
     torch.cuda.init()
     stream = torch.cuda.current_stream()
 
-    def log(msg):
-        print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
     # ------------------------------------------------------------------ inputs
     log("generating dense D-cut workload B=64 K=16 V=128000 bf16 (T=1)")
     w = synth.dcut_ragged(args.seed, T=1.0)
     B, K, V = w.B, w.K, w.V
     rows = synth.rows_verified(w)
     algo_bytes = synth.algorithmic_bytes(w, "sample")
-    working = algo_bytes
-    ncopy = max(2, -(-512 * 2**20 // working) + 1)
-    log(f"rows/step={rows} algorithmic bytes/step={algo_bytes/1e6:.1f} MB, rotating {ncopy} input copies")
+    rp_bytes = row_pass_rows(w, "sample") * V * 2
+    ncopy = max(2, -(-512 * 2**20 // algo_bytes) + 1)
+    log(f"rows/step={rows} algorithmic bytes/step={algo_bytes/1e6:.1f} MB "
+        f"(row pass {rp_bytes/1e6:.1f} MB), rotating {ncopy} input copies")
     tgt0, dr0 = dev(w.target), dev(w.draft)
     copies = [(tgt0, dr0)] + [(tgt0.clone(), dr0.clone()) for _ in range(ncopy - 1)]
     tok, T, ua, us = dev(w.tokens), dev(w.temperature), dev(w.u_accept), dev(w.u_sample)
@@ -80,18 +172,23 @@ def main():
     nacc = torch.empty((B,), dtype=torch.int32, device="cuda")
     pd = torch.empty((B, K), dtype=torch.float32, device="cuda")
     qd = torch.empty((B, K), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(sv.workspace_size(B, K, V), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(sv.workspace_size(B, 16, 152064), dtype=torch.uint8, device="cuda")
 
     def step(i):
         t, d = copies[i % ncopy]
         sv.verify_sample(t, d, tok, T, ua, us, out_tokens=out, num_accepted=nacc, p_draft=pd,
                          q_draft=qd, workspace=ws, stream=stream)
 
-    def timed(fn, steps, warmup):
+    def timed(fn, steps, warmup, stages=False):
+        """Warm up, then time exactly `steps` calls between two events on the
+        launch stream (synchronised on both sides).  With `stages`, the library
+        also records its per-kernel events for every timed call."""
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        if stages:
+            sv.timing_begin(steps)
         t0 = time.perf_counter()
         evs[0].record(stream)
         for i in range(steps):
@@ -100,14 +197,39 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-        return wall, per
+        st = sv.timing_end(steps) if stages else None
+        return wall, per, st
+
+    if args.pmc_pass:
+        for i in range(max(args.warmup, 1) + max(min(args.steps, 5), 1)):
+            step(i)
+        src = torch.rand(CALIB_BYTES // 4, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": "done", "row_pass_kernel": ROW_PASS_KERNEL,
+                          "calibration": f"torch.neg over {CALIB_BYTES} B of fp32 (reads and writes that many)"}))
+        return
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    wall, per = timed(step, args.steps, args.warmup)
+    wall, per, _ = timed(step, args.steps, args.warmup)
     ms = float(np.mean(per))
     value = rows / (ms * 1e-3)
-    n_mean = float(host_mean(nacc))
-    achieved = algo_bytes / (ms * 1e-3) / 1e9
+    # the same steps again with the library's per-kernel events armed (the
+    # event markers add a few microseconds per call, so they stay out of the
+    # headline region)
+    log(f"timing {args.steps} steps with per-kernel events")
+    _, sper, st = timed(step, args.steps, 2, stages=True)
+    st = np.asarray(st, dtype=np.float64)
+    stage_ms = st.mean(axis=0)
+    rp_ms = float(stage_ms[0])
+    achieved = rp_bytes / (rp_ms * 1e-3) / 1e9
+    n_mean = float(nacc.float().mean().item())
+    sha = source_sha256()
+    traffic = None
+    if ROW_PASS_TRAFFIC["source_sha256"] == sha and ROW_PASS_TRAFFIC["fetch_bytes"] is not None:
+        traffic = float(ROW_PASS_TRAFFIC["fetch_bytes"] + ROW_PASS_TRAFFIC["write_bytes"])
     result = {
         "metric": "verified logit rows/sec (B×(K+1) rows of V) + % of HBM peak, K=3 and K=16",
         "value": value,
@@ -121,23 +243,29 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "dense D-cut verification at full depth: B=64 K=16 V=128000 bf16, "
+        "config": {"workload": "dense D-cut verification at full depth: B=64 K=16 V=128000 bf16 logits, "
                                "rejection sampling at T=1, draft noise sigma_b~U(0.3,2.0)",
                    "global_batch": B, "K": K, "V": V, "rows_per_step": rows, "parallelism": "none (1 GPU)"},
-        "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBS,
+        "pct_hbm_peak": 100.0 * algo_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": algo_bytes,
         "ms_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
+        "stage_ms": {"row_pass": rp_ms, "finish": float(stage_ms[1]), "draw": float(stage_ms[2]),
+                     "step_with_events": float(np.mean(sper))},
         "wall_s_timed": wall,
         "mean_accepted": n_mean,
         "tau_incl_bonus": n_mean + 1.0,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "whole spec_verify_sample call (row pass + 2 sampler kernels)",
-                     "algorithmic_bytes_per_launch": algo_bytes},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": ROW_PASS_KERNEL + "<bf16> (row statistics)",
+                     "algorithmic_bytes_per_launch": rp_bytes,
+                     "avg_launch_ms": rp_ms},
+        "kernel_source_sha256": sha,
     }
 
     # -------------------------------------------------------------- secondary
     if not args.no_secondary:
         sec = {}
+        steps2, warm2 = max(args.steps // 2, 10), max(args.warmup // 2, 3)
         # greedy at full depth, same shape (T=0 drafts are the draft argmax)
         wg = synth.dcut_ragged(args.seed, T=0.0)
         gt = dev(wg.target)
@@ -147,12 +275,15 @@ def main():
         def gstep(i):
             sv.verify_greedy(gcopies[i % len(gcopies)], gtok, out_tokens=out, num_accepted=nacc, workspace=ws,
                              stream=stream)
-        _, gper = timed(gstep, args.steps, args.warmup)
+        _, gper, gst = timed(gstep, steps2, warm2, stages=True)
         gms = float(np.mean(gper))
         gbytes = synth.algorithmic_bytes(wg, "greedy")
+        grp = float(np.mean([s[0] for s in gst]))
         sec["greedy_dense_B64_K16"] = {"rows_per_s": rows / (gms * 1e-3), "ms": gms,
                                        "GB_s": gbytes / (gms * 1e-3) / 1e9,
-                                       "pct_hbm_peak": 100 * gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                                       "pct_hbm_peak": 100 * gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "row_pass_ms": grp,
+                                       "row_pass_GB_s": gbytes / (grp * 1e-3) / 1e9}
         del gcopies, gt
         # K=3 chat shape (B=4), sampled and greedy
         for mode in ("sample", "greedy"):
@@ -168,7 +299,7 @@ def main():
                                      want_probs=False, workspace=ws, stream=stream)
                 else:
                     sv.verify_greedy(ct, ctok, out_tokens=cout, num_accepted=cn, workspace=ws, stream=stream)
-            _, cper = timed(cstep, args.steps, args.warmup)
+            _, cper, _ = timed(cstep, steps2, warm2)
             cms = float(np.mean(cper))
             cb = synth.algorithmic_bytes(wc, mode)
             crow = synth.rows_verified(wc)
@@ -185,7 +316,7 @@ def main():
             sv.dcut_allocate(conf, w.budget, depth_out=depth, stream=stream)
             sv.verify_sample(t, d, tok, T, ua, us, depth, out_tokens=out, num_accepted=nacc, p_draft=pd,
                              q_draft=qd, workspace=ws, stream=stream)
-        _, pper = timed(pstep, args.steps, args.warmup)
+        _, pper, _ = timed(pstep, steps2, warm2)
         pms = float(np.mean(pper))
         dep = depth.cpu().numpy()
         prow = int(np.sum(dep + 1))
@@ -194,26 +325,47 @@ def main():
             "bytes_per_step": int((B * K + prow + int(dep.sum())) * V * 2),
             "note": "confidence pass reads all 1024 draft rows; ragged verify reads sum(d_b+1) target "
                     "and sum(d_b) draft rows"}
+        del copies
+        # mixed fp32 batch: per-request K_b and T_b, dcut_allocate(512), one sampled launch
+        wm = synth.mixed(args.seed)
+        mt, md = dev(wm.target), dev(wm.draft)
+        mtok, mT, mua, mus = dev(wm.tokens), dev(wm.temperature), dev(wm.u_accept), dev(wm.u_sample)
+        mK = dev(wm.max_depth)
+        mconf = torch.empty((wm.B, wm.K), dtype=torch.float32, device="cuda")
+        mdep = torch.empty((wm.B,), dtype=torch.int32, device="cuda")
+        mout = torch.empty((wm.B, wm.K + 1), dtype=torch.int32, device="cuda")
+        mn = torch.empty((wm.B,), dtype=torch.int32, device="cuda")
+
+        def mstep(i):
+            sv.draft_confidence(md, mK, conf=mconf, workspace=ws, stream=stream)
+            sv.dcut_allocate(mconf, wm.budget, mK, depth_out=mdep, stream=stream)
+            sv.verify_sample(mt, md, mtok, mT, mua, mus, mdep, out_tokens=mout, num_accepted=mn,
+                             want_probs=False, workspace=ws, stream=stream)
+        _, mper, _ = timed(mstep, steps2, warm2)
+        mms = float(np.mean(mper))
+        mdv = mdep.cpu().numpy()
+        mrow = int(np.sum(mdv + 1))
+        sec["mixed_fp32_B64_V152064_budget512"] = {
+            "verified_rows_per_s": mrow / (mms * 1e-3), "ms": mms, "rows_per_step": mrow,
+            "note": "confidence over all max_depth draft rows + dcut_allocate + one mixed-K/T sampled launch; "
+                    "inputs not rotated (fits the memory-side cache partly)"}
         result["secondary"] = sec
 
     # ----------------------------------------------------------- CPU baseline
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
-        nreq = 4
-        log(f"timing the CPU oracle on {nreq} of the {B} requests")
-        t0 = time.perf_counter()
-        oracle.verify_sample(w.target[:nreq], w.draft[:nreq], w.tokens[:nreq], w.temperature[:nreq],
-                             w.u_accept[:nreq], w.u_sample[:nreq])
-        dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": nreq * (K + 1) / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                                  "sample": f"{nreq} of the 64 requests of the same workload "
-                                            f"({nreq * (K + 1)} verified rows, {dt:.1f} s), single-threaded C, fp64"}
+        log("timing the CPU oracle on the same workload (all 64 requests, repeated to >= 10 s)")
+        reps, t_tot = 0, 0.0
+        while t_tot < 10.0 and reps < 8:
+            t0 = time.perf_counter()
+            oracle.verify_sample(w.target, w.draft, w.tokens, w.temperature, w.u_accept, w.u_sample)
+            t_tot += time.perf_counter() - t0
+            reps += 1
+        result["cpu_baseline"] = {"value": reps * rows / t_tot, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the full headline batch (64 requests, {rows} verified rows) "
+                                            f"run {reps} times in {t_tot:.1f} s; single-threaded C, fp64"}
     print(json.dumps(result), flush=True)
-
-
-def host_mean(t):
-    return float(t.float().mean().item())
 
 
 if __name__ == "__main__":

@@ -61,6 +61,10 @@ def _load() -> ctypes.CDLL:
     L.spec_draft_confidence.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, sz, vp]
     L.dcut_allocate.restype = ctypes.c_int
     L.dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.spec_verify_timing_begin.restype = ctypes.c_int
+    L.spec_verify_timing_begin.argtypes = [i32]
+    L.spec_verify_timing_end.restype = ctypes.c_int
+    L.spec_verify_timing_end.argtypes = [ctypes.POINTER(ctypes.c_float), i32]
     if L.spec_verify_abi_version() != 1:
         raise ImportError("libspecverify ABI version mismatch")
     return L
@@ -69,12 +73,29 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify_last_error",
-            "spec_verify_workspace_size",
+            "spec_verify_workspace_size", "spec_verify_timing_begin", "spec_verify_timing_end",
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate")
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
     return int(lib.spec_verify_workspace_size(B, K, V))
+
+
+def timing_begin(n: int) -> None:
+    """Arm per-kernel event timing for this thread's next ``n`` verification calls."""
+    st = lib.spec_verify_timing_begin(int(n))
+    if st:
+        _raise("spec_verify_timing_begin", st)
+
+
+def timing_end(n: int):
+    """Wait for the armed calls and return an (n, 3) list of stage milliseconds:
+    row statistics, finish (merge, accept scan, sampler sums), draw."""
+    buf = (ctypes.c_float * (3 * max(int(n), 1)))()
+    st = lib.spec_verify_timing_end(buf, int(n))
+    if st:
+        _raise("spec_verify_timing_end", st)
+    return [[buf[3 * i + s] for s in range(3)] for i in range(int(n))]
 
 
 # ----------------------------------------------------------------------------

@@ -49,6 +49,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include "specverify.h"
 
@@ -1675,6 +1676,21 @@ sv_status check_ws(void *ws, size_t ws_bytes, const Layout &L)
     return SV_OK;
 }
 
+// Stage timing of the calling thread's calls (benchmark instrumentation):
+// four events per armed call, recorded on the call's stream around its
+// kernels.
+struct StageTiming {
+    std::vector<hipEvent_t> ev;
+    int armed = 0, used = 0;
+    ~StageTiming()
+    {
+        for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    }
+};
+thread_local StageTiming g_timing;
+
+inline hipEvent_t stage_event(int call, int s) { return g_timing.ev[(size_t)4 * call + s]; }
+
 // Row pass, then the finish kernel with grid.x = sampler units / 4 (1 when
 // nothing is drawn), then for sampled calls the draw kernel.
 sv_status launch(Params &P, hipStream_t stream)
@@ -1688,12 +1704,21 @@ sv_status launch(Params &P, hipStream_t stream)
     const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1) + sizeof(float2) * (size_t)P.K;
     const bool sample = P.mode == MODE_SAMPLE;
     const dim3 grid_b((unsigned)(sample ? ceil_div(P.cs, NWAVE) : 1), (unsigned)P.B);
+    const int tcall = g_timing.used < g_timing.armed ? g_timing.used++ : -1;
     (void)hipGetLastError();
+#define SV_MARK(s)                                                            \
+    do {                                                                      \
+        if (tcall >= 0) (void)hipEventRecord(stage_event(tcall, s), stream); \
+    } while (0)
 #define SV_LAUNCH_PATH(BF, AL)                                                                              \
     do {                                                                                                    \
+        SV_MARK(0);                                                                                         \
         hipLaunchKernelGGL(row_pass_kernel<BF>, dim3((unsigned)grid), dim3(WG), lds_a, stream, P);           \
+        SV_MARK(1);                                                                                         \
         hipLaunchKernelGGL((finish_kernel<BF, AL>), grid_b, dim3(WG), lds_b, stream, P);                    \
+        SV_MARK(2);                                                                                         \
         if (sample) hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P); \
+        SV_MARK(3);                                                                                         \
     } while (0)
     if (P.bf16) {
         if (P.aligned) SV_LAUNCH_PATH(true, true);
@@ -1703,6 +1728,7 @@ sv_status launch(Params &P, hipStream_t stream)
         else SV_LAUNCH_PATH(false, false);
     }
 #undef SV_LAUNCH_PATH
+#undef SV_MARK
     return hip_status("kernel launch");
 }
 
@@ -1725,6 +1751,41 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
 }  // namespace
 
 extern "C" {
+
+sv_status spec_verify_timing_begin(int32_t n)
+{
+    if (n < 0 || n > (1 << 20)) return SV_ERR_INVALID_ARG;
+    for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+    g_timing.ev.clear();
+    g_timing.armed = g_timing.used = 0;
+    (void)hipGetLastError();
+    for (int i = 0; i < 4 * n; ++i) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDefault) != hipSuccess) return hip_status("hipEventCreate");
+        g_timing.ev.push_back(e);
+    }
+    g_timing.armed = n;
+    return SV_OK;
+}
+
+sv_status spec_verify_timing_end(float *ms, int32_t n)
+{
+    if (n < 0 || n > g_timing.used || (n > 0 && !ms)) return SV_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    for (int i = 0; i < n; ++i) {
+        if (hipEventSynchronize(stage_event(i, 3)) != hipSuccess) return hip_status("hipEventSynchronize");
+        for (int s = 0; s < 3; ++s) {
+            float t = 0.0f;
+            if (hipEventElapsedTime(&t, stage_event(i, s), stage_event(i, s + 1)) != hipSuccess)
+                return hip_status("hipEventElapsedTime");
+            ms[3 * i + s] = t;
+        }
+    }
+    for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+    g_timing.ev.clear();
+    g_timing.armed = g_timing.used = 0;
+    return SV_OK;
+}
 
 int32_t spec_verify_abi_version(void) { return 1; }
 

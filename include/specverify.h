@@ -31,13 +31,13 @@
  *     library allocates no device memory and keeps no state between calls.
  *   Execution.  Calls are asynchronous and ordered on `stream`; a call that
  *     returns SV_OK has only enqueued work.  Calls that share a workspace must
- *     be ordered (the same stream, or synchronised): their kernels use the
- *     workspace's counters.
+ *     be ordered (the same stream, or synchronised): their kernels keep
+ *     partial results there.
  *   Workspace.  At least spec_verify_workspace_size(B, K, V) bytes,
- *     256-byte aligned, contents arbitrary: each call's kernels clear the
- *     counters they use before using them, so one workspace can serve calls
- *     of any shape that fits it.  It holds per-call scratch (row partials,
- *     counters, sampler partials) and nothing that outlives the call.
+ *     256-byte aligned, contents arbitrary: each call writes every part of
+ *     it that it later reads, so one workspace can serve calls of any shape
+ *     that fits it.  It holds per-call scratch (row partials, sampler
+ *     partials, per-request records) and nothing that outlives the call.
  *   Errors.  Arguments the host can check (null pointers, sizes, dtype,
  *     alignment, workspace size, budget) are rejected with a status before
  *     anything is enqueued.  Bad DATA is found on the device and reported per
@@ -88,6 +88,20 @@ const char *spec_verify_last_error(void);
  * spec_draft_confidence need for a batch of this shape; 0 for sizes the
  * library rejects. */
 size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V);
+
+/* Per-kernel timing for benchmarks (instrumentation; changes no result).
+ * spec_verify_timing_begin(n) creates 4n HIP events on the current device and
+ * arms them for the calling thread: each of its next n calls of
+ * spec_verify_greedy, spec_verify_sample or spec_draft_confidence records
+ * four of them on its own stream -- before the row-statistics kernel, after
+ * it, after the finish kernel and after the draw kernel.
+ * spec_verify_timing_end(ms, n) waits for the first n armed calls' events,
+ * writes ms[3i + s] = milliseconds of stage s of call i (0 row statistics,
+ * 1 finish: merge, accept scan and sampler sums, 2 draw; a stage a call
+ * does not launch reads about 0) and releases all events.  n may not exceed
+ * the number of calls made since timing_begin (SV_ERR_INVALID_ARG). */
+sv_status spec_verify_timing_begin(int32_t n);
+sv_status spec_verify_timing_end(float *ms, int32_t n);
 
 /* Greedy (T = 0) verification.
  * For request b with depth d = depth[b] (or K when depth is NULL): drafted

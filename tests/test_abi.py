@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -38,6 +38,14 @@ def test_status_strings_and_version():
     for code, name in sv.STATUS.items():
         assert L.spec_verify_status_string(code).decode() == name
     assert L.spec_verify_status_string(99).decode() == "SV_ERR_UNKNOWN"
+
+
+def test_timing_arguments_rejected_on_host():
+    # argument checks that precede any HIP call
+    assert L.spec_verify_timing_begin(-1) == 1
+    buf = (ctypes.c_float * 3)()
+    assert L.spec_verify_timing_end(buf, 1) == 1       # nothing armed on this thread
+    assert L.spec_verify_timing_end(None, -1) == 1
 
 
 def test_workspace_size():
