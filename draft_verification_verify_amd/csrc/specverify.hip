@@ -373,32 +373,38 @@ __device__ double wg_excl_scan(double v, double *sm4, double &total)
     return wb + excl;
 }
 
-// fp64 2^x for x <= 0, within 1e-14 relative (the sampler needs per-term
-// accuracy far below 1e-10, not correct rounding).  x = k/512 + r with k = round(512 x)
-// taken from the low word of x*512 + 1.5*2^52, |r| <= 1/1024;
+// fp64 2^(s/512) for s <= 0, within 1e-14 relative (the sampler needs
+// per-term accuracy far below 1e-10, not correct rounding).  s = k + r with
+// k = round(s) taken from the low word of s + 1.5*2^52, |r| <= 1/2;
 // 2^(k/512) = 2^(k >> 9) * T[k & 511] with T[j] = 2^(j/512) tabulated in LDS
-// at kernel start, and 2^r by its Taylor polynomial of degree 3 (truncation
-// below 1e-14 relative).  Arguments below -2000 (and -inf) give exactly 0
-// through ldexp's underflow; NaN propagates.
+// at kernel start, and 2^(r/512) by its Taylor polynomial of degree 3
+// (truncation below 1e-14 relative).  Taking the argument pre-scaled by 512
+// lets callers fold the scale into their own constants.  s is clamped at
+// -2000*512, so -inf (a masked logit) and anything below 2^-2000 give exactly
+// 0 through ldexp's underflow; a NaN argument also gives 0 (rows holding NaN
+// are flagged separately wherever they are read).
 __device__ void init_exp2_table(double *tab)
 {
     for (int j = threadIdx.x; j < EXP2_TAB; j += blockDim.x) tab[j] = exp2((double)j / EXP2_TAB);
     __syncthreads();
 }
 
-__device__ __forceinline__ double exp2_tab(double x, const double *tab)
+__device__ __forceinline__ double exp2_512(double s, const double *tab)
 {
     constexpr double SHIFT = 6755399441055744.0;   // 1.5 * 2^52
-    constexpr double C1 = LN2, C2 = LN2 * LN2 / 2.0, C3 = LN2 * LN2 * LN2 / 6.0;
-    x = (x < -2000.0) ? -2000.0 : x;
-    const double kb = fma(x, (double)EXP2_TAB, SHIFT);
+    constexpr double D1 = LN2 / EXP2_TAB, D2 = D1 * D1 / 2.0, D3 = D1 * D1 * D1 / 6.0;
+    s = __builtin_fmax(s, -2000.0 * EXP2_TAB);
+    const double kb = s + SHIFT;
     const int k = (int)(uint32_t)(uint64_t)__double_as_longlong(kb);
-    const double r = fma(kb - SHIFT, -1.0 / EXP2_TAB, x);
-    double p = fma(r, C3, C2);
-    p = fma(r, p, C1);
+    const double r = s - (kb - SHIFT);
+    double p = fma(r, D3, D2);
+    p = fma(r, p, D1);
     p = fma(r, p, 1.0);
     return ldexp(tab[k & (EXP2_TAB - 1)] * p, k >> 9);
 }
+
+// fp64 2^x for x <= 0 (see exp2_512).
+__device__ __forceinline__ double exp2_tab(double x, const double *tab) { return exp2_512(x * EXP2_TAB, tab); }
 
 // ---------------------------------------------------------------------------
 // Batch plan: rows each request contributes to the row pass.
@@ -1000,19 +1006,30 @@ __device__ __forceinline__ void issue_vecs(const RowView<BF16> &rv, int v0, int 
     for (int j = 0; j < N; ++j) raw[j] = ld_plain(rv.vec + min(v0 + j * stride, rv.nvec - 1));
 }
 
-// Elements of vector vi as fp32, -inf outside the row (selects, no branch);
-// NaN / +inf flagged.
-template <bool BF16>
-__device__ __forceinline__ void chunk_vec(const RowView<BF16> &rv, int vi, const uint4 &raw,
+// Elements of vector vi as fp32, -inf outside the row (selects, no
+// branch); NaN / +inf flagged.  With ALIGNED (every row starts on a vector
+// boundary and V fills whole vectors) only vectors past the row's end hold
+// elements outside it, so the test is one per vector, on the raw data.
+template <bool BF16, bool ALIGNED = false>
+__device__ __forceinline__ void chunk_vec(const RowView<BF16> &rv, int vi, const uint4 &raw_in,
                                           float (&f)[RowView<BF16>::EPV], int &flag)
 {
-    unpack<BF16>(raw, f);
+    if constexpr (ALIGNED) {
+        constexpr uint32_t NEG = BF16 ? 0xff80ff80u : 0xff800000u;   // -inf in every element
+        const bool in = vi < rv.nvec;
+        const uint4 raw = make_uint4(in ? raw_in.x : NEG, in ? raw_in.y : NEG, in ? raw_in.z : NEG,
+                                     in ? raw_in.w : NEG);
+        unpack<BF16>(raw, f);
+    } else {
+        unpack<BF16>(raw_in, f);
 #pragma unroll
-    for (int e = 0; e < RowView<BF16>::EPV; ++e) {
-        const int x = rv.elem(vi, e);
-        f[e] = ((unsigned)x < (unsigned)rv.V) ? f[e] : -INFINITY;
-        flag |= (!(f[e] == f[e]) || f[e] == INFINITY);
+        for (int e = 0; e < RowView<BF16>::EPV; ++e) {
+            const int x = rv.elem(vi, e);
+            f[e] = ((unsigned)x < (unsigned)rv.V) ? f[e] : -INFINITY;
+        }
     }
+#pragma unroll
+    for (int e = 0; e < RowView<BF16>::EPV; ++e) flag |= (!(f[e] == f[e]) || f[e] == INFINITY);
 }
 
 // Draft logits on the target row's vector grid.  With ALIGNED (V * element
@@ -1030,7 +1047,7 @@ __device__ __forceinline__ void draft_vec(const DraftChunk<BF16> &dc, const RowV
 {
     int fl = 0;
     if constexpr (ALIGNED) {
-        chunk_vec<BF16>(dc.ry, vi, raw, g, fl);
+        chunk_vec<BF16, true>(dc.ry, vi, raw, g, fl);
     } else {
 #pragma unroll
         for (int e = 0; e < RowView<BF16>::EPV; ++e) {
@@ -1047,7 +1064,14 @@ template <bool BF16>
 struct DrawRows {
     RowView<BF16> rz;
     DraftChunk<BF16> dc;
-    double cd, mzc, myc;
+    double cd, mzc, myc;     // log2(e)/T and the row maxima times it
+    double cd5, mzc5, myc5;  // the same times 512 (arguments of exp2_512)
+    __device__ void scale()
+    {
+        cd5 = cd * EXP2_TAB;
+        mzc5 = mzc * EXP2_TAB;
+        myc5 = myc * EXP2_TAB;
+    }
 };
 
 template <bool BF16>
@@ -1061,6 +1085,7 @@ __device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int b, cons
     r.cd = LOG2E / (double)desc.T;
     r.mzc = (double)Mz * r.cd;
     r.myc = (double)My * r.cd;
+    r.scale();
     return r;
 }
 
@@ -1091,19 +1116,19 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
                 // one vector at a time: unbounded interleaving of the fp64
                 // exponentials would cost occupancy
                 __builtin_amdgcn_sched_barrier(0);
-                chunk_vec<BF16>(dr.rz, vi, rz[j], f, flag);
+                // the 64 vectors of this slot lie inside the row except near
+                // its ends (uniform test; the masking selects are skipped)
+                chunk_vec<BF16, ALIGNED>(dr.rz, vi, rz[j], f, flag);
                 draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry[j], g);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
-                    const double p = exp2_tab(fma((double)f[e], dr.cd, -dr.mzc), tab);
-                    const double q = exp2_tab(fma((double)g[e], dr.cd, -dr.myc), tab);
+                    const double p = exp2_512(fma((double)f[e], dr.cd5, -dr.mzc5), tab);
+                    const double q = exp2_512(fma((double)g[e], dr.cd5, -dr.myc5), tab);
                     sz += p;
                     sy += q;
                     const double t = fma(-rho_hat, q, p);
-                    if (t > 0.0) {
-                        dsum += t;
-                        bq += q;
-                    }
+                    dsum += __builtin_fmax(t, 0.0);
+                    bq += (t > 0.0) ? q : 0.0;
                 }
             }
         }
@@ -1125,7 +1150,7 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
             float ml = -INFINITY;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                chunk_vec<BF16>(dr.rz, v0 + j * 64, rz[j], f[j], flag);
+                chunk_vec<BF16, ALIGNED>(dr.rz, v0 + j * 64, rz[j], f[j], flag);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) ml = fmaxf(ml, f[j][e]);
             }
@@ -1134,11 +1159,11 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
                 m = ml;
             }
             if (m != -INFINITY && m != INFINITY) {
-                const double mc = (double)m * dr.cd;
+                const double mc5 = (double)m * dr.cd5;
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) s += exp2_tab(fma((double)f[j][e], dr.cd, -mc), tab);
+                    for (int e = 0; e < EPV; ++e) s += exp2_512(fma((double)f[j][e], dr.cd5, -mc5), tab);
             }
         }
         const float M = wave_max(m);
@@ -1257,13 +1282,13 @@ __device__ __forceinline__ void slot_terms(const DrawRows<BF16> &dr, int which, 
     constexpr int EPV = RowView<BF16>::EPV;
     int flag = 0;
     float f[EPV], g[EPV];
-    chunk_vec<BF16>(dr.rz, vi, rz, f, flag);
+    chunk_vec<BF16, ALIGNED>(dr.rz, vi, rz, f, flag);
     if (which == 0) draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry, g);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-        const double p = exp2_tab(fma((double)f[e], dr.cd, -dr.mzc), tab);
+        const double p = exp2_512(fma((double)f[e], dr.cd5, -dr.mzc5), tab);
         if (which == 0) {
-            const double q = exp2_tab(fma((double)g[e], dr.cd, -dr.myc), tab);
+            const double q = exp2_512(fma((double)g[e], dr.cd5, -dr.myc5), tab);
             const double t = fma(-rho, q, p);
             val[e] = t > 0.0 ? t : 0.0;
         } else {
@@ -1390,7 +1415,10 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
 
     // rescan unit cstar in token order: thread t takes vectors k*WG + t
     DrawRows<BF16> dr2 = dr;
-    if (!resid) dr2.mzc = (double)Mb * dr.cd;
+    if (!resid) {
+        dr2.mzc = (double)Mb * dr.cd;
+        dr2.scale();
+    }
     const int wsel = resid ? which : 1;
     int first = 0x7fffffff, lastp = -1;
     double carry = 0.0;
