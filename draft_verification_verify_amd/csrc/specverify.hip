@@ -710,6 +710,7 @@ struct Task {
     int r, c, b0, b1;
     bool lse;
     float c32;
+    float zx;   // sampled rows: the row's logit at the drafted token (read once per task)
 };
 
 template <bool BF16>
@@ -729,7 +730,17 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     else { is_draft = true; kk = local; k.lse = true; }   // KIND_CONF
     k.c32 = k.lse ? c32_of(kind, pl.T[b]) : 0.0f;
     const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
-    k.rv = RowView<BF16>((const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4), P.V);
+    const char *row_start = (const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4);
+    k.rv = RowView<BF16>(row_start, P.V);
+    // The accept test needs this row's logit at the drafted token x; every
+    // chunk reads it (the same address, uniform across the wave), so the
+    // finish kernel has it from the partials.  x outside [0, V) is clamped
+    // here and rejected as bad data by the scan.
+    k.zx = 0.0f;
+    if (kind == KIND_SAMPLED) {
+        const int x = min(max(P.tokens[(int64_t)b * P.K + kk], 0), P.V - 1);
+        k.zx = load_logit<BF16>(row_start, x);
+    }
     const int nbr = (int)ceil_div(k.rv.nvec, WVEC);
     k.b0 = k.c * nb;
     k.b1 = std::max(std::min(nbr, k.b0 + nb), k.b0 + 1);
@@ -756,6 +767,15 @@ __device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, cons
         st.idx = 0;
         st.s = wave_sum(sl);
     }
+    return st;
+}
+
+// Sampled rows carry the logit at the drafted token in the partial's index.
+template <bool BF16>
+__device__ __forceinline__ Stat finish_task(const Task<BF16> &k, const ArgmaxLane &am, const LseLane &ls)
+{
+    Stat st = finish_task(k.lse, am, ls, k.c32);
+    if (k.lse) st.idx = __float_as_int(k.zx);
     return st;
 }
 
@@ -810,7 +830,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         if (cur.lse) process_batch<BF16, true>(cur.rv, i * WVEC, A, cur.c32, ls);
         else process_batch<BF16, false>(cur.rv, i * WVEC, A, 0.0f, am);
         if (last) {
-            const Stat st = finish_task(cur.lse, am, ls, cur.c32);
+            const Stat st = finish_task<BF16>(cur, am, ls);
             if (lane_id() == 0) P.ws.part[(int64_t)cur.r * P.cpr_max + cur.c] = st;
             if (!more) break;
             am = ArgmaxLane();
@@ -883,7 +903,6 @@ __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const 
     int bad = unif_ok(P.u_sample[b]) ? 0 : 1;
     int n = d;
     const double c2 = (double)c32_of(q.kind, q.T);
-    const int64_t V = P.V;
     for (int k0 = 0; k0 < d; k0 += 64) {
         const int k = k0 + lane;
         const bool active = k < d;
@@ -895,8 +914,9 @@ __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const 
             const bool lb = (x < 0 || x >= P.V) || !unif_ok(ua) || stat_bad(st, true) || stat_bad(sd, true);
             double a = 0.0, c = 0.0;
             if (!lb) {
-                const float zx = load_logit_dt(P.target, P.bf16, ((int64_t)b * (K + 1) + k) * V + x);
-                const float yx = load_logit_dt(P.draft, P.bf16, (tb + k) * V + x);
+                // logits at x, carried by the row partials
+                const float zx = __int_as_float(st.idx);
+                const float yx = __int_as_float(sd.idx);
                 a = exp2_tab(((double)zx - (double)st.m) * c2, tab) / st.s;
                 c = exp2_tab(((double)yx - (double)sd.m) * c2, tab) / sd.s;
                 const double ratio = (c > 0.0) ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
@@ -940,6 +960,8 @@ __device__ void write_outputs(const Params &P, int b, int d, const ReqDesc &desc
 
 // Merge of two partial statistics of one row: (max, lowest argmax) with NaN
 // propagated, or (max, sum relative to the max) rescaled to the larger max.
+// Log-sum-exp partials carry the logit at the drafted token in idx (every
+// chunk the same value; the merge identity carries 0x7fffffff).
 __device__ __forceinline__ Stat merge2(Stat a, Stat b, bool lse, double cs, const double *tab)
 {
     if (!lse) {
@@ -948,6 +970,8 @@ __device__ __forceinline__ Stat merge2(Stat a, Stat b, bool lse, double cs, cons
         argmax_merge(a.m, a.idx, b.m, b.idx);
         return a;
     }
+    const int zx = (a.idx != 0x7fffffff) ? a.idx : b.idx;
+    a.idx = b.idx = zx;
     if (b.m > a.m) {
         const Stat t = a;
         a = b;
