@@ -49,6 +49,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include <vector>
 
 #include "specverify.h"
@@ -256,25 +257,75 @@ __device__ __forceinline__ uint4 ld_stream(gvec_t p)
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Butterfly partner exchanges without the LDS crossbar.  Level L pairs every
+// lane with one lane of the other half of its aligned group of 2^(L+1)
+// lanes: L0 lane^1 and L1 lane^2 (DPP quad permutes), L2 the mirror lane
+// within 8 and L3 within 16 (DPP row mirrors), L4 lane^16 and L5 lane^32
+// (gfx950 permlane swaps).  After levels 0..L every lane of a group holds the
+// group's combination (each pair combines the same two values).
+template <int L>
+__device__ __forceinline__ uint32_t xchg(uint32_t v)
+{
+    if constexpr (L == 0) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+    else if constexpr (L == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+    else if constexpr (L == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+    else if constexpr (L == 3) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+    else if constexpr (L == 4) {
+        const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (threadIdx.x & 16) ? q[0] : q[1];
+    } else {
+        const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? q[0] : q[1];
+    }
+}
+template <int L> __device__ __forceinline__ float xchg_f(float v) { return __uint_as_float(xchg<L>(__float_as_uint(v))); }
+template <int L> __device__ __forceinline__ int xchg_i(int v) { return (int)xchg<L>((uint32_t)v); }
+template <int L>
+__device__ __forceinline__ double xchg_d(double v)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t r = (uint64_t)xchg<L>((uint32_t)u) | ((uint64_t)xchg<L>((uint32_t)(u >> 32)) << 32);
+    return __longlong_as_double((long long)r);
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, xchg_f<0>(v));
+    v = fmaxf(v, xchg_f<1>(v));
+    v = fmaxf(v, xchg_f<2>(v));
+    v = fmaxf(v, xchg_f<3>(v));
+    v = fmaxf(v, xchg_f<4>(v));
+    return fmaxf(v, xchg_f<5>(v));
 }
 
 __device__ __forceinline__ double wave_sum(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += xchg_d<0>(v);
+    v += xchg_d<1>(v);
+    v += xchg_d<2>(v);
+    v += xchg_d<3>(v);
+    v += xchg_d<4>(v);
+    return v + xchg_d<5>(v);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v)
+{
+    v += xchg_i<0>(v);
+    v += xchg_i<1>(v);
+    v += xchg_i<2>(v);
+    v += xchg_i<3>(v);
+    v += xchg_i<4>(v);
+    return v + xchg_i<5>(v);
 }
 
 __device__ __forceinline__ int wave_or(int v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
-    return v;
+    v |= xchg_i<0>(v);
+    v |= xchg_i<1>(v);
+    v |= xchg_i<2>(v);
+    v |= xchg_i<3>(v);
+    v |= xchg_i<4>(v);
+    return v | xchg_i<5>(v);
 }
 
 // (value desc, index asc) argmax merge.
@@ -283,15 +334,66 @@ __device__ __forceinline__ void argmax_merge(float &m, int &i, float m2, int i2)
     if (m2 > m || (m2 == m && i2 < i)) { m = m2; i = i2; }
 }
 
+template <int L>
+__device__ __forceinline__ void argmax_level(float &m, int &i)
+{
+    const float m2 = xchg_f<L>(m);
+    const int i2 = xchg_i<L>(i);
+    argmax_merge(m, i, m2, i2);
+}
+
 __device__ __forceinline__ void wave_argmax(float &m, int &i)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o, 64);
-        const int i2 = __shfl_xor(i, o, 64);
-        argmax_merge(m, i, m2, i2);
-    }
+    argmax_level<0>(m, i);
+    argmax_level<1>(m, i);
+    argmax_level<2>(m, i);
+    argmax_level<3>(m, i);
+    argmax_level<4>(m, i);
+    argmax_level<5>(m, i);
 }
+
+// Inclusive scans over the wave in lane order with DPP: shifts right by 1, 2,
+// 4, 8 inside each 16-lane row (lanes without a source read 0), then each
+// row's total carried forward by the row broadcasts of lane 15 (into rows 1
+// and 3) and lane 31 (into rows 2 and 3).
+template <int CTRL, int ROWS, bool BC>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, BC);
+}
+template <int CTRL, int ROWS, bool BC>
+__device__ __forceinline__ double dpp_d(double v)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t r = (uint64_t)dpp_u<CTRL, ROWS, BC>((uint32_t)u) |
+                       ((uint64_t)dpp_u<CTRL, ROWS, BC>((uint32_t)(u >> 32)) << 32);
+    return __longlong_as_double((long long)r);
+}
+
+__device__ __forceinline__ double wave_incl_scan(double v)
+{
+    v += dpp_d<0x111, 0xF, true>(v);
+    v += dpp_d<0x112, 0xF, true>(v);
+    v += dpp_d<0x114, 0xF, true>(v);
+    v += dpp_d<0x118, 0xF, true>(v);
+    v += dpp_d<0x142, 0xA, false>(v);
+    v += dpp_d<0x143, 0xC, false>(v);
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v)
+{
+    v += (int)dpp_u<0x111, 0xF, true>((uint32_t)v);
+    v += (int)dpp_u<0x112, 0xF, true>((uint32_t)v);
+    v += (int)dpp_u<0x114, 0xF, true>((uint32_t)v);
+    v += (int)dpp_u<0x118, 0xF, true>((uint32_t)v);
+    v += (int)dpp_u<0x142, 0xA, false>((uint32_t)v);
+    v += (int)dpp_u<0x143, 0xC, false>((uint32_t)v);
+    return v;
+}
+
+// value of the previous lane (0 in lane 0): DPP wave shift right by one
+__device__ __forceinline__ double wave_shr1(double v) { return dpp_d<0x138, 0xF, true>(v); }
 
 // Workgroup reductions through LDS (all threads must call; result in all).
 struct RedSmem {
@@ -352,14 +454,8 @@ __device__ void wg_argmax(float &m, int &i, RedSmem &sm)
 __device__ double wg_excl_scan(double v, double *sm4, double &total)
 {
     const int lane = lane_id();
-    double incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
-    double excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0;
+    const double incl = wave_incl_scan(v);
+    const double excl = wave_shr1(incl);
     __syncthreads();
     if (lane == 63) sm4[wave_id()] = incl;
     __syncthreads();
@@ -466,13 +562,8 @@ __device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
         pl.row_off[b] = q.rows;   // count for now
         local += q.rows;
     }
-    int v = local;
+    const int v = wave_incl_scan_i(local);
     const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(v, o, 64);
-        if (lane >= o) v += y;
-    }
     if (lane == 63) scan_tmp[wave_id()] = v;
     __syncthreads();
     int wave_base = 0;
@@ -1001,13 +1092,24 @@ __device__ void merge_rows(const Params &P, int pre, int rows, int cpr, bool lse
             const Stat *pp = P.ws.part + (int64_t)(pre + r) * P.cpr_max;
             for (int j = l; j < cpr; j += tpr) acc = merge2(acc, pp[j], lse, cs, tab);
         }
-        for (int o = tpr >> 1; o > 0; o >>= 1) {
-            Stat other;
-            other.m = __shfl_xor(acc.m, o, 64);
-            other.idx = __shfl_xor(acc.idx, o, 64);
-            other.s = __shfl_xor(acc.s, o, 64);
-            acc = merge2(acc, other, lse, cs, tab);
-        }
+        // butterfly over the tpr lanes of the row (levels with 2^L < tpr;
+        // every workgroup of the request runs the same sequence)
+        auto level = [&](auto lv) {
+            constexpr int L = decltype(lv)::value;
+            if ((1 << L) < tpr) {
+                Stat other;
+                other.m = xchg_f<L>(acc.m);
+                other.idx = xchg_i<L>(acc.idx);
+                other.s = xchg_d<L>(acc.s);
+                acc = merge2(acc, other, lse, cs, tab);
+            }
+        };
+        level(std::integral_constant<int, 0>());
+        level(std::integral_constant<int, 1>());
+        level(std::integral_constant<int, 2>());
+        level(std::integral_constant<int, 3>());
+        level(std::integral_constant<int, 4>());
+        level(std::integral_constant<int, 5>());
         if (r < rows && l == 0) rows_s[r] = acc;
     }
     __syncthreads();
@@ -1223,8 +1325,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // first active row of request b: rows of the requests before it
     int pre = 0;
     for (int j = tid; j < b; j += WG) pre += plan_request(P, j).rows;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) pre += __shfl_xor(pre, o, 64);
+    pre = wave_sum_i(pre);
     if (lane_id() == 0) sh_pre[wave_id()] = pre;
     __syncthreads();
     pre = 0;
@@ -1508,8 +1609,7 @@ __device__ __forceinline__ float sanitize_conf(float c)
 
 __device__ int block_sum_int(int v, int *sm32)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v = wave_sum_i(v);
     __syncthreads();
     if (lane_id() == 0) sm32[wave_id()] = v;
     __syncthreads();
@@ -1522,12 +1622,7 @@ __device__ int block_sum_int(int v, int *sm32)
 __device__ int block_excl_scan_int(int v, int *sm32)
 {
     const int lane = lane_id();
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan_i(v);
     __syncthreads();
     if (lane == 63) sm32[wave_id()] = incl;
     __syncthreads();
