@@ -119,7 +119,8 @@ struct alignas(16) DrawRec {
 };
 
 struct Ws {
-    int32_t *meta;       // [4]: chunks per row and batches per chunk of the row pass
+    int32_t *meta;       // [4]: chunks per row and batches per chunk of the row pass;
+                         // then one Stat of scratch (the row pass's placeholder stores)
     Stat *part;          // [R_max * cpr_max] row-pass chunk partials
     ChunkPart *cp;       // [B * cs_max] sampler chunk sums
     DrawRec *rec;        // [B]
@@ -150,7 +151,7 @@ bool make_layout(int B, int K, int V, Layout &L)
     L.cs_max = (int)std::max(ceil_div(nv, (int64_t)UNIT_E / 4), ceil_div(nvec_max(V, 8), (int64_t)UNIT_E / 8));
     if (L.cs_max > UNITS_MAX) return false;
     const size_t sz[4] = {
-        sizeof(int32_t) * 4,
+        sizeof(int32_t) * 4 + sizeof(Stat),
         sizeof(Stat) * (size_t)L.r_max * (size_t)L.cpr_max,
         sizeof(ChunkPart) * (size_t)B * (size_t)L.cs_max,
         sizeof(DrawRec) * (size_t)B,
@@ -580,13 +581,15 @@ __device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
     __syncthreads();
 }
 
-// request containing global active row r (row_off is non-decreasing)
+// Request containing global active row r (row_off is non-decreasing).  r is
+// wave-uniform; the LDS values are made scalar so the search runs on the
+// scalar unit.
 __device__ __forceinline__ int find_request(const int *row_off, int B, int r)
 {
     int lo = 0, hi = B;   // row_off[lo] <= r < row_off[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (row_off[mid] <= r) lo = mid; else hi = mid;
+        if (__builtin_amdgcn_readfirstlane(row_off[mid]) <= r) lo = mid; else hi = mid;
     }
     return lo;
 }
@@ -792,49 +795,85 @@ __device__ __forceinline__ float c32_of(int kind, float T)
     return (float)(LOG2E / (double)(kind == KIND_CONF ? 1.0f : T));
 }
 
-// One chunk of one row: the row view and the batches [b0, b1) it covers.  A
-// chunk past the end of a short row (rows whose start is not 16-byte aligned
-// cover one vector more) gets one fully masked batch, so b1 > b0 always.
+// One chunk of one row: its row view and the end b1 of the batches
+// [c * nb, b1) it covers.  A chunk past the end of a short row (rows whose
+// start is not 16-byte aligned cover one vector more) gets one fully masked
+// batch, so a chunk is never empty.  All fields are wave-uniform (scalar).
 template <bool BF16>
 struct Task {
-    RowView<BF16> rv;
-    int r, c, b0, b1;
-    bool lse;
-    float c32;
-    float zx;   // sampled rows: the row's logit at the drafted token (read once per task)
+    gvec_t vec;    // row view: vector grid start, head elements, vectors
+    int head, nvec;
+    int r, c, b1;
+    float c32;     // log-sum-exp scale; 0 marks a greedy (argmax) row
+    float zx;      // sampled rows: the row's logit at the drafted token
+    __device__ __forceinline__ bool lse() const { return c32 != 0.0f; }
+    __device__ __forceinline__ RowView<BF16> view(int V) const
+    {
+        RowView<BF16> rv;
+        rv.vec = vec;
+        rv.head = head;
+        rv.nvec = nvec;
+        rv.V = V;
+        return rv;
+    }
 };
 
+// Wave-uniform loads through the scalar cache (constant address space): they
+// are counted apart from the vector loads of the stream, so waiting for one
+// never drains the batches in flight.
+__device__ __forceinline__ int ld_scalar_i32(const int *p)
+{
+    return *(const __attribute__((address_space(4))) int *)p;
+}
 template <bool BF16>
-__device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl, int64_t t, int cpr, int nb)
+__device__ __forceinline__ float ld_scalar_logit(const void *row, int x)
+{
+    if constexpr (BF16) {
+        // the aligned word holding the element (same page, always readable)
+        const uintptr_t a = (uintptr_t)row + 2 * (uintptr_t)x;
+        const uint32_t w = (uint32_t)ld_scalar_i32((const int *)(a & ~(uintptr_t)3));
+        return __uint_as_float((a & 2) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+        return __int_as_float(ld_scalar_i32((const int *)row + x));
+    }
+}
+
+// Task (r, c): chunk c of global active row r.  Everything here is
+// wave-uniform.
+template <bool BF16>
+__device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl, int r, int c, int nb)
 {
     Task<BF16> k;
-    k.r = (int)(t / cpr);
-    k.c = (int)(t - (int64_t)k.r * cpr);
-    const int b = find_request(pl.row_off, P.B, k.r);
-    const int local = k.r - pl.row_off[b];
-    const int info = pl.info[b];
+    k.r = r;
+    k.c = c;
+    bool lse;
+    const int b = find_request(pl.row_off, P.B, r);
+    const int local = r - __builtin_amdgcn_readfirstlane(pl.row_off[b]);
+    const int info = __builtin_amdgcn_readfirstlane(pl.info[b]);
     const int d = info & 0xffff, kind = info >> 16;
     bool is_draft;
     int kk;
-    if (kind == KIND_GREEDY) { is_draft = false; kk = local; k.lse = false; }
-    else if (kind == KIND_SAMPLED) { is_draft = local >= d; kk = is_draft ? local - d : local; k.lse = true; }
-    else { is_draft = true; kk = local; k.lse = true; }   // KIND_CONF
-    k.c32 = k.lse ? c32_of(kind, pl.T[b]) : 0.0f;
+    if (kind == KIND_GREEDY) { is_draft = false; kk = local; lse = false; }
+    else if (kind == KIND_SAMPLED) { is_draft = local >= d; kk = is_draft ? local - d : local; lse = true; }
+    else { is_draft = true; kk = local; lse = true; }   // KIND_CONF
+    k.c32 = lse ? c32_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b])))) : 0.0f;
     const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
     const char *row_start = (const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4);
-    k.rv = RowView<BF16>(row_start, P.V);
+    const RowView<BF16> rv(row_start, P.V);
+    k.vec = rv.vec;
+    k.head = rv.head;
+    k.nvec = rv.nvec;
     // The accept test needs this row's logit at the drafted token x; every
-    // chunk reads it (the same address, uniform across the wave), so the
-    // finish kernel has it from the partials.  x outside [0, V) is clamped
-    // here and rejected as bad data by the scan.
+    // chunk reads it, so the finish kernel has it from the partials.  x
+    // outside [0, V) is clamped here and rejected as bad data by the scan.
     k.zx = 0.0f;
     if (kind == KIND_SAMPLED) {
-        const int x = min(max(P.tokens[(int64_t)b * P.K + kk], 0), P.V - 1);
-        k.zx = load_logit<BF16>(row_start, x);
+        const int x = min(max(ld_scalar_i32(P.tokens + (int64_t)b * P.K + kk), 0), P.V - 1);
+        k.zx = ld_scalar_logit<BF16>(row_start, x);
     }
-    const int nbr = (int)ceil_div(k.rv.nvec, WVEC);
-    k.b0 = k.c * nb;
-    k.b1 = std::max(std::min(nbr, k.b0 + nb), k.b0 + 1);
+    const int nbr = (int)ceil_div(k.nvec, WVEC);
+    const int b0 = c * nb;
+    k.b1 = std::max(std::min(nbr, b0 + nb), b0 + 1);
     return k;
 }
 
@@ -865,9 +904,36 @@ __device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, cons
 template <bool BF16>
 __device__ __forceinline__ Stat finish_task(const Task<BF16> &k, const ArgmaxLane &am, const LseLane &ls)
 {
-    Stat st = finish_task(k.lse, am, ls, k.c32);
-    if (k.lse) st.idx = __float_as_int(k.zx);
+    Stat st = finish_task(k.lse(), am, ls, k.c32);
+    if (k.lse()) st.idx = __float_as_int(k.zx);
     return st;
+}
+
+// Reduces one batch of a task into the running lane state and stores the
+// task's partial slot: after the task's last batch the reduced partial
+// (plain store; the finish kernel reads it after the kernel boundary),
+// before that a placeholder the last store overwrites (same wave, same
+// address, so program order holds).  Storing on every batch keeps one store
+// per batch on every path, so the compiler's load-wait counts stay exact and
+// no wait ever covers a store.  The partial is wave-uniform (butterfly
+// reductions), so every lane stores the same 16 bytes: one write.
+template <bool BF16>
+__device__ __forceinline__ void consume(const Params &P, const Task<BF16> &k, int i, const uint4 (&raw)[UW],
+                                        ArgmaxLane &am, LseLane &ls)
+{
+    if (k.lse()) process_batch<BF16, true>(k.view(P.V), i * WVEC, raw, k.c32, ls);
+    else process_batch<BF16, false>(k.view(P.V), i * WVEC, raw, 0.0f, am);
+    Stat st;
+    if (i + 1 >= k.b1) {
+        st = finish_task<BF16>(k, am, ls);
+        am = ArgmaxLane();
+        ls = LseLane();
+    } else {
+        st.m = 0.0f;
+        st.idx = 0;
+        st.s = 0.0;
+    }
+    P.ws.part[(int64_t)k.r * P.cpr_max + k.c] = st;
 }
 
 // Four waves per SIMD (128 VGPRs) keep enough 16-byte loads in flight per CU
@@ -883,57 +949,79 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     pl.T = (float *)(plan_smem + 2 * P.B + 1);
     make_plan(P, pl, scan_tmp);
 
-    const int R = pl.row_off[P.B];
-    const int64_t nwaves = (int64_t)gridDim.x * NWAVE;
+    const int R = __builtin_amdgcn_readfirstlane(pl.row_off[P.B]);
+    const uint32_t nwaves = gridDim.x * NWAVE;
     int cpr, nb;
     row_chunking(R, P.V, BF16, nwaves, cpr, nb);
+    // The divisions above run on the vector unit; their (uniform) results
+    // are moved to scalar registers so everything derived stays scalar.
+    cpr = __builtin_amdgcn_readfirstlane(cpr);
+    nb = __builtin_amdgcn_readfirstlane(nb);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         P.ws.meta[0] = cpr;
         P.ws.meta[1] = nb;
     }
 
-    // Static assignment: wave w takes tasks w, w + nwaves, ...  The next
-    // batch -- of this task, or the first of the wave's next task -- is in
-    // flight while the current batch is reduced, so the load stream never
-    // drains at task boundaries.  Partials go out with plain stores; the
-    // finish kernel reads them after the kernel boundary.
-    const int64_t ntask = (int64_t)R * cpr;
-    int64_t t = (int64_t)blockIdx.x * NWAVE + wave_id();
-    if (t >= ntask) return;
-    Task<BF16> cur = make_task<BF16>(P, pl, t, cpr, nb);
+    // Static assignment: wave w takes tasks w, w + nwaves, ... (task t is
+    // chunk t % cpr of row t / cpr).  All loop state is wave-uniform, so the
+    // control flow is scalar.  Two batch buffers alternate: while one is
+    // reduced the other is in flight, across task boundaries too, and the
+    // buffers are never copied (a register copy would wait for the load).
+    const uint32_t ntask = (uint32_t)R * (uint32_t)cpr;
+    const uint32_t t0 = blockIdx.x * NWAVE + (uint32_t)__builtin_amdgcn_readfirstlane(wave_id());
+    if (t0 >= ntask) return;
+    const int dq = __builtin_amdgcn_readfirstlane((int)(nwaves / (uint32_t)cpr));
+    const int dr = (int)nwaves - dq * cpr;
+    const int r0 = __builtin_amdgcn_readfirstlane((int)(t0 / (uint32_t)cpr));
+    const int c0 = (int)t0 - r0 * cpr;
+
+    // (kn, in) = the batch after batch i of task k in this wave's stream;
+    // false past the stream's end.
+    auto next_batch = [&](const Task<BF16> &k, int i, Task<BF16> &kn, int &in) -> bool {
+        if (i + 1 < k.b1) {
+            kn = k;
+            in = i + 1;
+            return true;
+        }
+        int c = k.c + dr, r = k.r + dq;
+        if (c >= cpr) { c -= cpr; ++r; }
+        if (r >= R) return false;
+        kn = make_task<BF16>(P, pl, r, c, nb);
+        in = c * nb;
+        return true;
+    };
+
+    // Steady state: [A, store, B] in flight when A is reduced, [B, store, A]
+    // when B is.  Every step issues a batch, a store follows every
+    // reduction (or stands in for one), and the loop has one exit, at its
+    // bottom, so the compiler's wait counts stay exact: a reduction waits
+    // for its own buffer only, never for the other buffer or a store.  Past
+    // the stream's end the issue is a dummy: every lane loads the last vector
+    // of a row already read (one cached line) and the batch is not reduced.
+    Stat *const spare = (Stat *)(P.ws.meta + 4);
+    Stat zero;
+    zero.m = 0.0f;
+    zero.idx = 0;
+    zero.s = 0.0;
+    uint4 A[UW], Bv[UW];
+    Task<BF16> kA = make_task<BF16>(P, pl, r0, c0, nb);
+    Task<BF16> kB = kA;
+    int iA = c0 * nb, iB = iA;
+    bool vB = next_batch(kA, iA, kB, iB);
+    issue_batch(kA.vec, kA.nvec, iA * WVEC, A);
+    *spare = zero;
+    issue_batch(kB.vec, kB.nvec, vB ? iB * WVEC : kB.nvec, Bv);
     ArgmaxLane am;
     LseLane ls;
-    uint4 A[UW], Bv[UW];
-    issue_batch(cur.rv.vec, cur.rv.nvec, cur.b0 * WVEC, A);
-    int i = cur.b0;
     for (;;) {
-        const bool last = i + 1 >= cur.b1;
-        const int64_t tn = t + nwaves;
-        const bool more = tn < ntask;
-        Task<BF16> nxt = cur;
-        if (last && more) nxt = make_task<BF16>(P, pl, tn, cpr, nb);
-        // next batch: this task's, the next task's first, or (no work left)
-        // a harmless reload of a valid batch
-        const gvec_t nvec_ptr = last ? nxt.rv.vec : cur.rv.vec;
-        const int nnv = last ? nxt.rv.nvec : cur.rv.nvec;
-        const int nvb = last ? nxt.b0 : i + 1;
-        issue_batch(nvec_ptr, nnv, nvb * WVEC, Bv);
-        if (cur.lse) process_batch<BF16, true>(cur.rv, i * WVEC, A, cur.c32, ls);
-        else process_batch<BF16, false>(cur.rv, i * WVEC, A, 0.0f, am);
-        if (last) {
-            const Stat st = finish_task<BF16>(cur, am, ls);
-            if (lane_id() == 0) P.ws.part[(int64_t)cur.r * P.cpr_max + cur.c] = st;
-            if (!more) break;
-            am = ArgmaxLane();
-            ls = LseLane();
-            cur = nxt;
-            t = tn;
-            i = cur.b0;
-        } else {
-            ++i;
-        }
-#pragma unroll
-        for (int j = 0; j < UW; ++j) A[j] = Bv[j];
+        consume<BF16>(P, kA, iA, A, am, ls);
+        const bool vA = vB && next_batch(kB, iB, kA, iA);
+        issue_batch(kA.vec, kA.nvec, vA ? iA * WVEC : kA.nvec, A);
+        if (vB) consume<BF16>(P, kB, iB, Bv, am, ls);
+        else *spare = zero;
+        vB = vA && next_batch(kA, iA, kB, iB);
+        issue_batch(kB.vec, kB.nvec, vB ? iB * WVEC : kB.nvec, Bv);
+        if (!vA) break;
     }
 }
 
@@ -1320,6 +1408,10 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     __shared__ ReqDesc sh_desc;
     float2 *pq_s = (float2 *)(rows_s + 2 * P.K + 1);
     const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+    // The merge and the scan are a short latency chain that every unit of the
+    // request waits on; fp64 unit work of other workgroups on the same SIMD
+    // would otherwise delay it.  Raised issue priority until the units start.
+    __builtin_amdgcn_s_setprio(3);
     init_exp2_table(tab);
 
     // first active row of request b: rows of the requests before it
@@ -1376,6 +1468,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // this wave's unit of the drawn row pair (no workgroup barrier after here)
     const int unit = c * NWAVE + wave_id();
     if (unit >= P.cs) return;
+    __builtin_amdgcn_s_setprio(0);
     const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, resid ? sz_row.m : 0.0f, resid ? sy_row.m : 0.0f);
     const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rho_hat, unit * unit_v<BF16>(), tab);
     if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
@@ -1422,176 +1515,242 @@ __device__ __forceinline__ void slot_terms(const DrawRows<BF16> &dr, int which, 
     }
 }
 
+// A wave's own copy of the exp2 table: LDS operations of one wave complete in
+// program order, so the wave can read it right after writing it, with no
+// workgroup barrier.
+__device__ __forceinline__ void init_exp2_table_wave(double *tab)
+{
+    for (int j = lane_id(); j < EXP2_TAB; j += 64) tab[j] = exp2((double)j / EXP2_TAB);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Lane `src` (wave-uniform) of v.
+__device__ __forceinline__ double readlane_d(double v, int src)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Unit totals of the chosen distribution (wave-redundant: every wave of the
+// draw workgroup computes the same values from the same inputs).
+struct UnitPick {
+    int cstar;      // unit holding the draw, -1 if none
+    bool over;      // u*R reached no unit's inclusive prefix (rounding)
+    bool bad;       // the row pair cannot be drawn from
+    double base;    // exclusive prefix of unit cstar
+    double target;  // u*R
+    double rho;     // Sz/Sy (residual draw)
+    int which;      // 0: residual max(0, P - rho Q); 1: P
+    float Mb;       // bonus draw: the row maximum
+};
+
+// Every wave of the draw workgroup, redundantly and with wave operations
+// only: the unit totals of the chosen distribution in unit order (lane-
+// strided, unit j = 64 h + lane), their total R, and the first unit whose
+// inclusive prefix exceeds u*R (else the last unit with mass).
+template <bool BF16>
+__device__ UnitPick pick_unit(const Params &P, int b, const DrawRec &rec, const DrawRows<BF16> &dr, const double *tab)
+{
+    const int lane = lane_id();
+    const ChunkPart *cp = P.ws.cp + (int64_t)b * P.cs;
+    const int ncs = P.cs;
+    const int H = (int)ceil_div(ncs, 64);
+    const bool resid = rec.state == SREQ_RESID;
+    UnitPick k;
+    k.rho = 0.0;
+    k.which = 1;
+    k.Mb = 0.0f;
+    k.bad = false;
+    // pass 1: the row sums (residual) or the row maximum (bonus)
+    double lz = 0.0, ly = 0.0;
+    float lm = -INFINITY;
+    int lb = 0;
+    for (int h = 0; h < H; ++h) {
+        const int j = h * 64 + lane;
+        if (j < ncs) {
+            const ChunkPart c = cp[j];
+            lz += c.sz;
+            ly += c.sy;
+            lm = fmaxf(lm, c.m);
+            lb |= c.bad;
+        }
+    }
+    if (resid) {
+        const double Sz = wave_sum(lz), Sy = wave_sum(ly);
+        k.bad = !(Sz > 0.0) || !(Sy > 0.0);
+        k.rho = k.bad ? 0.0 : Sz / Sy;
+        // residual mass: draw from p if there is none
+        double lr = 0.0;
+        for (int h = 0; h < H; ++h) {
+            const int j = h * 64 + lane;
+            if (j < ncs) {
+                const ChunkPart c = cp[j];
+                lr += fmax(0.0, fma(rec.rho_hat - k.rho, c.bq, c.d));
+            }
+        }
+        k.which = wave_sum(lr) > 0.0 ? 0 : 1;
+    } else {
+        k.Mb = wave_max(lm);
+        k.bad = wave_or(lb) != 0 || k.Mb == -INFINITY || k.Mb == INFINITY;
+    }
+    // pass 2: unit totals, prefix scan in unit order, the unit holding u*R
+    double carry = 0.0;
+    k.target = 0.0;
+    int cand = -1, lastc = -1;
+    double cbase = 0.0;
+    double Rt = 0.0;
+    // R first (the target depends on it), then the search
+    for (int pass = 0; pass < 2; ++pass) {
+        carry = 0.0;
+        for (int h = 0; h < H; ++h) {
+            const int j = h * 64 + lane;
+            double t = 0.0;
+            if (j < ncs) {
+                const ChunkPart c = cp[j];
+                if (resid) t = k.which == 0 ? fmax(0.0, fma(rec.rho_hat - k.rho, c.bq, c.d)) : c.sz;
+                else t = (c.m == -INFINITY || k.bad) ? 0.0 : c.sz * exp2_tab(((double)c.m - (double)k.Mb) * dr.cd, tab);
+            }
+            const double raw = wave_incl_scan(t);
+            const double incl = raw + carry;
+            if (pass == 1) {
+                // lane l's exclusive prefix is lane l-1's inclusive one, bit for bit
+                const double excl = wave_shr1(raw) + carry;
+                const uint64_t hit = __ballot(j < ncs && incl > k.target);
+                if (cand < 0 && hit != 0) {
+                    const int l = __builtin_ctzll(hit);
+                    cand = h * 64 + l;
+                    cbase = readlane_d(excl, l);
+                }
+                const uint64_t mass = __ballot(t > 0.0);
+                if (mass != 0) lastc = h * 64 + 63 - __builtin_clzll(mass);
+            }
+            carry = readlane_d(incl, 63);
+        }
+        if (pass == 0) {
+            Rt = carry;
+            if (!(Rt > 0.0)) k.bad = true;
+            k.target = (double)P.u_sample[b] * Rt;
+        }
+    }
+    k.over = cand < 0;
+    k.cstar = k.over ? lastc : cand;
+    k.base = k.over ? 0.0 : cbase;
+    return k;
+}
+
 template <bool BF16, bool ALIGNED>
 __global__ __launch_bounds__(WG) void draw_kernel(Params P)
 {
-    constexpr int EPV = RowView<BF16>::EPV, UV = unit_v<BF16>(), UPT = UNITS_MAX / WG;
-    __shared__ double tab[EXP2_TAB];
-    __shared__ RedSmem sm;
-    __shared__ double sm4[NWAVE];
-    __shared__ double sh_base;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    constexpr int EPV = RowView<BF16>::EPV, UV = unit_v<BF16>(), VPW = UV / NWAVE, ROUNDS = VPW / 64;
+    static_assert(VPW % 64 == 0, "a wave rescans whole rounds of 64 vectors");
+    __shared__ double tabs[NWAVE][EXP2_TAB];
+    __shared__ double sh_tot[NWAVE];
+    __shared__ int sh_last[NWAVE];
+    __shared__ int sh_first[NWAVE];
+    const int b = blockIdx.x, w = wave_id(), lane = lane_id();
     const DrawRec rec = P.ws.rec[b];
     if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
-    init_exp2_table(tab);
+    double *tab = tabs[w];
+    init_exp2_table_wave(tab);
     const bool resid = rec.state == SREQ_RESID;
     const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
-    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
-
-    // combine the unit sums; thread t holds units t*per .. t*per + per - 1
-    const ChunkPart *cp = P.ws.cp + (int64_t)b * P.cs;
-    const int ncs = P.cs;
-    const int per = (int)ceil_div(ncs, WG);   // <= UPT
-    const int u0 = tid * per;
-    ChunkPart pa[UPT];
-#pragma unroll
-    for (int h = 0; h < UPT; ++h) {
-        const int j = u0 + h;
-        if (h < per && j < ncs) pa[h] = cp[j];
-        else pa[h] = ChunkPart{0.0, 0.0, 0.0, 0.0, -INFINITY, 0, {0, 0}};
-    }
-    double tot[UPT];
-    double rho = 0.0;
-    int which = 1;
-    float Mb = 0.0f;
-    bool bad = false;
-    if (resid) {
-        double lz = 0.0, ly = 0.0;
-#pragma unroll
-        for (int h = 0; h < UPT; ++h) {
-            lz += pa[h].sz;
-            ly += pa[h].sy;
-        }
-        const double Sz = wg_sum(lz, sm);
-        const double Sy = wg_sum(ly, sm);
-        bad = !(Sz > 0.0) || !(Sy > 0.0);
-        rho = bad ? 0.0 : Sz / Sy;
-        double lr = 0.0;
-#pragma unroll
-        for (int h = 0; h < UPT; ++h) {
-            tot[h] = fmax(0.0, fma(rec.rho_hat - rho, pa[h].bq, pa[h].d));
-            lr += tot[h];
-        }
-        if (wg_sum(lr, sm) > 0.0) {
-            which = 0;
-        } else {   // no residual mass: draw from p
-#pragma unroll
-            for (int h = 0; h < UPT; ++h) tot[h] = pa[h].sz;
-        }
-    } else {
-        float lm = -INFINITY;
-        int lb = 0;
-#pragma unroll
-        for (int h = 0; h < UPT; ++h) {
-            lm = fmaxf(lm, pa[h].m);
-            lb |= pa[h].bad;
-        }
-        Mb = wg_max(lm, sm);
-        bad = wg_or(lb, sm) != 0;
-        bad |= (Mb == -INFINITY || Mb == INFINITY);
-#pragma unroll
-        for (int h = 0; h < UPT; ++h)
-            tot[h] = (pa[h].m == -INFINITY || bad) ? 0.0
-                                                    : pa[h].sz * exp2_tab(((double)pa[h].m - (double)Mb) * dr.cd, tab);
-    }
-    // exclusive prefix of the unit totals in unit order; the total R
-    double lsum = 0.0;
-#pragma unroll
-    for (int h = 0; h < UPT; ++h) lsum += tot[h];
-    double Rt;
-    const double base0 = wg_excl_scan(lsum, sm4, Rt);
-    if (!(Rt > 0.0)) bad = true;
-    const double target = (double)P.u_sample[b] * Rt;
-    // first unit whose inclusive prefix exceeds u*R; last unit with mass
-    int cand = 0x7fffffff, lastc = -1;
-    double run = base0, cbase = 0.0;
-#pragma unroll
-    for (int h = 0; h < UPT; ++h) {
-        const int j = u0 + h;
-        if (cand == 0x7fffffff && h < per && j < ncs && run + tot[h] > target) {
-            cand = j;
-            cbase = run;
-        }
-        if (tot[h] > 0.0) lastc = j;
-        run += tot[h];
-    }
-    {
-        float m = (cand == 0x7fffffff) ? -INFINITY : 0.0f;
-        int i = cand;
-        wg_argmax(m, i, sm);
-        const int cw = (m == -INFINITY) ? 0x7fffffff : i;
-        if (cw != 0x7fffffff && cw == cand) sh_base = cbase;
-        cand = cw;
-        float m2 = (lastc < 0) ? -INFINITY : 0.0f;
-        int i2 = (lastc < 0) ? 0x7fffffff : (0x7fffffff - lastc);
-        wg_argmax(m2, i2, sm);   // contains a barrier: sh_base is visible after it
-        lastc = (m2 == -INFINITY) ? -1 : (0x7fffffff - i2);
-    }
-    const bool over = cand == 0x7fffffff;
-    const int cstar = over ? lastc : cand;
-    if (bad || cstar < 0) {   // the bonus row holds NaN, +inf or nothing but -inf
-        if (wave_id() == 0) {
+    DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
+    const UnitPick k = pick_unit<BF16>(P, b, rec, dr, tab);
+    if (k.bad || k.cstar < 0) {   // the drawn row holds NaN, +inf or nothing but -inf
+        if (w == 0) {
             const ReqDesc bd = {SREQ_BAD, 0, -1, rec.T};
             write_outputs(P, b, 0, bd, nullptr, -1);
         }
         return;
     }
-    const double base = over ? 0.0 : sh_base;
-
-    // rescan unit cstar in token order: thread t takes vectors k*WG + t
-    DrawRows<BF16> dr2 = dr;
     if (!resid) {
-        dr2.mzc = (double)Mb * dr.cd;
-        dr2.scale();
+        dr.mzc = (double)k.Mb * dr.cd;
+        dr.scale();
     }
-    const int wsel = resid ? which : 1;
-    int first = 0x7fffffff, lastp = -1;
-    double carry = 0.0;
-    uint4 rz[UV / WG], ry[UV / WG];
-    issue_vecs<BF16, UV / WG>(dr2.rz, cstar * UV + tid, WG, rz);
+    const int wsel = resid ? k.which : 1;
+
+    // rescan of unit cstar in token order: wave w takes its quarter, round
+    // r of it being vectors 64 r + lane
+    const int v0 = k.cstar * UV + w * VPW + lane;
+    uint4 rz[ROUNDS], ry[ROUNDS];
+    issue_vecs<BF16, ROUNDS>(dr.rz, v0, 64, rz);
     // the draft row exists only for a residual draw (a bonus draw reads
     // target row d; draft row d may lie past the draft logits)
-    if (wsel == 0 && ALIGNED) issue_vecs<BF16, UV / WG>(dr2.dc.ry, cstar * UV + tid, WG, ry);
+    if (wsel == 0 && ALIGNED) issue_vecs<BF16, ROUNDS>(dr.dc.ry, v0, 64, ry);
+    double val[ROUNDS][EPV], excl[ROUNDS];
+    double wtot = 0.0;
+    int lastp = -1;
 #pragma unroll
-    for (int k = 0; k < UV / WG; ++k) {
-        const int vi = cstar * UV + k * WG + tid;
-        double val[EPV];
-        slot_terms<BF16, ALIGNED>(dr2, wsel, rho, vi, rz[k], ry[k], tab, val);
+    for (int r = 0; r < ROUNDS; ++r) {
+        slot_terms<BF16, ALIGNED>(dr, wsel, k.rho, v0 + 64 * r, rz[r], ry[r], tab, val[r]);
         double vs = 0.0;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) vs += val[e];
-        double t;
-        const double ex = wg_excl_scan(vs, sm4, t);
-        const double slot0 = carry + ex;
+        for (int e = 0; e < EPV; ++e) {
+            vs += val[r][e];
+            const int x = dr.rz.elem(v0 + 64 * r, e);
+            if (val[r][e] > 0.0 && x >= 0 && x < P.V) lastp = max(lastp, x);
+        }
+        const double incl = wave_incl_scan(vs);
+        excl[r] = wave_shr1(incl) + wtot;
+        wtot += readlane_d(incl, 63);
+    }
+    if (lane == 0) {
+        sh_tot[w] = wtot;
+    }
+    {
+        // highest token with mass in this wave
+        int m = lastp;
+        m = max(m, xchg_i<0>(m));
+        m = max(m, xchg_i<1>(m));
+        m = max(m, xchg_i<2>(m));
+        m = max(m, xchg_i<3>(m));
+        m = max(m, xchg_i<4>(m));
+        m = max(m, xchg_i<5>(m));
+        if (lane == 0) sh_last[w] = m;
+    }
+    __syncthreads();
+    double wbase = 0.0;
+    for (int u = 0; u < w; ++u) wbase += sh_tot[u];
+    int first = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+        const double slot0 = wbase + excl[r];
         double part = 0.0;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-            part += val[e];
-            const int x = dr.rz.elem(vi, e);
-            if (val[e] > 0.0 && x >= 0 && x < P.V) {
-                if (x > lastp) lastp = x;
-                if (first == 0x7fffffff && base + (slot0 + part) > target) first = x;
-            }
+            part += val[r][e];
+            const int x = dr.rz.elem(v0 + 64 * r, e);
+            if (first == 0x7fffffff && val[r][e] > 0.0 && x >= 0 && x < P.V && k.base + (slot0 + part) > k.target)
+                first = x;
         }
-        carry += t;
-    }
-    int fi, lp;
-    {
-        float m = (first == 0x7fffffff) ? -INFINITY : 0.0f;
-        int i = first;
-        wg_argmax(m, i, sm);   // lowest token among threads holding a crossing
-        fi = (m == -INFINITY) ? 0x7fffffff : i;
     }
     {
-        float m = (lastp < 0) ? -INFINITY : 0.0f;
-        int i = (lastp < 0) ? 0x7fffffff : (0x7fffffff - lastp);
-        wg_argmax(m, i, sm);   // highest token with mass
-        lp = (m == -INFINITY) ? -1 : (0x7fffffff - i);
+        // lowest crossing token in this wave
+        int m = first;
+        m = min(m, xchg_i<0>(m));
+        m = min(m, xchg_i<1>(m));
+        m = min(m, xchg_i<2>(m));
+        m = min(m, xchg_i<3>(m));
+        m = min(m, xchg_i<4>(m));
+        m = min(m, xchg_i<5>(m));
+        if (lane == 0) sh_first[w] = m;
     }
-    const int tok = (!over && fi != 0x7fffffff) ? fi : lp;
+    __syncthreads();
+    if (w != 0) return;
+    int fi = 0x7fffffff, lp = -1;
+#pragma unroll
+    for (int u = 0; u < NWAVE; ++u) {
+        fi = min(fi, sh_first[u]);
+        lp = max(lp, sh_last[u]);
+    }
+    const int tok = (!k.over && fi != 0x7fffffff) ? fi : lp;
     if (tok >= 0) {
-        if (tid == 0) P.out_tokens[(int64_t)b * (P.K + 1) + rec.n] = tok;
-    } else if (wave_id() == 0) {
+        if (lane == 0) P.out_tokens[(int64_t)b * (P.K + 1) + rec.n] = tok;
+    } else {
         const ReqDesc bd = {SREQ_BAD, 0, -1, rec.T};
         write_outputs(P, b, 0, bd, nullptr, -1);
     }
