@@ -121,7 +121,8 @@ struct alignas(16) DrawRec {
 struct Ws {
     int32_t *meta;       // [4]: chunks per row and batches per chunk of the row pass;
                          // then one Stat of scratch (the row pass's placeholder stores)
-    Stat *part;          // [R_max * cpr_max] row-pass chunk partials
+    Stat *part;          // [B * (2K + 1) * cpr_max] row-pass chunk partials: row j of
+                         // request b in slot row b * (2K + 1) + j, chunk c in column c
     ChunkPart *cp;       // [B * cs_max] sampler chunk sums
     DrawRec *rec;        // [B]
 };
@@ -804,6 +805,7 @@ struct Task {
     gvec_t vec;    // row view: vector grid start, head elements, vectors
     int head, nvec;
     int r, c, b1;
+    int slot;      // partial slot row: request * (2K + 1) + row within the request
     float c32;     // log-sum-exp scale; 0 marks a greedy (argmax) row
     float zx;      // sampled rows: the row's logit at the drafted token
     __device__ __forceinline__ bool lse() const { return c32 != 0.0f; }
@@ -851,6 +853,7 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     const int local = r - __builtin_amdgcn_readfirstlane(pl.row_off[b]);
     const int info = __builtin_amdgcn_readfirstlane(pl.info[b]);
     const int d = info & 0xffff, kind = info >> 16;
+    k.slot = b * (2 * P.K + 1) + local;
     bool is_draft;
     int kk;
     if (kind == KIND_GREEDY) { is_draft = false; kk = local; lse = false; }
@@ -933,7 +936,7 @@ __device__ __forceinline__ void consume(const Params &P, const Task<BF16> &k, in
         st.idx = 0;
         st.s = 0.0;
     }
-    P.ws.part[(int64_t)k.r * P.cpr_max + k.c] = st;
+    P.ws.part[(int64_t)k.slot * P.cpr_max + k.c] = st;
 }
 
 // Four waves per SIMD (128 VGPRs) keep enough 16-byte loads in flight per CU
@@ -1404,7 +1407,6 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
 {
     extern __shared__ Stat rows_s[];   // [2K + 1] merged row statistics, then [K] (p, q) pairs
     __shared__ double tab[EXP2_TAB];
-    __shared__ int sh_pre[NWAVE];
     __shared__ ReqDesc sh_desc;
     float2 *pq_s = (float2 *)(rows_s + 2 * P.K + 1);
     const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
@@ -1412,21 +1414,16 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // request waits on; fp64 unit work of other workgroups on the same SIMD
     // would otherwise delay it.  Raised issue priority until the units start.
     __builtin_amdgcn_s_setprio(3);
+    // the request's plan and the row pass's chunking are read before the
+    // table is built, so their loads overlap its arithmetic
+    const ReqPlan q = plan_request(P, b);
+    const int cpr = P.ws.meta[0];
     init_exp2_table(tab);
 
-    // first active row of request b: rows of the requests before it
-    int pre = 0;
-    for (int j = tid; j < b; j += WG) pre += plan_request(P, j).rows;
-    pre = wave_sum_i(pre);
-    if (lane_id() == 0) sh_pre[wave_id()] = pre;
-    __syncthreads();
-    pre = 0;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) pre += sh_pre[w];
-
-    const ReqPlan q = plan_request(P, b);
+    // request b's partials start at slot row b * (2K + 1)
+    const int pre = b * (2 * P.K + 1);
     const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF;
-    merge_rows(P, pre, q.rows, P.ws.meta[0], lse, lse ? (double)c32_of(q.kind, q.T) : 0.0, tab, rows_s);
+    merge_rows(P, pre, q.rows, cpr, lse, lse ? (double)c32_of(q.kind, q.T) : 0.0, tab, rows_s);
 
     if (P.mode == MODE_CONF) {
         for (int k = tid; k < P.K; k += WG) {
