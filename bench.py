@@ -51,8 +51,8 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "74d91a599549029b4754d69f3c1c1ea908f04f703f7f320ae97fb0c37d10f3f9",
-                    "fetch_bytes": 540079945, "write_bytes": 527460}
+ROW_PASS_TRAFFIC = {"source_sha256": "c029036024c496e03550e68eebbc31fb5e98f0146ac01c6fe13b52e12840e096",
+                    "fetch_bytes": 525904142, "write_bytes": 536986}
 
 
 def parse():
