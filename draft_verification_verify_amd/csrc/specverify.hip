@@ -71,6 +71,11 @@ constexpr int V_MAX = 2000000;
 constexpr int DCUT_MAX = 32768;   // B*K for dcut_allocate (keys held in LDS)
 constexpr int DCUT_WG = 1024;
 constexpr int EXP2_TAB = 512;     // table entries of the fp64 exp2
+constexpr int SLOT_MAX = 4;       // dispatch slots of the row pass told apart
+// Task-count slope across dispatch slots (measured on MI355X: greedy rows,
+// which carry less arithmetic per byte, want a smaller slope).
+constexpr float ROW_SKEW_GREEDY = 0.2f;
+constexpr float ROW_SKEW_LSE = 0.3f;
 
 enum : int { MODE_GREEDY = 0, MODE_SAMPLE = 1, MODE_CONF = 2 };
 enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3 };
@@ -198,6 +203,8 @@ struct Params {
     int32_t cpr_max;
     int32_t cs;        // sampler units per row (this call's dtype)
     int32_t aligned;   // V * element size is a multiple of 16: every row starts 16-byte aligned
+    int32_t row_cus;   // compute units the row-pass grid is spread over
+    float row_skew;    // row pass: task-count slope across dispatch slots
     Ws ws;
 };
 
@@ -806,6 +813,8 @@ struct Task {
     int head, nvec;
     int r, c, b1;
     int slot;      // partial slot row: request * (2K + 1) + row within the request
+    int k;         // the wave's round of this task
+    uint32_t pre;  // first task index of round k
     float c32;     // log-sum-exp scale; 0 marks a greedy (argmax) row
     float zx;      // sampled rows: the row's logit at the drafted token
     __device__ __forceinline__ bool lse() const { return c32 != 0.0f; }
@@ -965,18 +974,53 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         P.ws.meta[1] = nb;
     }
 
-    // Static assignment: wave w takes tasks w, w + nwaves, ... (task t is
-    // chunk t % cpr of row t / cpr).  All loop state is wave-uniform, so the
-    // control flow is scalar.  Two batch buffers alternate: while one is
-    // reduced the other is in flight, across task boundaries too, and the
-    // buffers are never copied (a register copy would wait for the load).
+    // Static assignment in rounds.  Task t is chunk t % cpr of row t / cpr.
+    // Workgroups land on the CUs in blockIdx order, so blockIdx / row_cus is
+    // a workgroup's dispatch slot on its CU; waves of earlier slots are older
+    // and win more issue cycles, so slot group s gets n_s tasks per wave,
+    // n_s = ceil(avg * (1 + skew * ((nslot - 1) / 2 - s))), non-increasing in
+    // s.  Round k is run by the slot groups with n_s > k -- a prefix of the
+    // waves, of size A_k -- and wave gw's round-k task is pre_k + gw, with
+    // pre_k the tasks of the earlier rounds.  Skew 0 is the plain round robin
+    // w, w + nwaves, ...  All loop state is wave-uniform (scalar).
     const uint32_t ntask = (uint32_t)R * (uint32_t)cpr;
-    const uint32_t t0 = blockIdx.x * NWAVE + (uint32_t)__builtin_amdgcn_readfirstlane(wave_id());
-    if (t0 >= ntask) return;
-    const int dq = __builtin_amdgcn_readfirstlane((int)(nwaves / (uint32_t)cpr));
-    const int dr = (int)nwaves - dq * cpr;
-    const int r0 = __builtin_amdgcn_readfirstlane((int)(t0 / (uint32_t)cpr));
-    const int c0 = (int)t0 - r0 * cpr;
+    const uint32_t gw = blockIdx.x * NWAVE + (uint32_t)__builtin_amdgcn_readfirstlane(wave_id());
+    if (gw >= ntask) return;
+    const int Q = max(P.row_cus, 1);
+    const int nslot = min((int)ceil_div(gridDim.x, Q), SLOT_MAX);
+    const int myslot = min((int)blockIdx.x / Q, nslot - 1);
+    int nt[SLOT_MAX];        // tasks per wave of each slot group
+    uint32_t gend[SLOT_MAX]; // end (in waves) of each slot group
+    {
+        const float avg = (float)ntask / (float)nwaves;
+        uint32_t cover = 0;
+#pragma unroll
+        for (int g = 0; g < SLOT_MAX; ++g) {
+            const float w = 1.0f + P.row_skew * (0.5f * (float)(nslot - 1) - (float)g);
+            nt[g] = g < nslot ? max(1, (int)(avg * fmaxf(w, 0.0f) + 0.5f)) : 0;
+            if (g > 0) nt[g] = min(nt[g], nt[g - 1]);
+            gend[g] = g < nslot - 1 ? (uint32_t)((g + 1) * Q) * NWAVE : nwaves;
+            const uint32_t gbeg = g == 0 ? 0u : (uint32_t)(g * Q) * NWAVE;
+            if (g < nslot) cover += (uint32_t)nt[g] * (gend[g] - gbeg);
+        }
+        // rounding shortfall: more rounds for the first (fastest) group
+        const uint32_t g0 = gend[0];
+        if (cover < ntask) nt[0] += (int)ceil_div(ntask - cover, g0);
+    }
+    int mytasks = 0;
+#pragma unroll
+    for (int g = 0; g < SLOT_MAX; ++g)
+        if (g == myslot) mytasks = nt[g];
+    // waves active in round k: the slot groups with nt > k (a prefix)
+    auto active = [&](int k) -> uint32_t {
+        uint32_t a = 0;
+#pragma unroll
+        for (int g = 0; g < SLOT_MAX; ++g)
+            if (g < nslot && nt[g] > k) a = gend[g];
+        return a;
+    };
+    const int r0 = __builtin_amdgcn_readfirstlane((int)(gw / (uint32_t)cpr));
+    const int c0 = (int)gw - r0 * cpr;
 
     // (kn, in) = the batch after batch i of task k in this wave's stream;
     // false past the stream's end.
@@ -986,10 +1030,16 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
             in = i + 1;
             return true;
         }
-        int c = k.c + dr, r = k.r + dq;
-        if (c >= cpr) { c -= cpr; ++r; }
-        if (r >= R) return false;
+        const int k1 = k.k + 1;
+        if (k1 >= mytasks) return false;
+        const uint32_t pre1 = k.pre + active(k.k);
+        const uint32_t t = pre1 + gw;
+        if (t >= ntask) return false;
+        const int r = __builtin_amdgcn_readfirstlane((int)(t / (uint32_t)cpr));
+        const int c = (int)t - r * cpr;
         kn = make_task<BF16>(P, pl, r, c, nb);
+        kn.k = k1;
+        kn.pre = pre1;
         in = c * nb;
         return true;
     };
@@ -1008,6 +1058,8 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     zero.s = 0.0;
     uint4 A[UW], Bv[UW];
     Task<BF16> kA = make_task<BF16>(P, pl, r0, c0, nb);
+    kA.k = 0;
+    kA.pre = 0;
     Task<BF16> kB = kA;
     int iA = c0 * nb, iB = iA;
     bool vB = next_batch(kA, iA, kB, iB);
@@ -1320,12 +1372,17 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
     int flag = 0;
     if (resid) {
         double dsum = 0.0, bq = 0.0, sz = 0.0, sy = 0.0;
-#pragma unroll 1
+        // every step's loads are issued before the first step's arithmetic, so
+        // the second step's memory latency hides under the first's fp64 work
+        uint4 rz[SUB][NV], ry[SUB][NV];
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+            issue_vecs<BF16, NV>(dr.rz, vu + u * NV * 64 + lane, 64, rz[u]);
+            if (ALIGNED) issue_vecs<BF16, NV>(dr.dc.ry, vu + u * NV * 64 + lane, 64, ry[u]);
+        }
+#pragma unroll
         for (int u = 0; u < SUB; ++u) {
             const int v0 = vu + u * NV * 64 + lane;
-            uint4 rz[NV], ry[NV];
-            issue_vecs<BF16, NV>(dr.rz, v0, 64, rz);
-            if (ALIGNED) issue_vecs<BF16, NV>(dr.dc.ry, v0, 64, ry);
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int vi = v0 + j * 64;
@@ -1335,8 +1392,8 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
                 __builtin_amdgcn_sched_barrier(0);
                 // the 64 vectors of this slot lie inside the row except near
                 // its ends (uniform test; the masking selects are skipped)
-                chunk_vec<BF16, ALIGNED>(dr.rz, vi, rz[j], f, flag);
-                draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry[j], g);
+                chunk_vec<BF16, ALIGNED>(dr.rz, vi, rz[u][j], f, flag);
+                draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry[u][j], g);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
                     const double p = exp2_512(fma((double)f[e], dr.cd5, -dr.mzc5), tab);
@@ -1358,16 +1415,17 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
     } else {
         float m = -INFINITY;
         double s = 0.0;
-#pragma unroll 1
+        uint4 rz[SUB][NV];
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) issue_vecs<BF16, NV>(dr.rz, vu + u * NV * 64 + lane, 64, rz[u]);
+#pragma unroll
         for (int u = 0; u < SUB; ++u) {
             const int v0 = vu + u * NV * 64 + lane;
-            uint4 rz[NV];
-            issue_vecs<BF16, NV>(dr.rz, v0, 64, rz);
             float f[NV][EPV];
             float ml = -INFINITY;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                chunk_vec<BF16, ALIGNED>(dr.rz, v0 + j * 64, rz[j], f[j], flag);
+                chunk_vec<BF16, ALIGNED>(dr.rz, v0 + j * 64, rz[u][j], f[j], flag);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) ml = fmaxf(ml, f[j][e]);
             }
@@ -2045,6 +2103,8 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
     P.bf16 = dt == SV_BF16;
     P.mode = mode;
     P.cpr_max = L.cpr_max;
+    P.row_cus = cu_count();
+    P.row_skew = mode == MODE_GREEDY ? ROW_SKEW_GREEDY : ROW_SKEW_LSE;
     P.cs = (int)ceil_div(nvec_max(V, P.bf16 ? 8 : 4), (int64_t)UNIT_E / (P.bf16 ? 8 : 4));
     P.aligned = ((int64_t)V * (P.bf16 ? 2 : 4)) % 16 == 0;
     P.ws = carve(ws, L, B);
