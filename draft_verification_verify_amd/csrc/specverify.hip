@@ -1099,8 +1099,10 @@ __device__ __forceinline__ bool unif_ok(float u) { return u >= 0.0f && u < 1.0f;
 // rows: target rows 0..d (greedy) or target rows 0..d-1 then draft rows
 // 0..d-1 (sampled), in LDS.  For a sampled request pq[k] receives
 // (p_k(x_k), q_k(x_k)) for k < d.  Writes nothing to global memory.
+// (x0, ua0, us0): lane l's drafted token and accept uniform at position l, and
+// the request's draw uniform, loaded by the caller ahead of time.
 __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const Stat *rows, float2 *pq,
-                                const double *tab)
+                                const double *tab, int x0, float ua0, float us0)
 {
     const int K = P.K, d = q.d;
     const int lane = lane_id();
@@ -1119,7 +1121,7 @@ __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const 
                 const Stat s = rows[k];
                 bad |= stat_bad(s, false);
                 if (k < d) {
-                    const int x = P.tokens[tb + k];
+                    const int x = k0 == 0 ? x0 : P.tokens[tb + k];
                     bad |= (x < 0 || x >= P.V);
                     mism = (x != s.idx);
                 }
@@ -1134,7 +1136,7 @@ __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const 
     // Sampled request (T > 0): accept k iff u_k < min(1, p_k(x)/q_k(x)), in
     // double from the row statistics and the two logits at x, with the same
     // exponent scale c32 as the statistics.
-    int bad = unif_ok(P.u_sample[b]) ? 0 : 1;
+    int bad = unif_ok(us0) ? 0 : 1;
     int n = d;
     const double c2 = (double)c32_of(q.kind, q.T);
     for (int k0 = 0; k0 < d; k0 += 64) {
@@ -1142,8 +1144,8 @@ __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const 
         const bool active = k < d;
         bool rej = false;
         if (active) {
-            const int x = P.tokens[tb + k];
-            const float ua = P.u_accept[tb + k];
+            const int x = k0 == 0 ? x0 : P.tokens[tb + k];
+            const float ua = k0 == 0 ? ua0 : P.u_accept[tb + k];
             const Stat st = rows[k], sd = rows[d + k];
             const bool lb = (x < 0 || x >= P.V) || !unif_ok(ua) || stat_bad(st, true) || stat_bad(sd, true);
             double a = 0.0, c = 0.0;
@@ -1476,6 +1478,18 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // table is built, so their loads overlap its arithmetic
     const ReqPlan q = plan_request(P, b);
     const int cpr = P.ws.meta[0];
+    // the scan's inputs for positions 0..63, loaded now so their latency
+    // overlaps the table and the merge
+    int x0 = 0;
+    float ua0 = 0.0f, us0 = 0.0f;
+    if (wave_id() == 0 && P.mode != MODE_CONF) {
+        const int l = lane_id();
+        if (l < P.K) x0 = P.tokens[(int64_t)b * P.K + l];
+        if (P.mode == MODE_SAMPLE) {
+            if (l < P.K) ua0 = P.u_accept[(int64_t)b * P.K + l];
+            us0 = P.u_sample[b];
+        }
+    }
     init_exp2_table(tab);
 
     // request b's partials start at slot row b * (2K + 1)
@@ -1494,7 +1508,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
         return;
     }
     if (wave_id() == 0) {
-        const ReqDesc dsc = scan_request(P, b, q, rows_s, pq_s, tab);
+        const ReqDesc dsc = scan_request(P, b, q, rows_s, pq_s, tab, x0, ua0, us0);
         if (lane_id() == 0) sh_desc = dsc;
     }
     __syncthreads();
