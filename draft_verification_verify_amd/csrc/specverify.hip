@@ -488,9 +488,26 @@ __device__ double wg_excl_scan(double v, double *sm4, double &total)
 // -2000*512, so -inf (a masked logit) and anything below 2^-2000 give exactly
 // 0 through ldexp's underflow; a NaN argument also gives 0 (rows holding NaN
 // are flagged separately wherever they are read).
+// Entry j = q + 64 i of the table is 2^(q/512) * 2^(i/8): one exp2 per lane
+// and eight products, each entry within about 2 ulp.
+__device__ constexpr double EXP2_EIGHTHS[8] = {   // 2^(i/8), correctly rounded
+    0x1.0000000000000p+0, 0x1.172b83c7d517bp+0, 0x1.306fe0a31b715p+0, 0x1.4bfdad5362a27p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.8ace5422aa0dbp+0, 0x1.ae89f995ad3adp+0, 0x1.d5818dcfba487p+0};
+
+static_assert(EXP2_TAB == 64 * 8, "the table is 64 lanes times 8 eighths");
+
+// One wave writes the whole table.
+__device__ __forceinline__ void fill_exp2_table(double *tab)
+{
+    const int q = lane_id();
+    const double e = exp2((double)q / EXP2_TAB);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tab[q + 64 * i] = e * EXP2_EIGHTHS[i];
+}
+
 __device__ void init_exp2_table(double *tab)
 {
-    for (int j = threadIdx.x; j < EXP2_TAB; j += blockDim.x) tab[j] = exp2((double)j / EXP2_TAB);
+    if (wave_id() == 0) fill_exp2_table(tab);
     __syncthreads();
 }
 
@@ -1589,7 +1606,7 @@ __device__ __forceinline__ void slot_terms(const DrawRows<BF16> &dr, int which, 
 // workgroup barrier.
 __device__ __forceinline__ void init_exp2_table_wave(double *tab)
 {
-    for (int j = lane_id(); j < EXP2_TAB; j += 64) tab[j] = exp2((double)j / EXP2_TAB);
+    fill_exp2_table(tab);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
