@@ -51,8 +51,8 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "c029036024c496e03550e68eebbc31fb5e98f0146ac01c6fe13b52e12840e096",
-                    "fetch_bytes": 525904142, "write_bytes": 536986}
+ROW_PASS_TRAFFIC = {"source_sha256": "2ea128b7ad5ea1217e1c0fb25d65bbc03a0b5f0fe03cf6225c262a9f10ccb6f9",
+                    "fetch_bytes": 526035522, "write_bytes": 536013}
 
 
 def parse():
