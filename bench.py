@@ -325,6 +325,25 @@ def main():
             "bytes_per_step": int((B * K + prow + int(dep.sum())) * V * 2),
             "note": "confidence pass reads all 1024 draft rows; ragged verify reads sum(d_b+1) target "
                     "and sum(d_b) draft rows"}
+        # the same pipeline with the confidence pass's row statistics reused:
+        # the verify streams target rows only (plus the drawn draft row)
+        dstats = torch.empty((B, K, 2), dtype=torch.float64, device="cuda")
+
+        def rstep(i):
+            t, d = copies[i % ncopy]
+            sv.draft_confidence_stats(d, conf=conf, stats=dstats, workspace=ws, stream=stream)
+            sv.dcut_allocate(conf, w.budget, depth_out=depth, stream=stream)
+            sv.verify_sample_reuse(t, d, tok, T, ua, us, dstats, depth, out_tokens=out, num_accepted=nacc,
+                                   p_draft=pd, q_draft=qd, workspace=ws, stream=stream)
+        _, rper, _ = timed(rstep, steps2, warm2)
+        rms = float(np.mean(rper))
+        rdep = depth.cpu().numpy()
+        rrow = int(np.sum(rdep + 1))
+        sec["dcut_pipeline_reuse_B64_K16_budget384"] = {
+            "verified_rows_per_s": rrow / (rms * 1e-3), "ms": rms, "rows_per_step": rrow,
+            "bytes_per_step": int((B * K + int(rdep.sum())) * V * 2),
+            "note": "confidence pass (with row statistics) reads all 1024 draft rows; the verify reuses "
+                    "them and streams sum(d_b) target rows"}
         del copies
         # mixed fp32 batch: per-request K_b and T_b, dcut_allocate(512), one sampled launch
         wm = synth.mixed(args.seed)

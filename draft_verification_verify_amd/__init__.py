@@ -59,6 +59,11 @@ def _load() -> ctypes.CDLL:
                                      vp, vp, vp, vp, vp, sz, vp]
     L.spec_draft_confidence.restype = ctypes.c_int
     L.spec_draft_confidence.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, sz, vp]
+    L.spec_draft_confidence_stats.restype = ctypes.c_int
+    L.spec_draft_confidence_stats.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.spec_verify_sample_reuse.restype = ctypes.c_int
+    L.spec_verify_sample_reuse.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                           vp, vp, vp, vp, vp, sz, vp]
     L.dcut_allocate.restype = ctypes.c_int
     L.dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     L.spec_verify_timing_begin.restype = ctypes.c_int
@@ -74,7 +79,8 @@ lib = _load()
 
 EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify_last_error",
             "spec_verify_workspace_size", "spec_verify_timing_begin", "spec_verify_timing_end",
-            "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate")
+            "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
+            "spec_draft_confidence_stats", "spec_verify_sample_reuse")
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
@@ -245,6 +251,66 @@ def draft_confidence(draft, max_depth=None, *, conf=None, workspace=None, stream
                                    _ptr(ws), nbytes, _stream(stream))
     _raise("spec_draft_confidence", st)
     return conf
+
+
+def draft_confidence_stats(draft, max_depth=None, *, conf=None, want_conf: bool = True, stats=None,
+                           workspace=None, stream=None):
+    """Draft confidence plus every read draft row's statistics (sv_row_stat
+    records, returned as a float64 tensor [B, K, 2]: see row_stat_fields).
+    Returns (conf or None, stats)."""
+    torch = _torch()
+    B, K, V = draft.shape
+    _check(draft, "draft")
+    _check(max_depth, "max_depth", torch.int32, (B,))
+    if want_conf and conf is None:
+        conf = torch.empty((B, K), dtype=torch.float32, device=draft.device)
+    if stats is None:
+        stats = torch.empty((B, K, 2), dtype=torch.float64, device=draft.device)
+    _check(stats, "stats", torch.float64, (B, K, 2))
+    ws, nbytes = _ws(draft.device, B, K, V, workspace)
+    st = lib.spec_draft_confidence_stats(_ptr(draft), _dtype_code(draft), _ptr(max_depth), B, K, V,
+                                         _ptr(conf), _ptr(stats), _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_draft_confidence_stats", st)
+    return conf, stats
+
+
+def row_stat_fields(stats):
+    """(max float32 [B, K], sum float64 [B, K]) of sv_row_stat records."""
+    return stats.view(_torch().float32)[..., 0].contiguous(), stats[..., 1].contiguous()
+
+
+def verify_sample_reuse(target, draft, tokens, temperature, u_accept, u_sample, draft_stats, depth=None, *,
+                        out_tokens=None, num_accepted=None, p_draft=None, q_draft=None,
+                        want_probs: bool = True, workspace=None, stream=None):
+    """verify_sample with the draft rows' statistics from draft_confidence_stats
+    (used for requests at temperature 1)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check(target, "target")
+    _check(draft, "draft", target.dtype, (B, K, V))
+    _check(tokens, "tokens", torch.int32, (B, K))
+    _check(temperature, "temperature", torch.float32, (B,))
+    _check(u_accept, "u_accept", torch.float32, (B, K))
+    _check(u_sample, "u_sample", torch.float32, (B,))
+    _check(draft_stats, "draft_stats", torch.float64, (B, K, 2))
+    _check(depth, "depth", torch.int32, (B,))
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if want_probs and p_draft is None:
+        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if want_probs and q_draft is None:
+        q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    ws, nbytes = _ws(dev, B, K, V, workspace)
+    st = lib.spec_verify_sample_reuse(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens), _ptr(depth),
+                                      _ptr(temperature), _ptr(u_accept), _ptr(u_sample), _ptr(draft_stats),
+                                      B, K, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft),
+                                      _ptr(q_draft), _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_verify_sample_reuse", st)
+    return out_tokens, num_accepted, p_draft, q_draft
 
 
 def dcut_allocate(conf, budget: int, max_depth=None, *, depth_out=None, stream=None):

@@ -43,6 +43,7 @@
 // request.
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -78,7 +79,9 @@ constexpr float ROW_SKEW_GREEDY = 0.2f;
 constexpr float ROW_SKEW_LSE = 0.3f;
 
 enum : int { MODE_GREEDY = 0, MODE_SAMPLE = 1, MODE_CONF = 2 };
-enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3 };
+// KIND_SAMPLED_R: a sampled request at T = 1 whose draft-row statistics come
+// from a confidence pass (the row pass reads its target rows only).
+enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3, KIND_SAMPLED_R = 4 };
 // outcome of a request's accept scan
 enum : int { SREQ_BAD = 0, SREQ_GREEDY = 1, SREQ_RESID = 2, SREQ_BONUS = 3 };
 
@@ -93,6 +96,11 @@ struct alignas(16) Stat {
     int32_t idx;
     double s;
 };
+
+// The C ABI's sv_row_stat is this record.
+static_assert(sizeof(Stat) == sizeof(sv_row_stat) && alignof(Stat) == 16, "row statistics record");
+static_assert(offsetof(Stat, m) == offsetof(sv_row_stat, max) && offsetof(Stat, s) == offsetof(sv_row_stat, sum),
+              "row statistics fields");
 
 struct ReqDesc {
     int32_t state;   // SREQ_*
@@ -197,6 +205,8 @@ struct Params {
     float *p_draft;
     float *q_draft;
     float *conf;
+    const Stat *dstats_in;   // sampled calls: draft-row statistics [B, K] from a confidence pass, or NULL
+    Stat *dstats_out;        // confidence calls: draft-row statistics out [B, K], or NULL
     int32_t B, K, V;
     int32_t bf16;      // logits dtype: 1 bf16, 0 fp32
     int32_t mode;
@@ -560,7 +570,8 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
         q.T = (P.mode == MODE_SAMPLE) ? P.temperature[b] : 0.0f;
         const bool ok = q.d >= 0 && q.d <= P.K && temp_ok(q.T);
         q.kind = !ok ? KIND_BAD : (q.T > 0.0f ? KIND_SAMPLED : KIND_GREEDY);
-        q.rows = !ok ? 0 : (q.kind == KIND_SAMPLED ? 2 * q.d : q.d + 1);
+        if (q.kind == KIND_SAMPLED && P.dstats_in && q.T == 1.0f) q.kind = KIND_SAMPLED_R;
+        q.rows = !ok ? 0 : (q.kind == KIND_SAMPLED ? 2 * q.d : q.kind == KIND_SAMPLED_R ? q.d : q.d + 1);
     }
     if (q.kind == KIND_BAD) q.d = 0;
     return q;
@@ -884,6 +895,7 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     int kk;
     if (kind == KIND_GREEDY) { is_draft = false; kk = local; lse = false; }
     else if (kind == KIND_SAMPLED) { is_draft = local >= d; kk = is_draft ? local - d : local; lse = true; }
+    else if (kind == KIND_SAMPLED_R) { is_draft = false; kk = local; lse = true; }
     else { is_draft = true; kk = local; lse = true; }   // KIND_CONF
     k.c32 = lse ? c32_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b])))) : 0.0f;
     const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
@@ -896,7 +908,7 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     // chunk reads it, so the finish kernel has it from the partials.  x
     // outside [0, V) is clamped here and rejected as bad data by the scan.
     k.zx = 0.0f;
-    if (kind == KIND_SAMPLED) {
+    if (kind == KIND_SAMPLED || kind == KIND_SAMPLED_R) {
         const int x = min(max(ld_scalar_i32(P.tokens + (int64_t)b * P.K + kk), 0), P.V - 1);
         k.zx = ld_scalar_logit<BF16>(row_start, x);
     }
@@ -1511,16 +1523,40 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
 
     // request b's partials start at slot row b * (2K + 1)
     const int pre = b * (2 * P.K + 1);
-    const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF;
+    const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF || q.kind == KIND_SAMPLED_R;
+    if (q.kind == KIND_SAMPLED_R) {
+        // draft rows 0..d-1: the given statistics, with the draft logit at the
+        // drafted token in idx (the row pass's convention; a token outside
+        // [0, V) is clamped here and rejected by the scan); merge_rows' barrier
+        // publishes them with the merged target rows
+        const int64_t esz = P.bf16 ? 2 : 4;
+        for (int k = tid; k < q.d; k += WG) {
+            Stat st = P.dstats_in[(int64_t)b * P.K + k];
+            const int x = min(max(P.tokens[(int64_t)b * P.K + k], 0), P.V - 1);
+            const char *yrow = (const char *)P.draft + ((int64_t)b * P.K + k) * P.V * esz;
+            st.idx = __float_as_int(load_logit_dt(yrow, P.bf16 != 0, x));
+            rows_s[q.d + k] = st;
+        }
+    }
     merge_rows(P, pre, q.rows, cpr, lse, lse ? (double)c32_of(q.kind, q.T) : 0.0, tab, rows_s);
 
     if (P.mode == MODE_CONF) {
         for (int k = tid; k < P.K; k += WG) {
-            float v;
-            if (q.kind == KIND_BAD) v = NAN;
-            else if (k >= q.d) v = 0.0f;
-            else v = stat_bad(rows_s[k], true) ? NAN : (float)(1.0 / rows_s[k].s);
-            P.conf[(int64_t)b * P.K + k] = v;
+            const bool have = q.kind != KIND_BAD && k < q.d;
+            if (P.conf) {
+                float v;
+                if (q.kind == KIND_BAD) v = NAN;
+                else if (k >= q.d) v = 0.0f;
+                else v = stat_bad(rows_s[k], true) ? NAN : (float)(1.0 / rows_s[k].s);
+                P.conf[(int64_t)b * P.K + k] = v;
+            }
+            if (P.dstats_out) {
+                Stat st;
+                st.m = have ? rows_s[k].m : NAN;
+                st.idx = 0;
+                st.s = have ? rows_s[k].s : NAN;
+                P.dstats_out[(int64_t)b * P.K + k] = st;
+            }
         }
         return;
     }
@@ -2253,6 +2289,60 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     P.num_accepted = num_accepted;
     P.p_draft = p_draft;
     P.q_draft = q_draft;
+    return launch(P, stream);
+}
+
+sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_logits, sv_dtype dt,
+                                   const int32_t *draft_tokens, const int32_t *depth, const float *temperature,
+                                   const float *u_accept, const float *u_sample, const void *draft_stats,
+                                   int32_t B, int32_t K, int32_t V, int32_t *out_tokens, int32_t *num_accepted,
+                                   float *p_draft, float *q_draft, void *workspace, size_t ws_bytes,
+                                   hipStream_t stream)
+{
+    sv_status st = check_shape(B, K, V);
+    if (st != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (!target_logits || !temperature || !u_sample || !out_tokens || !num_accepted) return SV_ERR_INVALID_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens || !u_accept || !draft_stats)) return SV_ERR_INVALID_ARG;
+    if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits))) return SV_ERR_INVALID_ARG;
+    if (draft_stats && ((uintptr_t)draft_stats & 15u) != 0) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K, V, L);
+    if ((st = check_ws(workspace, ws_bytes, L)) != SV_OK) return st;
+    Params P = base_params(B, K, V, dt, MODE_SAMPLE, L, workspace);
+    P.target = target_logits;
+    P.draft = draft_logits;
+    P.tokens = draft_tokens;
+    P.depth = depth;
+    P.temperature = temperature;
+    P.u_accept = u_accept;
+    P.u_sample = u_sample;
+    P.out_tokens = out_tokens;
+    P.num_accepted = num_accepted;
+    P.p_draft = p_draft;
+    P.q_draft = q_draft;
+    P.dstats_in = (const Stat *)draft_stats;
+    return launch(P, stream);
+}
+
+sv_status spec_draft_confidence_stats(const void *draft_logits, sv_dtype dt, const int32_t *max_depth, int32_t B,
+                                      int32_t K, int32_t V, float *conf, void *draft_stats, void *workspace,
+                                      size_t ws_bytes, hipStream_t stream)
+{
+    sv_status st = check_shape(B, K, V);
+    if (st != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (K == 0) return SV_OK;
+    if (!draft_logits || !draft_stats || ((uintptr_t)draft_stats & 15u) != 0) return SV_ERR_INVALID_ARG;
+    if (!aligned16(draft_logits)) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K, V, L);
+    if ((st = check_ws(workspace, ws_bytes, L)) != SV_OK) return st;
+    Params P = base_params(B, K, V, dt, MODE_CONF, L, workspace);
+    P.draft = draft_logits;
+    P.max_depth = max_depth;
+    P.conf = conf;
+    P.dstats_out = (Stat *)draft_stats;
     return launch(P, stream);
 }
 

@@ -166,6 +166,55 @@ sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt,
                                 int32_t B, int32_t K, int32_t V, float *conf,
                                 void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Draft-row statistics, for reuse by spec_verify_sample_reuse.  Per draft
+ * row (b, k): max = the row's largest logit, sum = the sum over the row of
+ * 2^((v - max) * c) with c = (float)log2(e) (that is, T = 1), so that
+ * softmax(y)_v = 2^((v - max) * c) / sum.  A row the confidence pass did not
+ * read (k >= max_depth[b]) or could not use (NaN, +inf, all -inf) gets NaN
+ * in both fields.  16 bytes, 16-byte aligned. */
+typedef struct {
+    float max;
+    int32_t reserved;
+    double sum;
+} sv_row_stat;
+
+/* spec_draft_confidence that also returns every read draft row's
+ * statistics.  The prefix confidence that drives D-cut is computed from the
+ * draft rows before the target verifies them ([Stack], section "What
+ * problem does it solve", inference layer); at T = 1 those rows' softmax
+ * statistics are exactly the q_k normalisers the accept test needs, so a
+ * later spec_verify_sample_reuse need not read the draft rows again except
+ * the one it draws from.
+ *   conf         [B, K] float (out) or NULL
+ *   draft_stats  [B, K] sv_row_stat (out)
+ *   Other arguments as in spec_draft_confidence. */
+sv_status spec_draft_confidence_stats(const void *draft_logits, sv_dtype dt,
+                                      const int32_t *max_depth,
+                                      int32_t B, int32_t K, int32_t V, float *conf,
+                                      void *draft_stats,
+                                      void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* spec_verify_sample with the draft rows' statistics given: for a request
+ * with temperature exactly 1 the draft rows 0..d-1 are not streamed; their
+ * (max, sum) come from draft_stats[b, 0..d-1] (as written by
+ * spec_draft_confidence_stats on the same draft logits) and the draft logit
+ * at each drafted token is read singly.  Requests with another temperature
+ * are verified exactly as by spec_verify_sample.  The rule and every output
+ * are those of spec_verify_sample; a NaN statistic (a row the confidence
+ * pass did not read, depth[b] > its max_depth[b]) makes the request bad
+ * (num_accepted = -1).  The draft row a residual draw needs is still read.
+ *   draft_stats  [B, K] sv_row_stat (read: rows 0..d-1 of T = 1 requests)
+ *   Other arguments as in spec_verify_sample. */
+sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_logits,
+                                   sv_dtype dt, const int32_t *draft_tokens,
+                                   const int32_t *depth, const float *temperature,
+                                   const float *u_accept, const float *u_sample,
+                                   const void *draft_stats,
+                                   int32_t B, int32_t K, int32_t V,
+                                   int32_t *out_tokens, int32_t *num_accepted,
+                                   float *p_draft, float *q_draft,
+                                   void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* D-cut verification-depth allocation: verification compute is a shared
  * batch-level budget that is moved toward the requests whose drafted
  * prefixes are most likely to be accepted ([Stack], section "What problem

@@ -130,3 +130,13 @@ def run_sample(w: synth.Workload, depth=None):
                                     dev(w.u_accept), dev(w.u_sample), dev(depth))
     torch.cuda.synchronize()
     return host(out), host(n), host(p), host(q)
+
+
+def run_sample_reuse(w: synth.Workload, depth=None, max_depth=None):
+    """Confidence pass with statistics, then verification reusing them."""
+    import draft_verification_verify_amd as sv
+    _, st = sv.draft_confidence_stats(dev(w.draft), dev(max_depth), want_conf=False)
+    out, n, p, q = sv.verify_sample_reuse(dev(w.target), dev(w.draft), dev(w.tokens), dev(w.temperature),
+                                          dev(w.u_accept), dev(w.u_sample), st, dev(depth))
+    torch.cuda.synchronize()
+    return host(out), host(n), host(p), host(q)

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -120,6 +120,32 @@ def test_confidence_and_dcut_host_errors():
     assert L.dcut_allocate(NULL, NULL, 4, 3, 8, FAKE, NULL) == 1
     assert L.dcut_allocate(FAKE, NULL, 4, 3, 8, NULL, NULL) == 1
     assert L.dcut_allocate(FAKE, NULL, 4096, 16, 9000, FAKE, NULL) == 2  # B*K > 32768
+
+
+def test_reuse_entry_points_host_errors():
+    wsb = sv.workspace_size(4, 3, 1000)
+    stats, stats_mis = FAKE, ctypes.c_void_p(0x100008)
+    # spec_draft_confidence_stats: stats required and 16-byte aligned, conf optional
+    cs = L.spec_draft_confidence_stats
+    assert cs(NULL, 1, NULL, 4, 3, 1000, FAKE, stats, FAKE, wsb, NULL) == 1
+    assert cs(FAKE, 1, NULL, 4, 3, 1000, FAKE, NULL, FAKE, wsb, NULL) == 1
+    assert cs(FAKE, 1, NULL, 4, 3, 1000, FAKE, stats_mis, FAKE, wsb, NULL) == 1
+    assert cs(FAKE, 1, NULL, 4, 3, 1000, NULL, stats, FAKE, 16, NULL) == 3
+    assert cs(FAKE, 9, NULL, 4, 3, 1000, NULL, stats, FAKE, wsb, NULL) == 1
+    # spec_verify_sample_reuse: the statistics are required when K > 0
+    def reuse(draft_stats=stats, **kw):
+        a = dict(target=FAKE, draft=FAKE, dt=1, tokens=FAKE, depth=NULL, T=FAKE, ua=FAKE, us=FAKE,
+                 B=4, K=3, V=1000, out=FAKE, num=FAKE, ws=FAKE, wsb=wsb)
+        a.update(kw)
+        return L.spec_verify_sample_reuse(a["target"], a["draft"], a["dt"], a["tokens"], a["depth"], a["T"],
+                                          a["ua"], a["us"], draft_stats, a["B"], a["K"], a["V"], a["out"],
+                                          a["num"], NULL, NULL, a["ws"], a["wsb"], NULL)
+    assert reuse(draft_stats=NULL) == 1
+    assert reuse(draft_stats=stats_mis) == 1
+    assert reuse(target=NULL) == 1
+    assert reuse(draft=NULL) == 1
+    assert reuse(us=NULL) == 1
+    assert reuse(wsb=10) == 3
 
 
 def test_binding_shares_torch_hip_runtime():

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from parity import Tally, compare_greedy, compare_sample, dev, host, run_greedy, run_sample
+from parity import Tally, compare_greedy, compare_sample, dev, host, run_greedy, run_sample, run_sample_reuse
 
 pytestmark = pytest.mark.gpu
 
@@ -229,6 +229,69 @@ def test_mixed_fp32_pipeline_full_size():
     tal = compare_sample(w, out, n, p, q, depth)
     tal.assert_ok("mixed")
     assert np.all(n >= 0)
+
+
+# ---------------------------------------------- draft-statistics reuse ----
+
+def test_reuse_pipeline_full_size():
+    note("reuse pipeline B=64 K=16 V=128000: confidence + row statistics -> dcut_allocate(384) -> sample_reuse")
+    import draft_verification_verify_amd as sv
+    w = synth.dcut_ragged(0, T=1.0)
+    conf_g, st = sv.draft_confidence_stats(dev(w.draft))
+    conf_o = oracle.draft_confidence(w.draft)
+    assert np.max(np.abs(host(conf_g) - conf_o) / conf_o) < 2e-6
+    mx, sm = (host(t) for t in sv.row_stat_fields(st))
+    # the statistics are the rows' maxima and softmax normalisers at T = 1
+    assert np.array_equal(mx, synth.as_f64(w.draft).max(axis=2).astype(np.float32))
+    assert np.max(np.abs(1.0 / sm - conf_o) / conf_o) < 2e-6
+    depth = oracle.dcut_allocate(conf_o, w.budget)
+    out, n, p, q = sv.verify_sample_reuse(dev(w.target), dev(w.draft), dev(w.tokens), dev(w.temperature),
+                                          dev(w.u_accept), dev(w.u_sample), st, dev(depth))
+    torch.cuda.synchronize()
+    tal = compare_sample(w, host(out), host(n), host(p), host(q), depth)
+    tal.assert_ok("reuse ragged")
+    assert np.all(host(n) >= 0)
+
+
+def test_reuse_mixed_temperatures_fp32():
+    note("reuse mixed fp32 B=64 V=152064: T in {0, 0.7, 1}; only T = 1 requests use the statistics")
+    w = synth.mixed(0)
+    conf_o = oracle.draft_confidence(w.draft, w.max_depth)
+    depth = oracle.dcut_allocate(conf_o, w.budget, w.max_depth)
+    out, n, p, q = run_sample_reuse(w, depth, w.max_depth)
+    tal = compare_sample(w, out, n, p, q, depth)
+    tal.assert_ok("reuse mixed")
+    assert np.all(n >= 0)
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 7), ("bf16", 64), ("f32", 1000), ("bf16", 4099), ("f32", 9001)])
+@pytest.mark.parametrize("K", [1, 3, 16])
+def test_reuse_fuzz_shapes(dtype, V, K):
+    note(f"reuse fuzz {dtype} V={V} K={K}")
+    B = 6
+    w = synth.random_case(V * 11 + K, B=B, K=K, V=V, dtype=dtype, temps=(0.0, 0.7, 1.0, 1.0), sigma=0.6)
+    g = np.random.default_rng(V * 5 + K)
+    depth = g.integers(0, K + 1, B).astype(np.int32)
+    tal = Tally()
+    out, n, p, q = run_sample_reuse(w, depth)
+    compare_sample(w, out, n, p, q, depth, tal)
+    out, n, p, q = run_sample_reuse(w)
+    compare_sample(w, out, n, p, q, None, tal)
+    tal.assert_ok(f"reuse {dtype} V={V} K={K}")
+
+
+def test_reuse_depth_beyond_statistics_is_bad():
+    note("reuse: a depth past the confidence pass's max_depth is bad data; the rest still verify")
+    w = synth.random_case(77, B=4, K=3, V=1000, dtype="f32", temps=(1.0,))
+    max_depth = np.array([3, 1, 3, 0], np.int32)
+    depth = np.array([3, 2, 1, 0], np.int32)
+    out, n, p, q = run_sample_reuse(w, depth, max_depth)
+    assert n[1] == -1 and np.all(out[1] == -1)
+    ok = np.array([0, 2, 3])
+    sub = synth.Workload(w.name, w.dtype, w.target[ok], w.draft[ok], w.tokens[ok], w.temperature[ok],
+                         w.u_accept[ok], w.u_sample[ok], w.max_depth[ok])
+    tal = compare_sample(sub, out[ok], n[ok], p[ok], q[ok], depth[ok])
+    tal.assert_ok("reuse partial")
 
 
 def test_determinism_and_workspace_reuse():
