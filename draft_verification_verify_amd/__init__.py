@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     L.spec_verify_sample_reuse.restype = ctypes.c_int
     L.spec_verify_sample_reuse.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                            vp, vp, vp, vp, vp, sz, vp]
+    L.spec_accept_stats_update.restype = ctypes.c_int
+    L.spec_accept_stats_update.argtypes = [vp, vp, i32, i32, vp, vp]
     L.dcut_allocate.restype = ctypes.c_int
     L.dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     L.spec_verify_timing_begin.restype = ctypes.c_int
@@ -80,7 +82,7 @@ lib = _load()
 EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify_last_error",
             "spec_verify_workspace_size", "spec_verify_timing_begin", "spec_verify_timing_end",
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
-            "spec_draft_confidence_stats", "spec_verify_sample_reuse")
+            "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update")
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
@@ -311,6 +313,32 @@ def verify_sample_reuse(target, draft, tokens, temperature, u_accept, u_sample, 
                                       _ptr(q_draft), _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_sample_reuse", st)
     return out_tokens, num_accepted, p_draft, q_draft
+
+
+def accept_stats_update(num_accepted, K: int, depth=None, counters=None, *, stream=None):
+    """Adds one call's acceptance statistics into counters (int64 [2K + 4] on
+    the device; created zeroed when None) and returns them."""
+    torch = _torch()
+    B = num_accepted.shape[0]
+    _check(num_accepted, "num_accepted", torch.int32, (B,))
+    _check(depth, "depth", torch.int32, (B,))
+    if counters is None:
+        counters = torch.zeros(2 * K + 4, dtype=torch.int64, device=num_accepted.device)
+    _check(counters, "counters", torch.int64, (2 * K + 4,))
+    st = lib.spec_accept_stats_update(_ptr(num_accepted), _ptr(depth), B, K, _ptr(counters), _stream(stream))
+    _raise("spec_accept_stats_update", st)
+    return counters
+
+
+def accept_stats_summary(counters, K: int) -> dict:
+    """Per-position acceptance, mean accepted length and tau from the counters."""
+    c = counters.cpu().tolist() if hasattr(counters, "cpu") else list(counters)
+    reached, accepted = c[:K], c[K:2 * K]
+    req = c[2 * K]
+    return {"alpha": [a / r if r else float("nan") for a, r in zip(accepted, reached)],
+            "reached": reached, "accepted": accepted, "requests": req, "bad": c[2 * K + 1],
+            "mean_accepted": c[2 * K + 2] / req if req else float("nan"),
+            "tau": c[2 * K + 3] / req if req else float("nan")}
 
 
 def dcut_allocate(conf, budget: int, max_depth=None, *, depth_out=None, stream=None):

@@ -1879,6 +1879,64 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
 }
 
 // ---------------------------------------------------------------------------
+// Acceptance statistics: one workgroup.  Per valid request with n accepted
+// drafts and window d, position k < d was tested iff n >= k and accepted iff
+// n > k; with n <= d that makes accepted[k] = #{n > k} and reached[k] =
+// accepted[k] + #{n == k < d} (the requests rejected at k).  So each request
+// adds to two LDS histograms, and suffix sums give the counters.
+// ---------------------------------------------------------------------------
+
+constexpr int STATS_WG = 256;
+
+__global__ __launch_bounds__(STATS_WG) void accept_stats_kernel(const int32_t *num_accepted, const int32_t *depth,
+                                                                int B, int K, unsigned long long *counters)
+{
+    extern __shared__ unsigned int hist[];   // [K + 1] #{n}, then [K] #{rejected at k}
+    __shared__ unsigned long long tot[4];    // requests, bad, sum n, sum n + 1
+    unsigned int *hn = hist, *hr = hist + K + 1;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 2 * K + 1; i += STATS_WG) hist[i] = 0u;
+    if (tid < 4) tot[tid] = 0ull;
+    __syncthreads();
+    unsigned long long req = 0, bad = 0, sn = 0;
+    for (int b = tid; b < B; b += STATS_WG) {
+        const int n = num_accepted[b];
+        if (n < 0) { ++bad; continue; }
+        // positions outside the window [0, min(d, K)) are not counted
+        const int d = min(max(depth ? depth[b] : K, 0), K);
+        const int nw = min(n, d);
+        ++req;
+        sn += (unsigned long long)n;
+        atomicAdd(&hn[nw], 1u);
+        if (nw < d) atomicAdd(&hr[nw], 1u);
+    }
+    atomicAdd(&tot[0], req);
+    atomicAdd(&tot[1], bad);
+    atomicAdd(&tot[2], sn);
+    __syncthreads();
+    // suffix sums over n (K + 1 bins; K is at most 1024, one pass of the workgroup per 256)
+    if (tid == 0) {
+        unsigned long long above = 0;   // #{n > k}
+        for (int k = K - 1; k >= 0; --k) {
+            above += hn[k + 1];
+            hn[k + 1] = (unsigned int)above;   // now accepted[k], stored one bin up
+        }
+    }
+    __syncthreads();
+    for (int k = tid; k < K; k += STATS_WG) {
+        const unsigned int acc = hn[k + 1];
+        if (acc + hr[k]) atomicAdd(&counters[k], (unsigned long long)(acc + hr[k]));
+        if (acc) atomicAdd(&counters[K + k], (unsigned long long)acc);
+    }
+    if (tid == 0) {
+        atomicAdd(&counters[2 * K], tot[0]);
+        atomicAdd(&counters[2 * K + 1], tot[1]);
+        atomicAdd(&counters[2 * K + 2], tot[2]);
+        atomicAdd(&counters[2 * K + 3], tot[2] + tot[0]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // D-cut allocation: one workgroup of 1024 threads; keys in LDS.
 // ---------------------------------------------------------------------------
 
@@ -2364,6 +2422,19 @@ sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt, const int
     P.max_depth = max_depth;
     P.conf = conf;
     return launch(P, stream);
+}
+
+sv_status spec_accept_stats_update(const int32_t *num_accepted, const int32_t *depth, int32_t B, int32_t K,
+                                   unsigned long long *counters, hipStream_t stream)
+{
+    if (B < 1 || K < 0 || !num_accepted || !counters) return SV_ERR_INVALID_ARG;
+    if (B > B_MAX || K > K_MAX) return SV_ERR_UNSUPPORTED;
+    if (((uintptr_t)counters & 7u) != 0) return SV_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    const size_t lds = sizeof(unsigned int) * (size_t)(2 * K + 1);
+    hipLaunchKernelGGL(accept_stats_kernel, dim3(1), dim3(STATS_WG), lds, stream, num_accepted, depth, B, K,
+                       counters);
+    return hip_status("accept_stats_kernel launch");
 }
 
 sv_status dcut_allocate(const float *conf, const int32_t *max_depth, int32_t B, int32_t K, int32_t budget,

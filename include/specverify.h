@@ -215,6 +215,26 @@ sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_
                                    float *p_draft, float *q_draft,
                                    void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Acceptance statistics across calls: adds one verification call's outcome
+ * into counters [2K + 4] of uint64 (device memory the caller zeroes once and
+ * keeps).  A serving system has to watch acceptance length ([Remio],
+ * section "Cosa non dimostrano i numeri di AngelSpec"), and per-position
+ * acceptance is what [Hamidun] reports (section "Comment fonctionne la voie
+ * MTP").  For request b with num_accepted n >= 0 and window
+ * d = depth[b] (NULL => K), over positions k < min(d, K):
+ *   counters[k]     += 1 if position k was tested (n >= k)      (reached)
+ *   counters[K + k] += 1 if it was accepted (n > k)            (accepted)
+ * and counters[2K] += 1 (requests), counters[2K + 2] += n,
+ * counters[2K + 3] += n + 1 (tokens committed, the correction or bonus
+ * included); a request with n < 0 adds 1 to counters[2K + 1] (bad) only.
+ * alpha_k = accepted / reached, mean accepted = counters[2K+2] / requests,
+ * tau = counters[2K+3] / requests.  Inputs are the num_accepted and depth of
+ * a spec_verify_* call; stream-ordered after it on the same stream.
+ *   counters  [2K + 4] uint64, 8-byte aligned (read-modify-write, atomic) */
+sv_status spec_accept_stats_update(const int32_t *num_accepted, const int32_t *depth,
+                                   int32_t B, int32_t K, unsigned long long *counters,
+                                   hipStream_t stream);
+
 /* D-cut verification-depth allocation: verification compute is a shared
  * batch-level budget that is moved toward the requests whose drafted
  * prefixes are most likely to be accepted ([Stack], section "What problem

@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_draft_confidence.restype = ctypes.c_int
         L.oracle_dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp]
         L.oracle_dcut_allocate.restype = ctypes.c_int
+        L.oracle_accept_stats.argtypes = [vp, vp, i32, i32, vp]
+        L.oracle_accept_stats.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -190,3 +192,19 @@ def dcut_allocate(conf, budget: int, max_depth=None):
     if rc != 0:
         raise ValueError(f"dcut_allocate rejected its arguments (code {rc})")
     return depth
+
+
+def accept_stats(num_accepted, K: int, depth=None, counters=None):
+    """Adds one call's acceptance statistics into counters[2K + 4] (uint64):
+    reached[0:K], accepted[K:2K], then requests, bad, sum n, sum (n + 1)."""
+    num_accepted = _c(num_accepted, np.int32)
+    B = num_accepted.shape[0]
+    depth = _c(depth, np.int32)
+    if counters is None:
+        counters = np.zeros(2 * K + 4, np.uint64)
+    assert counters.dtype == np.uint64 and counters.shape == (2 * K + 4,)
+    rc = lib().oracle_accept_stats(_ptr(num_accepted), _ptr(depth), B, K, _ptr(counters))
+    if rc != 0:
+        raise ValueError(f"accept_stats rejected its arguments (code {rc})")
+    return counters
+

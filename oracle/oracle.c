@@ -439,3 +439,40 @@ int oracle_dcut_allocate(const float *conf, const int32_t *max_depth, int32_t B,
     free(e);
     return 0;
 }
+
+/* Acceptance statistics of one verification call, added into counters
+ * [2K + 4] (the monitoring of acceptance length the pages ask of a serving
+ * system, [Remio] section "Cosa non dimostrano i numeri di AngelSpec"; the
+ * per-position acceptance [Hamidun] reports, section "Comment fonctionne la
+ * voie MTP").  The definition, one request at a time:
+ *   a request with num_accepted n < 0 is bad: counters[2K + 1] += 1;
+ *   otherwise, with window d = depth[b] (NULL: K):
+ *     for every position k < d that was tested (all drafts before it were
+ *     accepted, n >= k): counters[k] += 1 (reached);
+ *     if it was also accepted (n > k): counters[K + k] += 1 (accepted);
+ *     counters[2K] += 1 (requests), counters[2K + 2] += n,
+ *     counters[2K + 3] += n + 1 (tokens committed: accepted prefix plus the
+ *     correction or bonus token).
+ * Returns 1 for B < 1 or K < 0. */
+int oracle_accept_stats(const int32_t *num_accepted, const int32_t *depth, int32_t B, int32_t K,
+                        uint64_t *counters)
+{
+    if (B < 1 || K < 0) return 1;
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t n = num_accepted[b];
+        if (n < 0) {
+            counters[2 * K + 1] += 1;
+            continue;
+        }
+        int32_t d = depth ? depth[b] : K;
+        for (int32_t k = 0; k < d && k < K; ++k) {
+            if (n >= k) counters[k] += 1;
+            if (n > k) counters[K + k] += 1;
+        }
+        counters[2 * K] += 1;
+        counters[2 * K + 2] += (uint64_t)n;
+        counters[2 * K + 3] += (uint64_t)n + 1;
+    }
+    return 0;
+}
+

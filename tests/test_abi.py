@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -146,6 +146,16 @@ def test_reuse_entry_points_host_errors():
     assert reuse(draft=NULL) == 1
     assert reuse(us=NULL) == 1
     assert reuse(wsb=10) == 3
+
+
+def test_accept_stats_host_errors():
+    f = L.spec_accept_stats_update
+    assert f(NULL, NULL, 4, 3, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, NULL, NULL) == 1
+    assert f(FAKE, NULL, 0, 3, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, -1, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, ctypes.c_void_p(0x100004), NULL) == 1   # counters 8-byte aligned
+    assert f(FAKE, NULL, 5000, 3, FAKE, NULL) == 2
 
 
 def test_binding_shares_torch_hip_runtime():

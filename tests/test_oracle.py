@@ -549,3 +549,40 @@ def test_metric_definition_tau_counts_bonus():
     for pair in m["pairs"]:
         assert abs((1 + K * pair["rate"]) - pair["tau"]) <= m["print_rounding"]["tau"] + K * m["print_rounding"]["rate"]
         assert abs(pair["rate"] * K - pair["tau"]) > 0.3      # tau does not exclude the bonus
+
+
+# ------------------------------------------------- acceptance statistics ----
+
+def test_accept_stats_hand_case():
+    # n = (0, 2, 3, bad, 1) with windows (3, 3, 3, 3, 1), K = 3, worked by hand:
+    # position 0 is tested by every valid request, accepted by all but the first;
+    # position 1 by the two that got past 0 inside a 3-wide window; and so on.
+    n = np.array([0, 2, 3, -1, 1], np.int32)
+    d = np.array([3, 3, 3, 3, 1], np.int32)
+    c = oracle.accept_stats(n, 3, d)
+    assert c.tolist() == [4, 2, 2, 3, 2, 1, 4, 1, 6, 10]
+
+
+def test_accept_stats_invariants_and_accumulation():
+    g = np.random.default_rng(5)
+    K, B = 7, 500
+    d = g.integers(0, K + 1, B).astype(np.int32)
+    n = np.minimum(g.integers(0, K + 1, B), d).astype(np.int32)
+    n[g.random(B) < 0.05] = -1
+    c = oracle.accept_stats(n, K, d)
+    ok = n >= 0
+    reached, accepted = c[:K].astype(np.int64), c[K:2 * K].astype(np.int64)
+    # every accepted draft is counted once at its position
+    assert accepted.sum() == np.minimum(n[ok], d[ok]).sum()
+    # a tested position that was not accepted is exactly one rejection
+    rej = np.bincount(n[ok & (n < d)], minlength=K)[:K]
+    assert np.array_equal(reached - accepted, rej)
+    assert c[2 * K] == ok.sum() and c[2 * K + 1] == (~ok).sum()
+    assert c[2 * K + 2] == n[ok].sum() and c[2 * K + 3] == n[ok].sum() + ok.sum()
+    # the counters add across calls
+    c2 = oracle.accept_stats(n, K, d, c.copy())
+    assert np.array_equal(c2, 2 * c)
+    # positions outside the window are never counted; NULL depth means K
+    c3 = oracle.accept_stats(np.array([5], np.int32), 3, np.array([9], np.int32))
+    assert c3[:3].tolist() == [1, 1, 1] and c3[3:6].tolist() == [1, 1, 1]
+    assert np.array_equal(oracle.accept_stats(n, K), oracle.accept_stats(n, K, np.full(B, K, np.int32)))
