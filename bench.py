@@ -344,6 +344,16 @@ def main():
             "bytes_per_step": int((B * K + int(rdep.sum())) * V * 2),
             "note": "confidence pass (with row statistics) reads all 1024 draft rows; the verify reuses "
                     "them and streams sum(d_b) target rows"}
+        # cost-aware D-cut on the same confidences (the pages' latency table), alone
+        cdep = torch.empty((B,), dtype=torch.int32, device="cuda")
+
+        def cstep2(i):
+            sv.dcut_allocate_cost(conf, 96.0, depth_out=cdep, stream=stream)
+        _, cper2, _ = timed(cstep2, steps2, warm2)
+        sec["dcut_allocate_cost_B64_K16"] = {
+            "ms": float(np.mean(cper2)), "admitted": int((cdep > 0).sum().item()),
+            "verify_slots": int(cdep.sum().item()),
+            "note": "max_verify 96 in the table's cost units (1.0 at depth 1 ... 3.0 at depth 16); one workgroup"}
         del copies
         # mixed fp32 batch: per-request K_b and T_b, dcut_allocate(512), one sampled launch
         wm = synth.mixed(args.seed)

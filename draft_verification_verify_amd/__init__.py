@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     L.spec_verify_sample_reuse.restype = ctypes.c_int
     L.spec_verify_sample_reuse.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                            vp, vp, vp, vp, vp, sz, vp]
+    L.dcut_allocate_cost.restype = ctypes.c_int
+    L.dcut_allocate_cost.argtypes = [vp, vp, i32, i32, vp, vp, i32, ctypes.c_double, vp, vp]
     L.spec_accept_stats_update.restype = ctypes.c_int
     L.spec_accept_stats_update.argtypes = [vp, vp, i32, i32, vp, vp]
     L.dcut_allocate.restype = ctypes.c_int
@@ -82,7 +84,8 @@ lib = _load()
 EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify_last_error",
             "spec_verify_workspace_size", "spec_verify_timing_begin", "spec_verify_timing_end",
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
-            "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update")
+            "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
+            "dcut_allocate_cost")
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
@@ -313,6 +316,29 @@ def verify_sample_reuse(target, draft, tokens, temperature, u_accept, u_sample, 
                                       _ptr(q_draft), _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_sample_reuse", st)
     return out_tokens, num_accepted, p_draft, q_draft
+
+
+# the latency table printed with the pages' cost-aware D-cut sketch (depth: relative cost)
+DEFAULT_COST_TABLE = ((1.0, 1.0), (2.0, 1.2), (4.0, 1.5), (8.0, 2.0), (16.0, 3.0))
+
+
+def dcut_allocate_cost(conf, max_verify: float, max_depth=None, table=DEFAULT_COST_TABLE, *,
+                       depth_out=None, stream=None):
+    """Cost-aware D-cut (per-request best benefit/cost depth, greedy budget fill)."""
+    torch = _torch()
+    B, K = conf.shape
+    _check(conf, "conf", torch.float32)
+    _check(max_depth, "max_depth", torch.int32, (B,))
+    if depth_out is None:
+        depth_out = torch.empty((B,), dtype=torch.int32, device=conf.device)
+    n = len(table)
+    td = (ctypes.c_double * n)(*[float(p[0]) for p in table])
+    tc = (ctypes.c_double * n)(*[float(p[1]) for p in table])
+    st = lib.dcut_allocate_cost(_ptr(conf), _ptr(max_depth), B, K, ctypes.cast(td, ctypes.c_void_p),
+                                ctypes.cast(tc, ctypes.c_void_p), n, float(max_verify),
+                                _ptr(depth_out), _stream(stream))
+    _raise("dcut_allocate_cost", st)
+    return depth_out
 
 
 def accept_stats_update(num_accepted, K: int, depth=None, counters=None, *, stream=None):

@@ -1878,6 +1878,112 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
     }
 }
 
+// Confidence as the D-cut rules read it: 0 for NaN or c <= 0, 1 above 1.
+__device__ __forceinline__ float sanitize_conf(float c)
+{
+    if (!(c > 0.0f)) return 0.0f;
+    return c > 1.0f ? 1.0f : c;
+}
+
+// ---------------------------------------------------------------------------
+// Cost-aware D-cut: one workgroup of 1024 threads.  Per request the depth with
+// the best benefit (prefix confidence times depth over the interpolated cost,
+// in double), then candidates ranked by (benefit desc, request asc) by
+// counting, then one thread fills the cost budget in rank order.  LDS:
+// benefit (8 B), chosen depth and rank (2 B each) per request, cost per depth.
+// ---------------------------------------------------------------------------
+
+constexpr int COST_TAB_MAX = 32;
+constexpr int COST_WG = 1024;
+constexpr int COST_B_MAX = 4096;
+
+struct CostTable {
+    double t[COST_TAB_MAX];   // depths, strictly increasing
+    double c[COST_TAB_MAX];   // costs, finite and > 0
+    int n;
+};
+
+// Piecewise-linear cost, first segment holding d; no contraction so the
+// rounding is that of the written operations.
+__device__ double table_cost(const CostTable &T, double d)
+{
+#pragma clang fp contract(off)
+    if (d <= T.t[0]) return T.c[0];
+    if (d >= T.t[T.n - 1]) return T.c[T.n - 1];
+    for (int i = 0; i + 1 < T.n; ++i) {
+        if (T.t[i] <= d && d <= T.t[i + 1]) {
+            const double r = (d - T.t[i]) / (T.t[i + 1] - T.t[i]);
+            return T.c[i] + r * (T.c[i + 1] - T.c[i]);
+        }
+    }
+    return T.c[T.n - 1];
+}
+
+__global__ __launch_bounds__(COST_WG) void dcut_cost_kernel(const float *conf, const int32_t *max_depth, int B,
+                                                            int K, CostTable T, double max_verify,
+                                                            int32_t *depth_out)
+{
+#pragma clang fp contract(off)
+    extern __shared__ double cost_smem[];
+    double *costd = cost_smem;                       // [K + 1] cost(d)
+    double *ben = cost_smem + (K + 1);               // [B] best benefit, -1 for no candidate
+    uint16_t *dst = (uint16_t *)(ben + B);           // [B] chosen depth (0 none)
+    uint16_t *order = dst + B;                       // [B] request at each rank
+    __shared__ int sh_cand[COST_WG / 64];
+    __shared__ uint8_t bad_req[COST_B_MAX];
+    const int tid = threadIdx.x;
+    for (int d = tid; d <= K; d += COST_WG) costd[d] = d == 0 ? 0.0 : table_cost(T, (double)d);
+    __syncthreads();
+    int cand = 0;
+    for (int b = tid; b < B; b += COST_WG) {
+        const int Kb = max_depth ? max_depth[b] : K;
+        bad_req[b] = (Kb < 0 || Kb > K) ? 1 : 0;
+        double best = -1.0;
+        int dbest = 0;
+        if (Kb >= 1 && Kb <= K) {
+            double P = 1.0;
+            for (int d = 1; d <= Kb; ++d) {
+                P = P * (double)sanitize_conf(conf[(int64_t)b * K + d - 1]);
+                const double v = (P * (double)d) / costd[d];
+                if (v > best) { best = v; dbest = d; }
+            }
+            ++cand;
+        }
+        ben[b] = best;
+        dst[b] = (uint16_t)dbest;
+    }
+    cand = wave_sum_i(cand);
+    if (lane_id() == 0) sh_cand[wave_id()] = cand;
+    __syncthreads();
+    int ncand = 0;
+    for (int w = 0; w < COST_WG / 64; ++w) ncand += sh_cand[w];
+    // rank of each candidate: how many candidates precede it
+    for (int b = tid; b < B; b += COST_WG) {
+        if (dst[b] == 0) continue;
+        const double v = ben[b];
+        int r = 0;
+        for (int o = 0; o < B; ++o) {
+            const double w = ben[o];
+            r += (dst[o] != 0) && (w > v || (w == v && o < b));
+        }
+        order[r] = (uint16_t)b;
+    }
+    __syncthreads();
+    // fill the budget in rank order (sequential: a candidate that does not fit
+    // is skipped and a later, cheaper one may still fit)
+    if (tid == 0) {
+        double total = 0.0;
+        for (int i = 0; i < ncand; ++i) {
+            const int b = order[i];
+            const double c = costd[dst[b]];
+            if (total + c <= max_verify) total = total + c;
+            else dst[b] = 0;
+        }
+    }
+    __syncthreads();
+    for (int b = tid; b < B; b += COST_WG) depth_out[b] = bad_req[b] ? -1 : (int32_t)dst[b];
+}
+
 // ---------------------------------------------------------------------------
 // Acceptance statistics: one workgroup.  Per valid request with n accepted
 // drafts and window d, position k < d was tested iff n >= k and accepted iff
@@ -1939,12 +2045,6 @@ __global__ __launch_bounds__(STATS_WG) void accept_stats_kernel(const int32_t *n
 // ---------------------------------------------------------------------------
 // D-cut allocation: one workgroup of 1024 threads; keys in LDS.
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float sanitize_conf(float c)
-{
-    if (!(c > 0.0f)) return 0.0f;
-    return c > 1.0f ? 1.0f : c;
-}
 
 __device__ int block_sum_int(int v, int *sm32)
 {
@@ -2422,6 +2522,32 @@ sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt, const int
     P.max_depth = max_depth;
     P.conf = conf;
     return launch(P, stream);
+}
+
+sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth, int32_t B, int32_t K,
+                             const double *table_depth, const double *table_cost, int32_t table_n,
+                             double max_verify, int32_t *depth_out, hipStream_t stream)
+{
+    if (B < 1 || K < 0 || !depth_out || (K > 0 && !conf)) return SV_ERR_INVALID_ARG;
+    if (B > COST_B_MAX || K > K_MAX) return SV_ERR_UNSUPPORTED;
+    if (!table_depth || !table_cost || table_n < 1 || table_n > COST_TAB_MAX) return SV_ERR_INVALID_ARG;
+    if (!(max_verify >= 0.0) || max_verify == INFINITY) return SV_ERR_INVALID_ARG;
+    CostTable T;
+    memset(&T, 0, sizeof T);
+    T.n = table_n;
+    for (int i = 0; i < table_n; ++i) {
+        const double t = table_depth[i], c = table_cost[i];
+        if (!std::isfinite(t) || !std::isfinite(c) || !(c > 0.0)) return SV_ERR_INVALID_ARG;
+        if (i > 0 && !(t > table_depth[i - 1])) return SV_ERR_INVALID_ARG;
+        T.t[i] = t;
+        T.c[i] = c;
+    }
+    const size_t lds = sizeof(double) * (size_t)(K + 1 + B) + 2 * sizeof(uint16_t) * (size_t)B;
+    if (lds > 60 * 1024) return SV_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(dcut_cost_kernel, dim3(1), dim3(COST_WG), lds, stream, conf, max_depth, B, K, T, max_verify,
+                       depth_out);
+    return hip_status("dcut_cost_kernel launch");
 }
 
 sv_status spec_accept_stats_update(const int32_t *num_accepted, const int32_t *depth, int32_t B, int32_t K,

@@ -215,6 +215,38 @@ sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_
                                    float *p_draft, float *q_draft,
                                    void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Cost-aware D-cut: the pages describe D-cut as weighing the expected value
+ * of keeping more drafted positions against a profiled runtime cost and
+ * steering verification toward high-confidence prefixes under a shared
+ * budget ([Remio], section "Come AngelSpec rende DFly più selettivo").
+ * Built as a per-request choice of depth followed by a greedy fill of a cost
+ * budget (all arithmetic in double, in the order written):
+ *   cost(d)  piecewise-linear in the latency table (table_depth[i],
+ *            table_cost[i]): table_cost[0] for d <= table_depth[0],
+ *            table_cost[n-1] for d >= table_depth[n-1], else on the first
+ *            segment i with table_depth[i] <= d <= table_depth[i+1]:
+ *            table_cost[i] + r * (table_cost[i+1] - table_cost[i]),
+ *            r = (d - table_depth[i]) / (table_depth[i+1] - table_depth[i]);
+ *   per request b with K_b = max_depth[b] (NULL => K) in [1, K]:
+ *            P_d = P_{d-1} * s(conf[b, d-1]) from P_0 = 1 (s as in
+ *            dcut_allocate), benefit(d) = (P_d * d) / cost(d), and d*_b =
+ *            the smallest d in [1, K_b] with the largest benefit;
+ *   candidates in order of benefit descending, then b ascending, each
+ *   admitted iff the admitted costs so far plus cost(d*_b) <= max_verify.
+ *   depth_out[b] = d*_b when admitted, 0 when not (or K_b = 0), -1 when K_b
+ *   is outside [0, K].
+ *   conf         [B, K] float (device)
+ *   table_depth, table_cost  HOST arrays of table_n (1..32) doubles: depths
+ *                strictly increasing, costs finite and > 0 (copied into the
+ *                launch; the call keeps no reference)
+ *   max_verify   finite, >= 0
+ *   B <= 4096 and B*8 + K*8 + B*4 <= 60 KiB of LDS (SV_ERR_UNSUPPORTED). */
+sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth,
+                             int32_t B, int32_t K,
+                             const double *table_depth, const double *table_cost,
+                             int32_t table_n, double max_verify,
+                             int32_t *depth_out, hipStream_t stream);
+
 /* Acceptance statistics across calls: adds one verification call's outcome
  * into counters [2K + 4] of uint64 (device memory the caller zeroes once and
  * keeps).  A serving system has to watch acceptance length ([Remio],

@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_dcut_allocate.restype = ctypes.c_int
         L.oracle_accept_stats.argtypes = [vp, vp, i32, i32, vp]
         L.oracle_accept_stats.restype = ctypes.c_int
+        L.oracle_dcut_cost.argtypes = [vp, vp, i32, dbl]
+        L.oracle_dcut_cost.restype = dbl
+        L.oracle_dcut_allocate_cost.argtypes = [vp, vp, i32, i32, vp, vp, i32, dbl, vp]
+        L.oracle_dcut_allocate_cost.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -207,4 +211,33 @@ def accept_stats(num_accepted, K: int, depth=None, counters=None):
     if rc != 0:
         raise ValueError(f"accept_stats rejected its arguments (code {rc})")
     return counters
+
+
+# the latency table printed with the pages' cost-aware D-cut sketch (depth: relative cost)
+DEFAULT_COST_TABLE = ((1.0, 1.0), (2.0, 1.2), (4.0, 1.5), (8.0, 2.0), (16.0, 3.0))
+
+
+def _table(table):
+    t = np.ascontiguousarray([p[0] for p in table], np.float64)
+    c = np.ascontiguousarray([p[1] for p in table], np.float64)
+    return t, c
+
+
+def dcut_cost(d: float, table=DEFAULT_COST_TABLE) -> float:
+    t, c = _table(table)
+    return float(lib().oracle_dcut_cost(_ptr(t), _ptr(c), len(t), float(d)))
+
+
+def dcut_allocate_cost(conf, max_verify: float, max_depth=None, table=DEFAULT_COST_TABLE):
+    """Cost-aware D-cut: depth[B] (int32), 0 for requests not admitted."""
+    conf = _c(conf, np.float32)
+    B, K = conf.shape
+    max_depth = _c(max_depth, np.int32)
+    t, c = _table(table)
+    depth = np.empty(B, np.int32)
+    rc = lib().oracle_dcut_allocate_cost(_ptr(conf), _ptr(max_depth), B, K, _ptr(t), _ptr(c), len(t),
+                                         float(max_verify), _ptr(depth))
+    if rc != 0:
+        raise ValueError(f"dcut_allocate_cost rejected its arguments (code {rc})")
+    return depth
 

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -146,6 +146,27 @@ def test_reuse_entry_points_host_errors():
     assert reuse(draft=NULL) == 1
     assert reuse(us=NULL) == 1
     assert reuse(wsb=10) == 3
+
+
+def test_dcut_cost_host_errors():
+    f = L.dcut_allocate_cost
+    dbl = ctypes.c_double
+
+    def tab(*v):
+        return ctypes.cast((dbl * len(v))(*v), ctypes.c_void_p)
+    td, tc = tab(1.0, 2.0, 4.0), tab(1.0, 1.2, 1.5)
+    assert f(NULL, NULL, 4, 3, td, tc, 3, 10.0, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, td, tc, 3, 10.0, NULL, NULL) == 1
+    assert f(FAKE, NULL, 0, 3, td, tc, 3, 10.0, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, NULL, tc, 3, 10.0, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, td, tc, 0, 10.0, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, td, tc, 33, 10.0, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, td, tc, 3, -1.0, FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, td, tc, 3, float("nan"), FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, td, tc, 3, float("inf"), FAKE, NULL) == 1
+    assert f(FAKE, NULL, 4, 3, tab(1.0, 1.0, 4.0), tc, 3, 10.0, FAKE, NULL) == 1    # depths not increasing
+    assert f(FAKE, NULL, 4, 3, td, tab(1.0, 0.0, 1.5), 3, 10.0, FAKE, NULL) == 1    # a cost not > 0
+    assert f(FAKE, NULL, 5000, 3, td, tc, 3, 10.0, FAKE, NULL) == 2
 
 
 def test_accept_stats_host_errors():

@@ -70,3 +70,41 @@ def test_dcut_config_sizes():
     assert np.array_equal(run(conf, 384), oracle.dcut_allocate(conf, 384))
     kb = np.where(g.random(64) < 0.5, 3, 16).astype(np.int32)
     assert np.array_equal(run(conf, 512, kb), oracle.dcut_allocate(conf, 512, kb))
+
+
+# ------------------------------------------------------- cost-aware D-cut ----
+
+def _rand_table(g, n):
+    t = np.cumsum(g.uniform(0.5, 4.0, n))
+    c = np.cumsum(g.uniform(0.05, 1.0, n))
+    return tuple(zip(t.tolist(), c.tolist()))
+
+
+@pytest.mark.parametrize("B,K", [(1, 1), (5, 3), (64, 16), (300, 64), (4096, 16)])
+def test_dcut_cost_random_bit_exact(B, K):
+    print(f"\n[case] dcut_allocate_cost random B={B} K={K}", flush=True)
+    import draft_verification_verify_amd as sv
+    g = np.random.default_rng(B * 7 + K)
+    for trial in range(3):
+        conf = g.uniform(0.0, 1.0, (B, K)).astype(np.float32)
+        conf[g.random((B, K)) < 0.05] = np.float32("nan")
+        conf[g.random((B, K)) < 0.03] = 1.5
+        conf[g.random((B, K)) < 0.03] = 1.0
+        md = g.integers(-1, K + 2, B).astype(np.int32) if trial != 1 else None
+        table = oracle.DEFAULT_COST_TABLE if trial == 0 else _rand_table(g, int(g.integers(1, 33)))
+        budget = float(g.uniform(0.0, 3.0 * B))
+        want = oracle.dcut_allocate_cost(conf, budget, md, table)
+        got = host(sv.dcut_allocate_cost(dev(conf), budget, dev(md), table))
+        assert np.array_equal(got, want), (trial, np.nonzero(got != want)[0][:10])
+
+
+def test_dcut_cost_ties_and_budget_edges():
+    print("\n[case] dcut_allocate_cost ties (equal benefits) and budget edges", flush=True)
+    import draft_verification_verify_amd as sv
+    conf = np.ones((64, 16), np.float32)
+    for budget in (0.0, 2.999, 3.0, 96.0, 191.9, 192.0, 1e9):
+        want = oracle.dcut_allocate_cost(conf, budget)
+        got = host(sv.dcut_allocate_cost(dev(conf), budget))
+        assert np.array_equal(got, want), budget
+    # equal benefits go in request order
+    assert host(sv.dcut_allocate_cost(dev(conf), 9.0)).tolist()[:4] == [16, 16, 16, 0]

@@ -586,3 +586,51 @@ def test_accept_stats_invariants_and_accumulation():
     c3 = oracle.accept_stats(np.array([5], np.int32), 3, np.array([9], np.int32))
     assert c3[:3].tolist() == [1, 1, 1] and c3[3:6].tolist() == [1, 1, 1]
     assert np.array_equal(oracle.accept_stats(n, K), oracle.accept_stats(n, K, np.full(B, K, np.int32)))
+
+
+# ------------------------------------------------------- cost-aware D-cut ----
+
+def test_dcut_cost_interpolation_hand_values():
+    # the pages' latency table: 1 -> 1.0, 2 -> 1.2, 4 -> 1.5, 8 -> 2.0, 16 -> 3.0
+    want = {0.5: 1.0, 1: 1.0, 2: 1.2, 3: 1.35, 4: 1.5, 5: 1.625, 6: 1.75, 8: 2.0, 12: 2.5, 16: 3.0, 40: 3.0}
+    for d, c in want.items():
+        assert abs(oracle.dcut_cost(d) - c) < 1e-15, (d, oracle.dcut_cost(d), c)
+
+
+def test_dcut_cost_choices_closed_forms():
+    # confidence 1 everywhere: benefit d / cost(d) grows with d on this table, so the
+    # whole window is chosen (16 / 3.0 at K_b = 16; 5 / 1.625 beats 4 / 1.5 at K_b = 5)
+    conf = np.ones((2, 16), np.float32)
+    assert oracle.dcut_allocate_cost(conf, 100.0, np.array([16, 5], np.int32)).tolist() == [16, 5]
+    # a zero after the first position: every longer prefix has benefit 0, so depth 1
+    conf = np.zeros((1, 8), np.float32)
+    conf[0, 0] = 0.9
+    assert oracle.dcut_allocate_cost(conf, 100.0).tolist() == [1]
+    # NaN, negatives and values above 1 are read as 0, 0 and 1
+    conf = np.array([[np.nan, 1.0], [2.0, -1.0]], np.float32)
+    assert oracle.dcut_allocate_cost(conf, 100.0).tolist() == [1, 1]
+    # invalid windows and empty ones
+    conf = np.ones((3, 4), np.float32)
+    assert oracle.dcut_allocate_cost(conf, 100.0, np.array([0, 5, -1], np.int32)).tolist() == [0, -1, -1]
+
+
+def test_dcut_cost_budget_fill_order_and_skip():
+    # equal benefits: admitted in request order until the budget runs out (cost 3.0 each)
+    conf = np.ones((4, 16), np.float32)
+    assert oracle.dcut_allocate_cost(conf, 9.0).tolist() == [16, 16, 16, 0]
+    assert oracle.dcut_allocate_cost(conf, 8.999).tolist() == [16, 16, 0, 0]
+    # a candidate that does not fit is skipped and a later, cheaper one still fits:
+    # request 0 wants depth 16 (benefit 5.33, cost 3.0); request 1 stops at depth 1
+    # (benefit 0.5, cost 1.0); with 2.5 of budget only request 1 is admitted
+    conf = np.ones((2, 16), np.float32)
+    conf[1, :] = 0.0
+    conf[1, 0] = 0.5
+    assert oracle.dcut_allocate_cost(conf, 2.5).tolist() == [0, 1]
+    assert oracle.dcut_allocate_cost(conf, 4.0).tolist() == [16, 1]
+    # invariant on random inputs: admitted cost within budget, and every candidate left
+    # out met a budget too small for it
+    g = np.random.default_rng(11)
+    conf = g.uniform(0.3, 1.0, (40, 16)).astype(np.float32)
+    dep = oracle.dcut_allocate_cost(conf, 30.0)
+    costs = [oracle.dcut_cost(d) for d in dep if d > 0]
+    assert sum(costs) <= 30.0 and min(dep) >= 0
