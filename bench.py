@@ -51,8 +51,8 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "2ea128b7ad5ea1217e1c0fb25d65bbc03a0b5f0fe03cf6225c262a9f10ccb6f9",
-                    "fetch_bytes": 526035522, "write_bytes": 536013}
+ROW_PASS_TRAFFIC = {"source_sha256": "8fd116845f1c92b251797a1baef9a184beb379c2d9a4b15d9f6e6952786a698b",
+                    "fetch_bytes": 526053157, "write_bytes": 536941}
 
 
 def parse():
@@ -353,7 +353,7 @@ def main():
         sec["dcut_allocate_cost_B64_K16"] = {
             "ms": float(np.mean(cper2)), "admitted": int((cdep > 0).sum().item()),
             "verify_slots": int(cdep.sum().item()),
-            "note": "max_verify 96 in the table's cost units (1.0 at depth 1 ... 3.0 at depth 16); one workgroup"}
+            "note": "max_verify 96 in the table's cost units (1.0 at depth 1 ... 3.0 at depth 16); one workgroup; on these high-entropy drafts every request's best benefit/cost depth is 1"}
         del copies
         # mixed fp32 batch: per-request K_b and T_b, dcut_allocate(512), one sampled launch
         wm = synth.mixed(args.seed)
