@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_verify_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
                                            i32, i32, i64, vp, vp, vp, vp, vp]
         L.oracle_verify_sample.restype = ctypes.c_int
+        L.oracle_verify_early_exit.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
+                                               i32, i32, i64, vp, vp, vp, vp]
+        L.oracle_verify_early_exit.restype = ctypes.c_int
         L.oracle_draft_confidence.argtypes = [vp, ctypes.c_int, vp, i32, i32, i64, vp]
         L.oracle_draft_confidence.restype = ctypes.c_int
         L.oracle_dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp]
@@ -175,6 +178,36 @@ def verify_sample(target, draft, tokens, temperature, u_accept, u_sample, depth=
                                _ptr(temperature), _ptr(u_accept), _ptr(u_sample), B, K, V,
                                _ptr(out), _ptr(n), _ptr(p), _ptr(q), _ptr(ratio))
     return {"out": out, "n": n, "p_draft": p, "q_draft": q, "ratio": ratio}
+
+
+def verify_early_exit(target, tokens, draft=None, temperature=None, u_accept=None, u_sample=None,
+                      depth=None):
+    """Sequential (early-exit) verification: positions in order, stop at the
+    first rejection, nothing after it read.  temperature None means every
+    request uses the greedy rule (draft and uniforms may then be None).
+    Returns dict with out, n, p_draft, q_draft (float32 [B,K])."""
+    target = _c(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    tokens = _c(tokens, np.int32).reshape(B, K)
+    if temperature is not None:
+        draft = _c(draft)
+        if draft.dtype != target.dtype or draft.shape != (B, K, V):
+            raise ValueError("draft must match target dtype and have shape [B,K,V]")
+        temperature = _c(temperature, np.float32).reshape(B)
+        u_accept = _c(u_accept, np.float32).reshape(B, K)
+        u_sample = _c(u_sample, np.float32).reshape(B)
+    else:
+        draft = u_accept = u_sample = None
+    depth = _c(depth, np.int32)
+    out = np.empty((B, K + 1), np.int32)
+    n = np.empty(B, np.int32)
+    p = np.empty((B, K), np.float32)
+    q = np.empty((B, K), np.float32)
+    lib().oracle_verify_early_exit(_ptr(target), _ptr(draft), _dt(target), _ptr(tokens), _ptr(depth),
+                                   _ptr(temperature), _ptr(u_accept), _ptr(u_sample), B, K, V,
+                                   _ptr(out), _ptr(n), _ptr(p), _ptr(q))
+    return {"out": out, "n": n, "p_draft": p, "q_draft": q}
 
 
 def draft_confidence(draft, max_depth=None):

@@ -357,6 +357,108 @@ int oracle_verify_sample(const void *target, const void *draft, int dtype,
     return 0;
 }
 
+/* Early-exit verification of a batch: the same accept rules (the greedy
+ * rule at T = 0, rejection sampling at T > 0), but positions are examined in
+ * order and the first rejection ends the request.  The accepted length
+ * counts the drafted tokens approved before the first discrepancy ([Remio],
+ * section "Come AngelSpec rende DFly più selettivo"), so nothing after that
+ * position can change the committed prefix or the emitted token; this
+ * reading reads nothing after it.
+ *
+ * For request b with depth d and temperature T (temperature NULL: all 0):
+ *   position k = 0, 1, ... < d reads tokens[b,k], target row k and, at
+ *   T > 0, u_accept[b,k] and draft row k.  Bad data at position k (a token
+ *   outside [0,V), a uniform outside [0,1), NaN, +inf or all -inf in a row
+ *   read there) makes the request bad; a rejection at k ends the scan with
+ *   n = k.  If no position rejects, n = d and the bonus row d is read.
+ *   The emitted token is chosen as in oracle_verify_greedy (argmax of target
+ *   row n) or oracle_verify_sample (inverse CDF of the residual or bonus
+ *   distribution at u_sample[b], which is read only then).
+ * Bad data after the stopping position is never read and so never reported.
+ * On inputs with no bad data the outputs equal oracle_verify_sample's
+ * out_tokens and num_accepted.
+ *
+ * p_draft / q_draft [B,K] (may be NULL) receive (float)a and (float)c for
+ * the positions read, k <= min(n, d-1), of sampled requests; 0 elsewhere and
+ * everywhere for bad or greedy requests. */
+int oracle_verify_early_exit(const void *target, const void *draft, int dtype,
+                             const int32_t *tokens, const int32_t *depth,
+                             const float *temperature, const float *u_accept,
+                             const float *u_sample, int32_t B, int32_t K, int64_t V,
+                             int32_t *out_tokens, int32_t *num_accepted,
+                             float *p_draft, float *q_draft)
+{
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t *out_row = out_tokens + b * (K + 1);
+        const int32_t *tok = tokens + b * K;
+        int32_t d = depth ? depth[b] : K;
+        float Tf = temperature ? temperature[b] : 0.0f;
+        double T = (double)Tf;
+        for (int32_t k = 0; k < K; ++k) {
+            if (p_draft) p_draft[b * K + k] = 0.0f;
+            if (q_draft) q_draft[b * K + k] = 0.0f;
+        }
+        int bad = d < 0 || d > K || bad_temperature(Tf);
+        int32_t n = d;
+        int64_t emit = -1;
+        if (!bad && T == 0.0) {
+            for (int32_t k = 0; k < d; ++k) {
+                const void *zr = row_ptr(target, dtype, b * (K + 1) + k, V);
+                if (tok[k] < 0 || (int64_t)tok[k] >= V || row_check(zr, dtype, V) != ROW_OK) { bad = 1; break; }
+                int64_t g = oracle_argmax(zr, dtype, V);
+                if ((int64_t)tok[k] != g) { n = k; emit = g; break; }
+            }
+            if (!bad && n == d) {
+                const void *zr = row_ptr(target, dtype, b * (K + 1) + d, V);
+                if (row_check(zr, dtype, V) != ROW_OK) bad = 1;
+                else emit = oracle_argmax(zr, dtype, V);
+            }
+        } else if (!bad) {
+            for (int32_t k = 0; k < d; ++k) {
+                const int32_t x = tok[k];
+                if (x < 0 || (int64_t)x >= V || bad_uniform(u_accept[b * K + k])) { bad = 1; break; }
+                int rc1, rc2;
+                double a = prob_of(row_ptr(target, dtype, b * (K + 1) + k, V), dtype, V, T, x, &rc1);
+                double c = prob_of(row_ptr(draft, dtype, b * K + k, V), dtype, V, T, x, &rc2);
+                if (rc1 != ROW_OK || rc2 != ROW_OK) { bad = 1; break; }
+                double ratio;
+                if (c > 0.0) ratio = (a / c < 1.0) ? a / c : 1.0;
+                else ratio = (a > 0.0) ? 1.0 : 0.0;
+                if (p_draft) p_draft[b * K + k] = (float)a;
+                if (q_draft) q_draft[b * K + k] = (float)c;
+                if (!((double)u_accept[b * K + k] < ratio)) { n = k; break; }
+            }
+            if (!bad && bad_uniform(u_sample[b])) bad = 1;
+            if (!bad) {
+                int rc;
+                if (n < d)
+                    rc = oracle_residual(row_ptr(target, dtype, b * (K + 1) + n, V),
+                                         row_ptr(draft, dtype, b * K + n, V), dtype, V, T, r);
+                else
+                    rc = oracle_residual(row_ptr(target, dtype, b * (K + 1) + d, V),
+                                         NULL, dtype, V, T, r);
+                if (rc == ROW_HAS_NAN || rc == ROW_ALL_NEG_INF) bad = 1;
+                else emit = oracle_inverse_cdf(r, V, (double)u_sample[b]);
+            }
+        }
+        if (bad) {
+            mark_bad(out_row, K, num_accepted + b);
+            for (int32_t k = 0; k < K; ++k) {
+                if (p_draft) p_draft[b * K + k] = 0.0f;
+                if (q_draft) q_draft[b * K + k] = 0.0f;
+            }
+            continue;
+        }
+        for (int32_t k = 0; k <= K; ++k) out_row[k] = -1;
+        for (int32_t k = 0; k < n; ++k) out_row[k] = tok[k];
+        out_row[n] = (int32_t)emit;
+        num_accepted[b] = n;
+    }
+    free(r);
+    return 0;
+}
+
 /* Draft confidence: the largest softmax probability of each draft row at
  * T = 1, which equals 1/S with S = sum_v exp(y_v - M).  Rows k >= K_b
  * (max_depth[b], NULL => K) are not read and get 0; a bad row gets NaN.

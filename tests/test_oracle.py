@@ -439,6 +439,111 @@ def test_zero_temperature_request_uses_greedy_rule():
 
 
 # --------------------------------------------------------------------------
+# early-exit verification: positions in order, nothing read after the stop
+# --------------------------------------------------------------------------
+
+def _poison_after_stop(w, depth, n):
+    """NaN rows, out-of-range tokens and invalid uniforms at every position
+    after each request's stopping position (what an early-exit reading never
+    reads)."""
+    t, tok = w.target.copy(), w.tokens.copy()
+    d_ = None if w.draft is None else w.draft.copy()
+    ua = None if w.u_accept is None else w.u_accept.copy()
+    nan = synth.to_bf16_bits(np.array([np.nan], np.float32))[0] if t.dtype == np.uint16 else np.nan
+    for b in range(w.B):
+        nb, db = int(n[b]), int(depth[b])
+        if 0 <= nb < db:
+            t[b, nb + 1:, :] = nan
+            tok[b, nb + 1:] = -3
+            if d_ is not None:
+                d_[b, nb + 1:, :] = nan
+                ua[b, nb + 1:] = 2.0
+    return t, d_, tok, ua
+
+
+def test_early_exit_greedy_invariants_and_nothing_read_after_stop():
+    for seed in range(3):
+        w = synth.random_case(seed, B=7, K=5, V=300, dtype="f32", temps=(0.0,), sigma=0.4)
+        depth = np.random.default_rng(seed).integers(0, w.K + 1, w.B).astype(np.int32)
+        res = oracle.verify_early_exit(w.target, w.tokens, depth=depth)
+        _greedy_invariants(w.target, w.tokens, depth, res["out"], res["n"])
+        stopped = (res["n"] < depth)
+        assert stopped.any()
+        t2, _, tok2, _ = _poison_after_stop(w, depth, res["n"])
+        res2 = oracle.verify_early_exit(t2, tok2, depth=depth)
+        assert np.array_equal(res2["out"], res["out"]) and np.array_equal(res2["n"], res["n"])
+        # the one-pass rule reads the whole window, so the same data is bad there
+        _, n1 = oracle.verify_greedy(t2, tok2, depth)
+        assert np.all(n1[stopped] == -1) and np.array_equal(n1[~stopped], res["n"][~stopped])
+
+
+def test_early_exit_greedy_bad_data_before_stop_and_bonus_row():
+    g = np.random.default_rng(5)
+    B, K, V = 4, 4, 30
+    target = g.standard_normal((B, K + 1, V)).astype(np.float32)
+    am = np.argmax(target, axis=2).astype(np.int32)
+    tokens = am[:, :K].copy()
+    tokens[:, 2] = (am[:, 2] + 1) % V          # every request rejects at position 2
+    target[0, 1, 3] = np.nan                    # before the stop: bad
+    target[1, 2, :] = -np.inf                   # at the stop: bad
+    tokens[2, 3] = V + 7                        # after the stop: never read
+    tokens[3, 2] = am[3, 2]                     # request 3 accepts everything ...
+    target[3, K, 0] = np.inf                    # ... and its bonus row is bad
+    res = oracle.verify_early_exit(target, tokens)
+    assert res["n"].tolist() == [-1, -1, 2, -1]
+    assert res["out"][2].tolist() == [am[2, 0], am[2, 1], am[2, 2], -1, -1]
+    assert np.all(res["out"][[0, 1, 3]] == -1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_early_exit_sampled_equals_one_pass_on_clean_data(dtype):
+    for seed in range(3):
+        w = synth.random_case(seed, B=9, K=6, V=64, dtype=dtype, temps=(0.0, 0.7, 1.0), sigma=0.8)
+        depth = np.random.default_rng(10 + seed).integers(0, w.K + 1, w.B).astype(np.int32)
+        ee = oracle.verify_early_exit(w.target, w.tokens, w.draft, w.temperature, w.u_accept,
+                                      w.u_sample, depth)
+        full = oracle.verify_sample(w.target, w.draft, w.tokens, w.temperature, w.u_accept,
+                                    w.u_sample, depth)
+        assert np.array_equal(ee["out"], full["out"]) and np.array_equal(ee["n"], full["n"])
+        for b in range(w.B):
+            m = min(int(ee["n"][b]), int(depth[b]) - 1)   # last position read
+            for key in ("p_draft", "q_draft"):
+                assert np.array_equal(ee[key][b, :m + 1], full[key][b, :m + 1])
+                assert np.all(ee[key][b, m + 1:] == 0)
+        t2, d2, tok2, ua2 = _poison_after_stop(w, depth, ee["n"])
+        ee2 = oracle.verify_early_exit(t2, tok2, d2, w.temperature, ua2, w.u_sample, depth)
+        for key in ("out", "n", "p_draft", "q_draft"):
+            assert np.array_equal(ee2[key], ee[key])
+
+
+def test_early_exit_sampled_hand_case():
+    # target uniform over 4 tokens, draft uniform over tokens {0, 3}: the
+    # ratio at x = 0 is (1/4)/(1/2) = 1/2 at every position.  u = 0.1 accepts,
+    # 0.9 rejects; position 2 comes after the stop and is not read, so its
+    # invalid uniform and NaN rows do not matter and its p/q stay 0.
+    z = _inf([[0, 0, 0, 0]] * 4)
+    y = _inf([[0, -1e30, -1e30, 0]] * 3)
+    z[2, 1] = np.nan
+    y[2, 2] = np.nan
+    res = oracle.verify_early_exit(z[None], np.zeros((1, 3), np.int32), y[None], f32([1.0]),
+                                   f32([[0.1, 0.9, 7.0]]), f32([0.0]))
+    assert int(res["n"][0]) == 1
+    # residual at position 1: max(0, 1/4 - q) is 1/4 on tokens 1 and 2; u = 0 takes token 1
+    assert res["out"][0].tolist() == [0, 1, -1, -1]
+    assert res["p_draft"][0].tolist() == [0.25, 0.25, 0.0]
+    assert res["q_draft"][0].tolist() == [0.5, 0.5, 0.0]
+    # the one-pass rule reads position 2 and reports the request as bad
+    full = oracle.verify_sample(z[None], y[None], np.zeros((1, 3), np.int32), f32([1.0]),
+                                f32([[0.1, 0.9, 7.0]]), f32([0.0]))
+    assert int(full["n"][0]) == -1
+    # a bad uniform before the stop, and a bad draw uniform, are bad data
+    assert int(oracle.verify_early_exit(z[None], np.zeros((1, 3), np.int32), y[None], f32([1.0]),
+                                        f32([[1.0, 0.9, 0.1]]), f32([0.0]))["n"][0]) == -1
+    assert int(oracle.verify_early_exit(z[None], np.zeros((1, 3), np.int32), y[None], f32([1.0]),
+                                        f32([[0.1, 0.9, 0.1]]), f32([1.0]))["n"][0]) == -1
+
+
+# --------------------------------------------------------------------------
 # draft confidence
 # --------------------------------------------------------------------------
 
