@@ -536,6 +536,10 @@ def test_early_exit_sampled_hand_case():
     full = oracle.verify_sample(z[None], y[None], np.zeros((1, 3), np.int32), f32([1.0]),
                                 f32([[0.1, 0.9, 7.0]]), f32([0.0]))
     assert int(full["n"][0]) == -1
+    # the accept test is strict: u equal to the ratio rejects
+    tie = oracle.verify_early_exit(z[None], np.zeros((1, 3), np.int32), y[None], f32([1.0]),
+                                   f32([[0.5, 0.1, 0.1]]), f32([0.0]))
+    assert int(tie["n"][0]) == 0
     # a bad uniform before the stop, and a bad draw uniform, are bad data
     assert int(oracle.verify_early_exit(z[None], np.zeros((1, 3), np.int32), y[None], f32([1.0]),
                                         f32([[1.0, 0.9, 0.1]]), f32([0.0]))["n"][0]) == -1

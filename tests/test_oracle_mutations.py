@@ -16,8 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 MUTATIONS = {
-    "accept_with_less_equal": ("!((double)u_accept[b * K + k] < ratio)",
-                               "!((double)u_accept[b * K + k] <= ratio)"),
+    "accept_with_less_equal": ("if (n == d && !((double)u_accept[b * K + k] < ratio))",
+                               "if (n == d && !((double)u_accept[b * K + k] <= ratio))"),
     "residual_sign_flipped": ("double d = p[v] - q[v];", "double d = q[v] - p[v];"),
     "bonus_from_row_K": ("row_ptr(target, dtype, b * (K + 1) + d, V),\n                                     NULL",
                          "row_ptr(target, dtype, b * (K + 1) + K, V),\n                                     NULL"),
@@ -33,6 +33,16 @@ MUTATIONS = {
     "greedy_bonus_from_row_n_plus_1": ("b * (K + 1) + n, V), dtype, V);\n    for (int32_t k = 0; k <= K; ++k) out_row[k] = -1;",
                                        "b * (K + 1) + (n < d ? n + 1 : n), V), dtype, V);\n    for (int32_t k = 0; k <= K; ++k) out_row[k] = -1;"),
     "confidence_not_inverse": ("(float)(1.0 / S)", "(float)(S)"),
+    # early-exit verification
+    "ee_accept_with_less_equal": ("if (!((double)u_accept[b * K + k] < ratio)) { n = k; break; }",
+                                  "if (!((double)u_accept[b * K + k] <= ratio)) { n = k; break; }"),
+    "ee_sampled_reads_past_stop": ("if (!((double)u_accept[b * K + k] < ratio)) { n = k; break; }",
+                                   "if (!((double)u_accept[b * K + k] < ratio) && n == d) n = k;"),
+    "ee_greedy_reads_past_stop": ("if ((int64_t)tok[k] != g) { n = k; emit = g; break; }",
+                                  "if ((int64_t)tok[k] != g && n == d) { n = k; emit = g; }"),
+    "ee_greedy_bonus_row_unchecked": ("if (row_check(zr, dtype, V) != ROW_OK) bad = 1;\n                else emit",
+                                      "if (0) bad = 1;\n                else emit"),
+    "ee_draw_uniform_unchecked": ("if (!bad && bad_uniform(u_sample[b])) bad = 1;", "if (0) bad = 1;"),
 }
 
 
