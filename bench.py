@@ -354,6 +354,28 @@ def main():
             "ms": float(np.mean(cper2)), "admitted": int((cdep > 0).sum().item()),
             "verify_slots": int(cdep.sum().item()),
             "note": "max_verify 96 in the table's cost units (1.0 at depth 1 ... 3.0 at depth 16); one workgroup; on these high-entropy drafts every request's best benefit/cost depth is 1"}
+        # early-exit verification of the same dense batch: windows of W
+        # positions, no row read after a request's first rejection; the
+        # committed tokens are those of the one-pass step
+        step(0)
+        n_one = nacc.cpu().numpy().copy()
+        for W in (2, 4, 8):
+            def estep(i, W=W):
+                t, d = copies[i % ncopy]
+                sv.verify_sample_early_exit(t, d, tok, T, ua, us, window=W, out_tokens=out, num_accepted=nacc,
+                                            p_draft=pd, q_draft=qd, workspace=ws, stream=stream)
+            _, eper, _ = timed(estep, steps2, warm2)
+            ems = float(np.mean(eper))
+            en = nacc.cpu().numpy()
+            # positions whose target and draft rows the row passes stream
+            pos_read = [K if n >= K else min(K, (n // W + 1) * W) for n in en.tolist()]
+            sec[f"early_exit_window{W}_B64_K16"] = {
+                "rows_per_s": rows / (ems * 1e-3), "ms": ems, "vs_one_pass_ms": ms / ems,
+                "row_pass_rows_per_step": 2 * int(sum(pos_read)), "one_pass_row_pass_rows": 2 * B * K,
+                "windows": -(-K // W), "same_num_accepted_as_one_pass": bool(np.array_equal(en, n_one)),
+                "note": "rows_per_s counts the B*(K+1) rows the step decides, as the headline does; "
+                        "the row passes stream the positions up to the end of each request's stopping "
+                        "window"}
         del copies
         # mixed fp32 batch: per-request K_b and T_b, dcut_allocate(512), one sampled launch
         wm = synth.mixed(args.seed)

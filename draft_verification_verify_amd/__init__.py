@@ -57,6 +57,11 @@ def _load() -> ctypes.CDLL:
     L.spec_verify_sample.restype = ctypes.c_int
     L.spec_verify_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_greedy_early_exit.restype = ctypes.c_int
+    L.spec_verify_greedy_early_exit.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.spec_verify_sample_early_exit.restype = ctypes.c_int
+    L.spec_verify_sample_early_exit.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                vp, vp, vp, vp, vp, sz, vp]
     L.spec_draft_confidence.restype = ctypes.c_int
     L.spec_draft_confidence.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, sz, vp]
     L.spec_draft_confidence_stats.restype = ctypes.c_int
@@ -85,7 +90,7 @@ EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify
             "spec_verify_workspace_size", "spec_verify_timing_begin", "spec_verify_timing_end",
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
             "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
-            "dcut_allocate_cost")
+            "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit")
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
@@ -240,6 +245,62 @@ def verify_sample(target, draft, tokens, temperature, u_accept, u_sample, depth=
                                 _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft),
                                 _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_sample", st)
+    return out_tokens, num_accepted, p_draft, q_draft
+
+
+def verify_greedy_early_exit(target, tokens, depth=None, *, window: int = 8, out_tokens=None,
+                             num_accepted=None, workspace=None, stream=None):
+    """verify_greedy that reads no row after a request's first rejection
+    (windows of ``window`` positions)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check(target, "target")
+    _check(tokens, "tokens", torch.int32, (B, K))
+    _check(depth, "depth", torch.int32, (B,))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=target.device)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
+    ws, nbytes = _ws(target.device, B, K, V, workspace)
+    st = lib.spec_verify_greedy_early_exit(_ptr(target), _dtype_code(target), _ptr(tokens), _ptr(depth),
+                                           B, K, V, int(window), _ptr(out_tokens), _ptr(num_accepted),
+                                           _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_verify_greedy_early_exit", st)
+    return out_tokens, num_accepted
+
+
+def verify_sample_early_exit(target, draft, tokens, temperature, u_accept, u_sample, depth=None, *,
+                             window: int = 8, out_tokens=None, num_accepted=None, p_draft=None,
+                             q_draft=None, want_probs: bool = True, workspace=None, stream=None):
+    """verify_sample that reads no row after a request's first rejection
+    (windows of ``window`` positions).  Returns (out_tokens, num_accepted,
+    p_draft, q_draft)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check(target, "target")
+    _check(draft, "draft", target.dtype, (B, K, V))
+    _check(tokens, "tokens", torch.int32, (B, K))
+    _check(temperature, "temperature", torch.float32, (B,))
+    _check(u_accept, "u_accept", torch.float32, (B, K))
+    _check(u_sample, "u_sample", torch.float32, (B,))
+    _check(depth, "depth", torch.int32, (B,))
+    dev = target.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if want_probs and p_draft is None:
+        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if want_probs and q_draft is None:
+        q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    ws, nbytes = _ws(dev, B, K, V, workspace)
+    st = lib.spec_verify_sample_early_exit(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens),
+                                           _ptr(depth), _ptr(temperature), _ptr(u_accept), _ptr(u_sample),
+                                           B, K, V, int(window), _ptr(out_tokens), _ptr(num_accepted),
+                                           _ptr(p_draft), _ptr(q_draft), _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_verify_sample_early_exit", st)
     return out_tokens, num_accepted, p_draft, q_draft
 
 

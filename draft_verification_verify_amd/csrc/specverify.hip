@@ -81,9 +81,12 @@ constexpr float ROW_SKEW_LSE = 0.3f;
 enum : int { MODE_GREEDY = 0, MODE_SAMPLE = 1, MODE_CONF = 2 };
 // KIND_SAMPLED_R: a sampled request at T = 1 whose draft-row statistics come
 // from a confidence pass (the row pass reads its target rows only).
-enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3, KIND_SAMPLED_R = 4 };
-// outcome of a request's accept scan
-enum : int { SREQ_BAD = 0, SREQ_GREEDY = 1, SREQ_RESID = 2, SREQ_BONUS = 3 };
+// KIND_DONE: early-exit calls, a request that ended in an earlier window.
+enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3, KIND_SAMPLED_R = 4, KIND_DONE = 5 };
+// outcome of a request's accept scan; SREQ_CONT (early-exit calls): every
+// position of the window accepted and the depth lies beyond it; SREQ_DONE:
+// nothing to do in this window
+enum : int { SREQ_BAD = 0, SREQ_GREEDY = 1, SREQ_RESID = 2, SREQ_BONUS = 3, SREQ_CONT = 4, SREQ_DONE = 5 };
 
 constexpr double LOG2E = 1.4426950408889634;
 constexpr double LN2 = 0.6931471805599453;
@@ -138,10 +141,11 @@ struct Ws {
                          // request b in slot row b * (2K + 1) + j, chunk c in column c
     ChunkPart *cp;       // [B * cs_max] sampler chunk sums
     DrawRec *rec;        // [B]
+    int32_t *alive;      // [2 * B] early-exit calls: request still verifying, per window parity
 };
 
 struct Layout {
-    size_t off[4];
+    size_t off[5];
     size_t total;
     int64_t r_max;
     int cpr_max;
@@ -164,14 +168,15 @@ bool make_layout(int B, int K, int V, Layout &L)
     L.cpr_max = (int)std::min<int64_t>(CPR_CAP, ceil_div(nv, WVEC));
     L.cs_max = (int)std::max(ceil_div(nv, (int64_t)UNIT_E / 4), ceil_div(nvec_max(V, 8), (int64_t)UNIT_E / 8));
     if (L.cs_max > UNITS_MAX) return false;
-    const size_t sz[4] = {
+    const size_t sz[5] = {
         sizeof(int32_t) * 4 + sizeof(Stat),
         sizeof(Stat) * (size_t)L.r_max * (size_t)L.cpr_max,
         sizeof(ChunkPart) * (size_t)B * (size_t)L.cs_max,
         sizeof(DrawRec) * (size_t)B,
+        sizeof(int32_t) * 2 * (size_t)B,
     };
     size_t o = 0;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 5; ++i) {
         L.off[i] = o;
         o += align256(sz[i]);
     }
@@ -187,6 +192,7 @@ Ws carve(void *base, const Layout &L, int B)
     w.part = (Stat *)(p + L.off[1]);
     w.cp = (ChunkPart *)(p + L.off[2]);
     w.rec = (DrawRec *)(p + L.off[3]);
+    w.alive = (int32_t *)(p + L.off[4]);
     (void)B;
     return w;
 }
@@ -215,6 +221,13 @@ struct Params {
     int32_t aligned;   // V * element size is a multiple of 16: every row starts 16-byte aligned
     int32_t row_cus;   // compute units the row-pass grid is spread over
     float row_skew;    // row pass: task-count slope across dispatch slots
+    // Early-exit calls: this launch verifies positions [win_lo, win_hi) of
+    // the requests still verifying (alive_in, read when win_lo > 0) and
+    // records in alive_out which of them continue into the next window.
+    int32_t ee;
+    int32_t win_lo, win_hi;
+    const int32_t *alive_in;
+    int32_t *alive_out;
     Ws ws;
 };
 
@@ -544,6 +557,12 @@ __device__ __forceinline__ double exp2_tab(double x, const double *tab) { return
 //   sampled request (T > 0): target rows 0..d-1, then draft rows 0..d-1
 //   confidence call: draft rows 0..K_b-1
 // A request whose depth or temperature is invalid contributes no rows.
+// Early-exit calls verify the positions [lo, hi) of a window, lo = win_lo
+// and hi = min(win_hi, d), of the requests still verifying: a greedy
+// request reads target rows lo..hi-1, plus its bonus row d when the window
+// reaches the depth (win_hi >= d); a sampled request reads target rows and
+// then draft rows lo..hi-1.  Row indices within the request are relative to
+// lo, and d below is then the window's position count hi - lo.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ bool temp_ok(float T)
@@ -554,12 +573,16 @@ __device__ __forceinline__ bool temp_ok(float T)
 struct ReqPlan {
     int d, kind, rows;
     float T;
+    int lo;      // first position of the window (0 outside early-exit calls)
+    bool fin;    // the window reaches the depth: the request ends in it
 };
 
 __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
 {
     ReqPlan q;
     q.T = 0.0f;
+    q.lo = 0;
+    q.fin = true;
     if (P.mode == MODE_CONF) {
         q.d = P.max_depth ? P.max_depth[b] : P.K;
         const bool ok = q.d >= 0 && q.d <= P.K;
@@ -572,8 +595,22 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
         q.kind = !ok ? KIND_BAD : (q.T > 0.0f ? KIND_SAMPLED : KIND_GREEDY);
         if (q.kind == KIND_SAMPLED && P.dstats_in && q.T == 1.0f) q.kind = KIND_SAMPLED_R;
         q.rows = !ok ? 0 : (q.kind == KIND_SAMPLED ? 2 * q.d : q.kind == KIND_SAMPLED_R ? q.d : q.d + 1);
+        if (P.ee) {
+            q.lo = P.win_lo;
+            if (q.lo > 0 && !P.alive_in[b]) {
+                q.kind = KIND_DONE;
+                q.rows = 0;
+            } else if (ok) {
+                // a request still verifying at lo > 0 accepted positions
+                // 0..lo-1 of a window that ended before its depth: lo < d
+                q.fin = P.win_hi >= q.d;
+                const int nd = min(P.win_hi, q.d) - q.lo;
+                q.rows = q.kind == KIND_SAMPLED ? 2 * nd : nd + (q.fin ? 1 : 0);
+                q.d = nd;
+            }
+        }
     }
-    if (q.kind == KIND_BAD) q.d = 0;
+    if (q.kind == KIND_BAD || q.kind == KIND_DONE) q.d = 0;
     return q;
 }
 
@@ -897,6 +934,7 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     else if (kind == KIND_SAMPLED) { is_draft = local >= d; kk = is_draft ? local - d : local; lse = true; }
     else if (kind == KIND_SAMPLED_R) { is_draft = false; kk = local; lse = true; }
     else { is_draft = true; kk = local; lse = true; }   // KIND_CONF
+    kk += P.win_lo;   // the window's first position (early-exit calls)
     k.c32 = lse ? c32_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b])))) : 0.0f;
     const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
     const char *row_start = (const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4);
@@ -1219,6 +1257,106 @@ __device__ void write_outputs(const Params &P, int b, int d, const ReqDesc &desc
     if (lane == 0) P.num_accepted[b] = bad ? -1 : n;
 }
 
+// Early-exit scan of one window (one wave, lanes over the window's
+// positions).  Positions are taken in order and the first one that is
+// rejected or holds bad data ends the request; nothing after it is looked
+// at, so bad data there is not reported.  rows: the window's rows as the
+// plan lays them out (position lo + j at j; sampled draft rows after the q.d
+// target rows; a greedy request's bonus row at q.d when the window reaches
+// the depth).  pq[j] receives (p, q) at the drafted token of position lo + j.
+// (x0, ua0): lane l's drafted token and accept uniform at position lo + l;
+// us0: the draw uniform.  Returned positions n are absolute.
+__device__ ReqDesc scan_window(const Params &P, int b, const ReqPlan &q, const Stat *rows, float2 *pq,
+                               const double *tab, int x0, float ua0, float us0)
+{
+    const int nd = q.d, lo = q.lo;
+    const int lane = lane_id();
+    const int64_t tb = (int64_t)b * P.K + lo;
+    ReqDesc desc = {SREQ_BAD, 0, -1, q.T};
+    if (q.kind == KIND_BAD) return desc;
+    if (q.kind == KIND_DONE) return {SREQ_DONE, 0, -1, q.T};
+    const bool greedy = q.kind == KIND_GREEDY;
+    const double c2 = greedy ? 0.0 : (double)c32_of(q.kind, q.T);
+    int stop = nd;          // first position (relative) that rejects or is bad
+    bool stop_bad = false;
+    for (int k0 = 0; k0 < nd; k0 += 64) {
+        const int k = k0 + lane;
+        bool badk = false, rej = false;
+        if (k < nd) {
+            const int x = k0 == 0 ? x0 : P.tokens[tb + k];
+            const bool xbad = x < 0 || x >= P.V;
+            const Stat st = rows[k];
+            if (greedy) {
+                badk = xbad || stat_bad(st, false);
+                rej = x != st.idx;
+            } else {
+                const float ua = k0 == 0 ? ua0 : P.u_accept[tb + k];
+                const Stat sd = rows[nd + k];
+                badk = xbad || !unif_ok(ua) || stat_bad(st, true) || stat_bad(sd, true);
+                double a = 0.0, c = 0.0;
+                if (!badk) {
+                    const float zx = __int_as_float(st.idx);
+                    const float yx = __int_as_float(sd.idx);
+                    a = exp2_tab(((double)zx - (double)st.m) * c2, tab) / st.s;
+                    c = exp2_tab(((double)yx - (double)sd.m) * c2, tab) / sd.s;
+                    const double ratio = (c > 0.0) ? fmin(1.0, a / c) : (a > 0.0 ? 1.0 : 0.0);
+                    rej = !((double)ua < ratio);
+                }
+                pq[k] = make_float2((float)a, (float)c);
+            }
+        }
+        const uint64_t ev = __ballot(k < nd && (badk || rej));
+        if (ev && stop == nd) {
+            const int f = __builtin_ctzll(ev);
+            stop = k0 + f;
+            stop_bad = (__ballot(badk) >> f) & 1;
+        }
+    }
+    if (stop_bad) return desc;
+    if (stop < nd) {
+        if (greedy) return {SREQ_GREEDY, lo + stop, rows[stop].idx, q.T};
+        if (!unif_ok(us0)) return desc;
+        return {SREQ_RESID, lo + stop, -1, q.T};
+    }
+    if (!q.fin) return {SREQ_CONT, lo + nd, -1, q.T};
+    if (greedy) {
+        const Stat s = rows[nd];
+        if (stat_bad(s, false)) return desc;
+        return {SREQ_GREEDY, lo + nd, s.idx, q.T};
+    }
+    if (!unif_ok(us0)) return desc;
+    return {SREQ_BONUS, lo + nd, -1, q.T};
+}
+
+// One wave writes what an early-exit window decides for request b.
+// (p, q) for the window's positions up to the stop (0 after it and for
+// greedy requests); when the request ends here, the outputs as the one-pass
+// call writes them, zero probabilities past the window (never read) and,
+// for a bad request, zero probabilities for the earlier windows too.
+__device__ void write_window(const Params &P, int b, const ReqPlan &q, const ReqDesc &desc, const float2 *pq,
+                             int token)
+{
+    const int K = P.K, lane = lane_id();
+    const int64_t ob = (int64_t)b * (K + 1), tb = (int64_t)b * K;
+    if (desc.state == SREQ_DONE) return;
+    const bool bad = desc.state == SREQ_BAD, cont = desc.state == SREQ_CONT;
+    const int n = desc.n, lo = q.lo, hi = q.lo + q.d;
+    if (P.mode == MODE_SAMPLE) {
+        const bool sampled = !bad && q.kind == KIND_SAMPLED;
+        for (int k = lane; k < K; k += 64) {
+            if (k < lo && !bad) continue;       // an earlier window's position
+            if (cont && k >= hi) continue;      // a later window's position
+            const float2 v = (sampled && k < hi && k <= n) ? pq[k - lo] : make_float2(0.0f, 0.0f);
+            if (P.p_draft) P.p_draft[tb + k] = v.x;
+            if (P.q_draft) P.q_draft[tb + k] = v.y;
+        }
+    }
+    if (cont) return;
+    for (int k = lane; k <= K; k += 64)
+        P.out_tokens[ob + k] = bad ? -1 : (k < n ? P.tokens[tb + k] : (k == n ? token : -1));
+    if (lane == 0) P.num_accepted[b] = bad ? -1 : n;
+}
+
 // ---------------------------------------------------------------------------
 // Finish kernel: merge, accept scan, sampler chunk sums.
 // ---------------------------------------------------------------------------
@@ -1506,13 +1644,17 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // the request's plan and the row pass's chunking are read before the
     // table is built, so their loads overlap its arithmetic
     const ReqPlan q = plan_request(P, b);
+    if (q.kind == KIND_DONE) {   // early-exit calls: ended in an earlier window
+        if (c == 0 && tid == 0) P.alive_out[b] = 0;
+        return;
+    }
     const int cpr = P.ws.meta[0];
-    // the scan's inputs for positions 0..63, loaded now so their latency
+    // the scan's inputs for positions lo..lo+63, loaded now so their latency
     // overlaps the table and the merge
     int x0 = 0;
     float ua0 = 0.0f, us0 = 0.0f;
     if (wave_id() == 0 && P.mode != MODE_CONF) {
-        const int l = lane_id();
+        const int l = q.lo + lane_id();
         if (l < P.K) x0 = P.tokens[(int64_t)b * P.K + l];
         if (P.mode == MODE_SAMPLE) {
             if (l < P.K) ua0 = P.u_accept[(int64_t)b * P.K + l];
@@ -1561,7 +1703,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
         return;
     }
     if (wave_id() == 0) {
-        const ReqDesc dsc = scan_request(P, b, q, rows_s, pq_s, tab, x0, ua0, us0);
+        const ReqDesc dsc = P.ee ? scan_window(P, b, q, rows_s, pq_s, tab, x0, ua0, us0)
+                                 : scan_request(P, b, q, rows_s, pq_s, tab, x0, ua0, us0);
         if (lane_id() == 0) sh_desc = dsc;
     }
     __syncthreads();
@@ -1569,11 +1712,18 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     const bool draw = desc.state == SREQ_RESID || desc.state == SREQ_BONUS;
     const bool resid = desc.state == SREQ_RESID;
     const int d = q.d;
-    const Stat sz_row = rows_s[draw ? desc.n : 0];
-    const Stat sy_row = resid ? rows_s[d + desc.n] : sz_row;
+    const int nl = desc.n - q.lo;   // the drawn position within the window's rows
+    const Stat sz_row = rows_s[draw ? nl : 0];
+    const Stat sy_row = resid ? rows_s[d + nl] : sz_row;
     const double rho_hat = resid ? sz_row.s / sy_row.s : 0.0;
     if (c == 0 && wave_id() == 0) {
-        write_outputs(P, b, d, desc, pq_s, desc.state == SREQ_GREEDY ? desc.emit : -1);
+        const int token = desc.state == SREQ_GREEDY ? desc.emit : -1;
+        if (P.ee) {
+            write_window(P, b, q, desc, pq_s, token);
+            if (lane_id() == 0) P.alive_out[b] = desc.state == SREQ_CONT;
+        } else {
+            write_outputs(P, b, d, desc, pq_s, token);
+        }
         if (P.mode == MODE_SAMPLE && lane_id() == 0) {
             DrawRec r;
             r.state = desc.state;
@@ -1586,13 +1736,34 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
             P.ws.rec[b] = r;
         }
     }
-    if (!draw) return;
+    // early-exit calls sum the drawn rows after the last window
+    if (!draw || P.ee) return;
     // this wave's unit of the drawn row pair (no workgroup barrier after here)
     const int unit = c * NWAVE + wave_id();
     if (unit >= P.cs) return;
     __builtin_amdgcn_s_setprio(0);
     const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, resid ? sz_row.m : 0.0f, resid ? sy_row.m : 0.0f);
     const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rho_hat, unit * unit_v<BF16>(), tab);
+    if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
+}
+
+// Early-exit calls: the sampler units of every request that draws, after the
+// last window, from the draw record the request's final window wrote (grid:
+// units / 4 by B, as the one-pass finish kernel's unit part).
+template <bool BF16, bool ALIGNED>
+__global__ __launch_bounds__(WG) void units_kernel(Params P)
+{
+    __shared__ double tab[EXP2_TAB];
+    const int b = blockIdx.y, c = blockIdx.x;
+    const DrawRec rec = P.ws.rec[b];
+    if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
+    init_exp2_table(tab);
+    const int unit = c * NWAVE + wave_id();
+    if (unit >= P.cs) return;
+    const bool resid = rec.state == SREQ_RESID;
+    const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
+    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
+    const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rec.rho_hat, unit * unit_v<BF16>(), tab);
     if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
 }
 
@@ -2282,15 +2453,16 @@ inline hipEvent_t stage_event(int call, int s) { return g_timing.ev[(size_t)4 * 
 sv_status launch(Params &P, hipStream_t stream)
 {
     const int64_t nv = nvec_max(P.V, P.bf16 ? 8 : 4);
-    const int64_t rows_max = (P.mode == MODE_SAMPLE) ? (int64_t)P.B * (2 * P.K + 1)
-                           : (P.mode == MODE_GREEDY) ? (int64_t)P.B * (P.K + 1) : (int64_t)P.B * P.K;
+    const int kw = P.ee ? P.win_hi - P.win_lo : P.K;   // positions one launch can verify
+    const int64_t rows_max = (P.mode == MODE_SAMPLE) ? (int64_t)P.B * (2 * kw + 1)
+                           : (P.mode == MODE_GREEDY) ? (int64_t)P.B * (kw + 1) : (int64_t)P.B * P.K;
     const size_t lds_a = sizeof(int) * (size_t)(3 * P.B + 1);
     int64_t grid = (int64_t)cu_count() * row_wgs_per_cu(P.bf16, lds_a);
     grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div(rows_max * ceil_div(nv, WVEC), NWAVE)));
     const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1) + sizeof(float2) * (size_t)P.K;
     const bool sample = P.mode == MODE_SAMPLE;
-    const dim3 grid_b((unsigned)(sample ? ceil_div(P.cs, NWAVE) : 1), (unsigned)P.B);
-    const int tcall = g_timing.used < g_timing.armed ? g_timing.used++ : -1;
+    const dim3 grid_b((unsigned)(sample && !P.ee ? ceil_div(P.cs, NWAVE) : 1), (unsigned)P.B);
+    const int tcall = (!P.ee && g_timing.used < g_timing.armed) ? g_timing.used++ : -1;
     (void)hipGetLastError();
 #define SV_MARK(s)                                                            \
     do {                                                                      \
@@ -2303,7 +2475,7 @@ sv_status launch(Params &P, hipStream_t stream)
         SV_MARK(1);                                                                                         \
         hipLaunchKernelGGL((finish_kernel<BF, AL>), grid_b, dim3(WG), lds_b, stream, P);                    \
         SV_MARK(2);                                                                                         \
-        if (sample) hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P); \
+        if (sample && !P.ee) hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P); \
         SV_MARK(3);                                                                                         \
     } while (0)
     if (P.bf16) {
@@ -2315,6 +2487,44 @@ sv_status launch(Params &P, hipStream_t stream)
     }
 #undef SV_LAUNCH_PATH
 #undef SV_MARK
+    return hip_status("kernel launch");
+}
+
+// Early-exit verification: per window of `window` positions a row pass and
+// a finish kernel (merge, scan, outputs, draw record), back to back on the
+// stream (the host never waits); for sampled calls, after the last window,
+// the sampler units and the draw of every request that draws, whichever
+// window it ended in.  Window w verifies positions [w * window, (w + 1) *
+// window) of the requests that accepted every earlier position; the last
+// window reaches K.  The still-verifying flags alternate between two arrays
+// so that a window never overwrites what its own kernels read.
+sv_status launch_windows(Params &P, int window, hipStream_t stream)
+{
+    const int nwin = P.K == 0 ? 1 : (int)ceil_div(P.K, window);
+    P.ee = 1;
+    for (int w = 0; w < nwin; ++w) {
+        P.win_lo = w * window;
+        P.win_hi = P.win_lo + window;
+        P.alive_in = P.ws.alive + (size_t)(w & 1) * (size_t)P.B;
+        P.alive_out = P.ws.alive + (size_t)((w + 1) & 1) * (size_t)P.B;
+        const sv_status st = launch(P, stream);
+        if (st != SV_OK) return st;
+    }
+    if (P.mode != MODE_SAMPLE) return SV_OK;
+    const dim3 grid_u((unsigned)ceil_div(P.cs, NWAVE), (unsigned)P.B);
+#define SV_DRAW_PATH(BF, AL)                                                                          \
+    do {                                                                                              \
+        hipLaunchKernelGGL((units_kernel<BF, AL>), grid_u, dim3(WG), 0, stream, P);                   \
+        hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P);       \
+    } while (0)
+    if (P.bf16) {
+        if (P.aligned) SV_DRAW_PATH(true, true);
+        else SV_DRAW_PATH(true, false);
+    } else {
+        if (P.aligned) SV_DRAW_PATH(false, true);
+        else SV_DRAW_PATH(false, false);
+    }
+#undef SV_DRAW_PATH
     return hip_status("kernel launch");
 }
 
@@ -2448,6 +2658,61 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     P.p_draft = p_draft;
     P.q_draft = q_draft;
     return launch(P, stream);
+}
+
+sv_status spec_verify_greedy_early_exit(const void *target_logits, sv_dtype dt, const int32_t *draft_tokens,
+                                        const int32_t *depth, int32_t B, int32_t K, int32_t V, int32_t window,
+                                        int32_t *out_tokens, int32_t *num_accepted, void *workspace,
+                                        size_t ws_bytes, hipStream_t stream)
+{
+    sv_status st = check_shape(B, K, V);
+    if (st != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (window < 1) return SV_ERR_INVALID_ARG;
+    if (!target_logits || !out_tokens || !num_accepted || (K > 0 && !draft_tokens)) return SV_ERR_INVALID_ARG;
+    if (!aligned16(target_logits)) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K, V, L);
+    if ((st = check_ws(workspace, ws_bytes, L)) != SV_OK) return st;
+    Params P = base_params(B, K, V, dt, MODE_GREEDY, L, workspace);
+    P.target = target_logits;
+    P.tokens = draft_tokens;
+    P.depth = depth;
+    P.out_tokens = out_tokens;
+    P.num_accepted = num_accepted;
+    return launch_windows(P, std::min(window, std::max(K, 1)), stream);
+}
+
+sv_status spec_verify_sample_early_exit(const void *target_logits, const void *draft_logits, sv_dtype dt,
+                                        const int32_t *draft_tokens, const int32_t *depth,
+                                        const float *temperature, const float *u_accept, const float *u_sample,
+                                        int32_t B, int32_t K, int32_t V, int32_t window, int32_t *out_tokens,
+                                        int32_t *num_accepted, float *p_draft, float *q_draft, void *workspace,
+                                        size_t ws_bytes, hipStream_t stream)
+{
+    sv_status st = check_shape(B, K, V);
+    if (st != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (window < 1) return SV_ERR_INVALID_ARG;
+    if (!target_logits || !temperature || !u_sample || !out_tokens || !num_accepted) return SV_ERR_INVALID_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+    if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits))) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K, V, L);
+    if ((st = check_ws(workspace, ws_bytes, L)) != SV_OK) return st;
+    Params P = base_params(B, K, V, dt, MODE_SAMPLE, L, workspace);
+    P.target = target_logits;
+    P.draft = draft_logits;
+    P.tokens = draft_tokens;
+    P.depth = depth;
+    P.temperature = temperature;
+    P.u_accept = u_accept;
+    P.u_sample = u_sample;
+    P.out_tokens = out_tokens;
+    P.num_accepted = num_accepted;
+    P.p_draft = p_draft;
+    P.q_draft = q_draft;
+    return launch_windows(P, std::min(window, std::max(K, 1)), stream);
 }
 
 sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_logits, sv_dtype dt,

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -107,6 +107,29 @@ def test_sample_host_errors():
     assert sample(dt=2) == 1
     assert sample(B=0) == 1
     assert sample(wsb=10) == 3
+
+
+def test_early_exit_host_errors():
+    wsb = sv.workspace_size(4, 3, 1000)
+
+    def g(target=FAKE, dt=1, tokens=FAKE, B=4, K=3, V=1000, window=2, out=FAKE, num=FAKE, ws=FAKE,
+          n=wsb):
+        return L.spec_verify_greedy_early_exit(target, dt, tokens, NULL, B, K, V, window, out, num, ws, n,
+                                               NULL)
+
+    def s(target=FAKE, draft=FAKE, T=FAKE, ua=FAKE, us=FAKE, window=2, B=4, ws=FAKE, n=wsb):
+        return L.spec_verify_sample_early_exit(target, draft, 1, FAKE, NULL, T, ua, us, B, 3, 1000, window,
+                                               FAKE, FAKE, NULL, NULL, ws, n, NULL)
+
+    assert g(window=0) == 1 and g(window=-3) == 1
+    assert g(target=NULL) == 1 and g(tokens=NULL) == 1 and g(out=NULL) == 1 and g(num=NULL) == 1
+    assert g(dt=5) == 1 and g(B=0) == 1 and g(K=-1) == 1 and g(V=0) == 1
+    assert g(B=5000) == 2 and g(target=FAKE_MIS) == 1
+    assert g(ws=NULL) == 3 and g(n=64) == 3
+    assert s(window=0) == 1
+    assert s(target=NULL) == 1 and s(draft=NULL) == 1 and s(T=NULL) == 1
+    assert s(ua=NULL) == 1 and s(us=NULL) == 1 and s(draft=FAKE_MIS) == 1
+    assert s(B=0) == 1 and s(n=10) == 3
 
 
 def test_confidence_and_dcut_host_errors():
