@@ -577,6 +577,7 @@ struct ReqPlan {
     bool fin;    // the window reaches the depth: the request ends in it
 };
 
+template <bool EE>
 __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
 {
     ReqPlan q;
@@ -595,7 +596,7 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
         q.kind = !ok ? KIND_BAD : (q.T > 0.0f ? KIND_SAMPLED : KIND_GREEDY);
         if (q.kind == KIND_SAMPLED && P.dstats_in && q.T == 1.0f) q.kind = KIND_SAMPLED_R;
         q.rows = !ok ? 0 : (q.kind == KIND_SAMPLED ? 2 * q.d : q.kind == KIND_SAMPLED_R ? q.d : q.d + 1);
-        if (P.ee) {
+        if constexpr (EE) {
             q.lo = P.win_lo;
             if (q.lo > 0 && !P.alive_in[b]) {
                 q.kind = KIND_DONE;
@@ -621,6 +622,7 @@ struct Plan {
 };
 
 // Whole-workgroup plan: row_off = exclusive prefix of per-request rows.
+template <bool EE>
 __device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
 {
     const int B = P.B;
@@ -630,7 +632,7 @@ __device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
     for (int j = 0; j < per; ++j) {
         const int b = b0 + j;
         if (b >= B) break;
-        const ReqPlan q = plan_request(P, b);
+        const ReqPlan q = plan_request<EE>(P, b);
         pl.info[b] = q.d | (q.kind << 16);
         pl.T[b] = q.T;
         pl.row_off[b] = q.rows;   // count for now
@@ -916,7 +918,7 @@ __device__ __forceinline__ float ld_scalar_logit(const void *row, int x)
 
 // Task (r, c): chunk c of global active row r.  Everything here is
 // wave-uniform.
-template <bool BF16>
+template <bool BF16, bool EE>
 __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl, int r, int c, int nb)
 {
     Task<BF16> k;
@@ -934,7 +936,7 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     else if (kind == KIND_SAMPLED) { is_draft = local >= d; kk = is_draft ? local - d : local; lse = true; }
     else if (kind == KIND_SAMPLED_R) { is_draft = false; kk = local; lse = true; }
     else { is_draft = true; kk = local; lse = true; }   // KIND_CONF
-    kk += P.win_lo;   // the window's first position (early-exit calls)
+    if constexpr (EE) kk += P.win_lo;   // the window's first position
     k.c32 = lse ? c32_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b])))) : 0.0f;
     const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
     const char *row_start = (const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4);
@@ -1017,7 +1019,7 @@ __device__ __forceinline__ void consume(const Params &P, const Task<BF16> &k, in
 
 // Four waves per SIMD (128 VGPRs) keep enough 16-byte loads in flight per CU
 // to cover HBM latency; the register budget fits without spills.
-template <bool BF16>
+template <bool BF16, bool EE>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void row_pass_kernel(Params P)
 {
     extern __shared__ int plan_smem[];
@@ -1026,7 +1028,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     pl.row_off = plan_smem;
     pl.info = plan_smem + P.B + 1;
     pl.T = (float *)(plan_smem + 2 * P.B + 1);
-    make_plan(P, pl, scan_tmp);
+    make_plan<EE>(P, pl, scan_tmp);
 
     const int R = __builtin_amdgcn_readfirstlane(pl.row_off[P.B]);
     const uint32_t nwaves = gridDim.x * NWAVE;
@@ -1104,7 +1106,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         if (t >= ntask) return false;
         const int r = __builtin_amdgcn_readfirstlane((int)(t / (uint32_t)cpr));
         const int c = (int)t - r * cpr;
-        kn = make_task<BF16>(P, pl, r, c, nb);
+        kn = make_task<BF16, EE>(P, pl, r, c, nb);
         kn.k = k1;
         kn.pre = pre1;
         in = c * nb;
@@ -1124,7 +1126,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     zero.idx = 0;
     zero.s = 0.0;
     uint4 A[UW], Bv[UW];
-    Task<BF16> kA = make_task<BF16>(P, pl, r0, c0, nb);
+    Task<BF16> kA = make_task<BF16, EE>(P, pl, r0, c0, nb);
     kA.k = 0;
     kA.pre = 0;
     Task<BF16> kB = kA;
@@ -1629,7 +1631,7 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
 //     draw kernel) and the record the draw kernel reads;
 //  3. for a request that draws a token (sampled calls), each wave sums one
 //     unit of the drawn row pair in fp64 (unit 4c + wave).
-template <bool BF16, bool ALIGNED>
+template <bool BF16, bool ALIGNED, bool EE>
 __global__ __launch_bounds__(WG) void finish_kernel(Params P)
 {
     extern __shared__ Stat rows_s[];   // [2K + 1] merged row statistics, then [K] (p, q) pairs
@@ -1643,7 +1645,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     __builtin_amdgcn_s_setprio(3);
     // the request's plan and the row pass's chunking are read before the
     // table is built, so their loads overlap its arithmetic
-    const ReqPlan q = plan_request(P, b);
+    const ReqPlan q = plan_request<EE>(P, b);
     if (q.kind == KIND_DONE) {   // early-exit calls: ended in an earlier window
         if (c == 0 && tid == 0) P.alive_out[b] = 0;
         return;
@@ -1703,8 +1705,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
         return;
     }
     if (wave_id() == 0) {
-        const ReqDesc dsc = P.ee ? scan_window(P, b, q, rows_s, pq_s, tab, x0, ua0, us0)
-                                 : scan_request(P, b, q, rows_s, pq_s, tab, x0, ua0, us0);
+        const ReqDesc dsc = EE ? scan_window(P, b, q, rows_s, pq_s, tab, x0, ua0, us0)
+                               : scan_request(P, b, q, rows_s, pq_s, tab, x0, ua0, us0);
         if (lane_id() == 0) sh_desc = dsc;
     }
     __syncthreads();
@@ -1718,7 +1720,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     const double rho_hat = resid ? sz_row.s / sy_row.s : 0.0;
     if (c == 0 && wave_id() == 0) {
         const int token = desc.state == SREQ_GREEDY ? desc.emit : -1;
-        if (P.ee) {
+        if constexpr (EE) {
             write_window(P, b, q, desc, pq_s, token);
             if (lane_id() == 0) P.alive_out[b] = desc.state == SREQ_CONT;
         } else {
@@ -1737,7 +1739,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
         }
     }
     // early-exit calls sum the drawn rows after the last window
-    if (!draw || P.ee) return;
+    if (!draw || EE) return;
     // this wave's unit of the drawn row pair (no workgroup barrier after here)
     const int unit = c * NWAVE + wave_id();
     if (unit >= P.cs) return;
@@ -2377,16 +2379,17 @@ int cu_count()
 // Resident workgroups of the persistent row pass per compute unit (from the
 // occupancy calculator; the grid never exceeds what can run at once, so the
 // static task assignment stays balanced).
-int row_wgs_per_cu(bool bf16, size_t lds)
+int row_wgs_per_cu(bool bf16, bool ee, size_t lds)
 {
-    static std::atomic<int> cache[2][64];
+    static std::atomic<int> cache[2][2][64];
     const int bucket = (int)std::min<size_t>(63, lds / 1024);
-    int n = cache[bf16][bucket].load(std::memory_order_relaxed);
+    int n = cache[bf16][ee][bucket].load(std::memory_order_relaxed);
     if (n <= 0) {
-        const void *fn = bf16 ? (const void *)row_pass_kernel<true> : (const void *)row_pass_kernel<false>;
+        const void *fn = bf16 ? (ee ? (const void *)row_pass_kernel<true, true> : (const void *)row_pass_kernel<true, false>)
+                              : (ee ? (const void *)row_pass_kernel<false, true> : (const void *)row_pass_kernel<false, false>);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, WG, (bucket + 1) * 1024) != hipSuccess || n <= 0)
             n = 2;
-        cache[bf16][bucket].store(n, std::memory_order_relaxed);
+        cache[bf16][ee][bucket].store(n, std::memory_order_relaxed);
     }
     return n;
 }
@@ -2457,7 +2460,7 @@ sv_status launch(Params &P, hipStream_t stream)
     const int64_t rows_max = (P.mode == MODE_SAMPLE) ? (int64_t)P.B * (2 * kw + 1)
                            : (P.mode == MODE_GREEDY) ? (int64_t)P.B * (kw + 1) : (int64_t)P.B * P.K;
     const size_t lds_a = sizeof(int) * (size_t)(3 * P.B + 1);
-    int64_t grid = (int64_t)cu_count() * row_wgs_per_cu(P.bf16, lds_a);
+    int64_t grid = (int64_t)cu_count() * row_wgs_per_cu(P.bf16, P.ee, lds_a);
     grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div(rows_max * ceil_div(nv, WVEC), NWAVE)));
     const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1) + sizeof(float2) * (size_t)P.K;
     const bool sample = P.mode == MODE_SAMPLE;
@@ -2471,9 +2474,14 @@ sv_status launch(Params &P, hipStream_t stream)
 #define SV_LAUNCH_PATH(BF, AL)                                                                              \
     do {                                                                                                    \
         SV_MARK(0);                                                                                         \
-        hipLaunchKernelGGL(row_pass_kernel<BF>, dim3((unsigned)grid), dim3(WG), lds_a, stream, P);           \
-        SV_MARK(1);                                                                                         \
-        hipLaunchKernelGGL((finish_kernel<BF, AL>), grid_b, dim3(WG), lds_b, stream, P);                    \
+        if (P.ee) {                                                                                         \
+            hipLaunchKernelGGL((row_pass_kernel<BF, true>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
+            hipLaunchKernelGGL((finish_kernel<BF, AL, true>), grid_b, dim3(WG), lds_b, stream, P);            \
+        } else {                                                                                            \
+            hipLaunchKernelGGL((row_pass_kernel<BF, false>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
+            SV_MARK(1);                                                                                     \
+            hipLaunchKernelGGL((finish_kernel<BF, AL, false>), grid_b, dim3(WG), lds_b, stream, P);           \
+        }                                                                                                   \
         SV_MARK(2);                                                                                         \
         if (sample && !P.ee) hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P); \
         SV_MARK(3);                                                                                         \
