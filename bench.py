@@ -51,8 +51,8 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "8fd116845f1c92b251797a1baef9a184beb379c2d9a4b15d9f6e6952786a698b",
-                    "fetch_bytes": 526053157, "write_bytes": 536941}
+ROW_PASS_TRAFFIC = {"source_sha256": "8a9a623218ee16b3a7781ff748039809c53d6ffe90c227913b822d216973d572",
+                    "fetch_bytes": 526028740, "write_bytes": 535102}
 
 
 def parse():
@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR")
+    ap.add_argument("--early-exit-window", type=int, default=0, metavar="W",
+                    help="time only early-exit calls with windows of W positions (for kernel traces)")
     return ap.parse_args()
 
 
@@ -210,6 +212,18 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"pmc_pass": "done", "row_pass_kernel": ROW_PASS_KERNEL,
                           "calibration": f"torch.neg over {CALIB_BYTES} B of fp32 (reads and writes that many)"}))
+        return
+
+    if args.early_exit_window > 0:
+        W = args.early_exit_window
+
+        def estep(i):
+            t, d = copies[i % ncopy]
+            sv.verify_sample_early_exit(t, d, tok, T, ua, us, window=W, out_tokens=out, num_accepted=nacc,
+                                        p_draft=pd, q_draft=qd, workspace=ws, stream=stream)
+        _, eper, _ = timed(estep, args.steps, args.warmup)
+        print(json.dumps({"early_exit_window": W, "ms_per_call": float(np.mean(eper)), "steps": args.steps,
+                          "windows": -(-K // W), "mean_accepted": float(nacc.float().mean().item())}))
         return
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
