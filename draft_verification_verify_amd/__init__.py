@@ -192,7 +192,7 @@ def _ws(device, B, K, V, workspace):
 
 def _raise(fn, st):
     if st != 0:
-        detail = lib.spec_verify_last_error().decode() if st == 6 else ""
+        detail = lib.spec_verify_last_error().decode() if st in (5, 6) else ""
         raise SpecVerifyError(fn, st, detail)
 
 

@@ -46,6 +46,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -2376,6 +2377,26 @@ int cu_count()
     return n;
 }
 
+// Check mode (environment variable SPECVERIFY_CHECK=1; a debugging aid, not
+// for graph capture): a call that enqueued its work waits for it and returns
+// SV_ERR_BAD_INPUT when a request reported bad data (a negative value in
+// vals[0..n): num_accepted of a verify call, depth_out of dcut_allocate).
+sv_status checked(sv_status st, const int32_t *vals, int32_t n, hipStream_t stream, const char *what)
+{
+    const char *e = getenv("SPECVERIFY_CHECK");
+    if (st != SV_OK || !e || e[0] != '1') return st;
+    std::vector<int32_t> h((size_t)n);
+    if (hipMemcpyAsync(h.data(), vals, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return hip_status(what);
+    for (int32_t i = 0; i < n; ++i)
+        if (h[(size_t)i] < 0) {
+            snprintf(g_last_error, sizeof g_last_error, "%s: request %d holds bad data", what, (int)i);
+            return SV_ERR_BAD_INPUT;
+        }
+    return SV_OK;
+}
+
 // Resident workgroups of the persistent row pass per compute unit (from the
 // occupancy calculator; the grid never exceeds what can run at once, so the
 // static task assignment stays balanced).
@@ -2635,7 +2656,7 @@ sv_status spec_verify_greedy(const void *target_logits, sv_dtype dt, const int32
     P.depth = depth;
     P.out_tokens = out_tokens;
     P.num_accepted = num_accepted;
-    return launch(P, stream);
+    return checked(launch(P, stream), num_accepted, B, stream, "spec_verify_greedy");
 }
 
 sv_status spec_verify_sample(const void *target_logits, const void *draft_logits, sv_dtype dt,
@@ -2665,7 +2686,7 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     P.num_accepted = num_accepted;
     P.p_draft = p_draft;
     P.q_draft = q_draft;
-    return launch(P, stream);
+    return checked(launch(P, stream), num_accepted, B, stream, "spec_verify_sample");
 }
 
 sv_status spec_verify_greedy_early_exit(const void *target_logits, sv_dtype dt, const int32_t *draft_tokens,
@@ -2688,7 +2709,8 @@ sv_status spec_verify_greedy_early_exit(const void *target_logits, sv_dtype dt, 
     P.depth = depth;
     P.out_tokens = out_tokens;
     P.num_accepted = num_accepted;
-    return launch_windows(P, std::min(window, std::max(K, 1)), stream);
+    const sv_status ls = launch_windows(P, std::min(window, std::max(K, 1)), stream);
+    return checked(ls, num_accepted, B, stream, "spec_verify_greedy_early_exit");
 }
 
 sv_status spec_verify_sample_early_exit(const void *target_logits, const void *draft_logits, sv_dtype dt,
@@ -2720,7 +2742,8 @@ sv_status spec_verify_sample_early_exit(const void *target_logits, const void *d
     P.num_accepted = num_accepted;
     P.p_draft = p_draft;
     P.q_draft = q_draft;
-    return launch_windows(P, std::min(window, std::max(K, 1)), stream);
+    const sv_status ls = launch_windows(P, std::min(window, std::max(K, 1)), stream);
+    return checked(ls, num_accepted, B, stream, "spec_verify_sample_early_exit");
 }
 
 sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_logits, sv_dtype dt,
@@ -2753,7 +2776,7 @@ sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_
     P.p_draft = p_draft;
     P.q_draft = q_draft;
     P.dstats_in = (const Stat *)draft_stats;
-    return launch(P, stream);
+    return checked(launch(P, stream), num_accepted, B, stream, "spec_verify_sample_reuse");
 }
 
 sv_status spec_draft_confidence_stats(const void *draft_logits, sv_dtype dt, const int32_t *max_depth, int32_t B,
@@ -2847,7 +2870,7 @@ sv_status dcut_allocate(const float *conf, const int32_t *max_depth, int32_t B, 
     if (!dcut_lds_ok(lds)) return SV_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     hipLaunchKernelGGL(dcut_kernel, dim3(1), dim3(DCUT_WG), lds, stream, conf, max_depth, B, K, budget, depth_out);
-    return hip_status("dcut_kernel launch");
+    return checked(hip_status("dcut_kernel launch"), depth_out, B, stream, "dcut_allocate");
 }
 
 }  // extern "C"

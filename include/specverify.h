@@ -47,6 +47,12 @@
  *     [0, V), a uniform outside [0, 1), or a row that is read and holds a NaN
  *     or +inf, or only -inf.  -inf logits (masked tokens) are allowed
  *     otherwise.  No C++ exception crosses this interface.
+ *   Check mode.  With the environment variable SPECVERIFY_CHECK=1 the verify
+ *     calls and dcut_allocate wait for their own work and return
+ *     SV_ERR_BAD_INPUT when a request reported bad data (num_accepted[b] or
+ *     depth_out[b] = -1; spec_verify_last_error names the first such
+ *     request).  A debugging aid: it synchronises the stream, so it is not
+ *     for graph capture.
  *   Limits.  1 <= B <= 4096, 0 <= K <= 1024, 1 <= V <= 2000000.
  */
 #ifndef SPECVERIFY_H
@@ -66,7 +72,7 @@ typedef enum sv_status {
     SV_ERR_UNSUPPORTED = 2,   /* size beyond the limits above                 */
     SV_ERR_WORKSPACE = 3,     /* workspace missing, too small or misaligned   */
     SV_ERR_BUDGET = 4,        /* D-cut budget smaller than the batch          */
-    SV_ERR_BAD_INPUT = 5,     /* reserved: bad data found while checking      */
+    SV_ERR_BAD_INPUT = 5,     /* check mode: a request reported bad data      */
     SV_ERR_HIP = 6            /* a HIP launch or query failed                 */
 } sv_status;
 
