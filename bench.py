@@ -240,6 +240,15 @@ def main():
     rp_ms = float(stage_ms[0])
     achieved = rp_bytes / (rp_ms * 1e-3) / 1e9
     n_mean = float(nacc.float().mean().item())
+    # practical ceiling: a plain read of as many bytes as the row pass reads,
+    # alternating two buffers so the 256 MB MALL serves none of it
+    log("timing the plain read of the row pass's bytes")
+    rbufs = [torch.ones(rp_bytes // 2, dtype=torch.int16, device="cuda") for _ in range(2)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _, cper, _ = timed(lambda i: sv.read_ceiling(rbufs[i % 2], sink, stream), args.steps, args.warmup)
+    ceil_ms = float(np.mean(cper))
+    ceil_gbs = rp_bytes / (ceil_ms * 1e-3) / 1e9
+    del rbufs
     sha = source_sha256()
     traffic = None
     if ROW_PASS_TRAFFIC["source_sha256"] == sha and ROW_PASS_TRAFFIC["fetch_bytes"] is not None:
@@ -274,6 +283,10 @@ def main():
                      "algorithmic_bytes_per_launch": rp_bytes,
                      "avg_launch_ms": rp_ms},
         "kernel_source_sha256": sha,
+        "read_ceiling": {"GB_s": ceil_gbs, "ms": ceil_ms, "bytes": rp_bytes,
+                         "row_pass_frac_of_ceiling": achieved / ceil_gbs,
+                         "note": "spec_verify_read_ceiling: one plain read of the row pass's bytes, same load "
+                                 "width and cache policy, two alternating buffers"},
     }
 
     # -------------------------------------------------------------- secondary
@@ -427,9 +440,16 @@ def main():
             oracle.verify_sample(w.target, w.draft, w.tokens, w.temperature, w.u_accept, w.u_sample)
             t_tot += time.perf_counter() - t0
             reps += 1
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+        except OSError:
+            pass
         result["cpu_baseline"] = {"value": reps * rows / t_tot, "unit": "rows/s", "cores": 1, "kind": "oracle",
                                   "sample": f"the full headline batch (64 requests, {rows} verified rows) "
-                                            f"run {reps} times in {t_tot:.1f} s; single-threaded C, fp64"}
+                                            f"run {reps} times in {t_tot:.1f} s; single-threaded C, fp64",
+                                  "cpu": f"1 core of {os.cpu_count()} visible, {cpu_model}"}
     print(json.dumps(result), flush=True)
 
 

@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
     L.spec_accept_stats_update.argtypes = [vp, vp, i32, i32, vp, vp]
     L.dcut_allocate.restype = ctypes.c_int
     L.dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.spec_verify_read_ceiling.restype = ctypes.c_int
+    L.spec_verify_read_ceiling.argtypes = [vp, sz, vp, vp]
     L.spec_verify_timing_begin.restype = ctypes.c_int
     L.spec_verify_timing_begin.argtypes = [i32]
     L.spec_verify_timing_end.restype = ctypes.c_int
@@ -90,11 +92,26 @@ EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify
             "spec_verify_workspace_size", "spec_verify_timing_begin", "spec_verify_timing_end",
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
             "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
-            "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit")
+            "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit",
+            "spec_verify_read_ceiling")
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
     return int(lib.spec_verify_workspace_size(B, K, V))
+
+
+def read_ceiling(buf, sink=None, stream=None):
+    """Benchmark instrumentation: one plain read of every byte of ``buf`` (a
+    contiguous CUDA tensor) with the row-statistics kernel's load width."""
+    torch = _torch()
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    st = lib.spec_verify_read_ceiling(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
+    _raise("spec_verify_read_ceiling", st)
+    return sink
 
 
 def timing_begin(n: int) -> None:

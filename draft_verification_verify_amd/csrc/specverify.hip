@@ -2060,6 +2060,48 @@ __device__ __forceinline__ float sanitize_conf(float c)
 }
 
 // ---------------------------------------------------------------------------
+// Read ceiling (benchmark instrumentation): a plain stream over a buffer with
+// the row pass's load width and cache policy, every byte read once, against
+// which the row pass's bandwidth is compared.  A wave reads contiguous 4 KiB
+// blocks (UW 16-byte loads per lane, each load instruction 1 KiB), two blocks
+// in flight, handed out grid-stride; lanes fold what they read so the loads
+// stay live, and the fold reaches memory only in the unlikely case that it
+// equals a fixed value.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(WG) void read_ceiling_kernel(const uint4 *buf_, int64_t nvec, uint32_t *sink)
+{
+    const gvec_t buf = (gvec_t)buf_;
+    const int64_t nwaves = (int64_t)gridDim.x * NWAVE;
+    const int64_t gw = (int64_t)blockIdx.x * NWAVE + wave_id();
+    const int lane = lane_id();
+    const int64_t nblk = nvec / WVEC;
+    uint32_t acc = 0;
+    int64_t blk = gw;
+    for (; blk + nwaves < nblk; blk += 2 * nwaves) {
+        uint4 r0[UW], r1[UW];
+#pragma unroll
+        for (int j = 0; j < UW; ++j) r0[j] = ld_stream(buf + blk * WVEC + j * 64 + lane);
+#pragma unroll
+        for (int j = 0; j < UW; ++j) r1[j] = ld_stream(buf + (blk + nwaves) * WVEC + j * 64 + lane);
+#pragma unroll
+        for (int j = 0; j < UW; ++j) acc ^= r0[j].x ^ r0[j].y ^ r0[j].z ^ r0[j].w ^ r1[j].x ^ r1[j].y ^ r1[j].z ^ r1[j].w;
+    }
+    if (blk < nblk) {
+#pragma unroll
+        for (int j = 0; j < UW; ++j) {
+            const uint4 r = ld_stream(buf + blk * WVEC + j * 64 + lane);
+            acc ^= r.x ^ r.y ^ r.z ^ r.w;
+        }
+    }
+    for (int64_t v = nblk * WVEC + gw * 64 + lane; v < nvec; v += nwaves * 64) {
+        const uint4 r = ld_stream(buf + v);
+        acc ^= r.x ^ r.y ^ r.z ^ r.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+// ---------------------------------------------------------------------------
 // Cost-aware D-cut: one workgroup of 1024 threads.  Per request the depth with
 // the best benefit (prefix confidence times depth over the interpolated cost,
 // in double), then candidates ranked by (benefit desc, request asc) by
@@ -2578,6 +2620,16 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
 }  // namespace
 
 extern "C" {
+
+sv_status spec_verify_read_ceiling(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream)
+{
+    if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || !aligned16(buf)) return SV_ERR_INVALID_ARG;
+    const int64_t grid = (int64_t)cu_count() * 8;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(read_ceiling_kernel, dim3((unsigned)grid), dim3(WG), 0, stream, (const uint4 *)buf,
+                       (int64_t)(bytes / 16), sink);
+    return hip_status("read_ceiling_kernel launch");
+}
 
 sv_status spec_verify_timing_begin(int32_t n)
 {

@@ -109,6 +109,15 @@ size_t spec_verify_workspace_size(int32_t B, int32_t K, int32_t V);
 sv_status spec_verify_timing_begin(int32_t n);
 sv_status spec_verify_timing_end(float *ms, int32_t n);
 
+/* Read ceiling for benchmarks (instrumentation; computes nothing of the
+ * method): one kernel that reads `bytes` bytes of `buf` once, with the load
+ * width and cache policy of the row-statistics kernel, the practical
+ * bandwidth ceiling that kernel's rate is compared with.  buf: device
+ * pointer, 16-byte aligned, bytes a positive multiple of 16; sink: one
+ * device uint32 the kernel may write (a fold of the data, kept so the loads
+ * are not removed).  Asynchronous on `stream`. */
+sv_status spec_verify_read_ceiling(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Greedy (T = 0) verification.
  * For request b with depth d = depth[b] (or K when depth is NULL): drafted
  * token k is accepted iff it equals the argmax of target row (b, k) (values

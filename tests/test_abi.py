@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -46,6 +46,14 @@ def test_timing_arguments_rejected_on_host():
     buf = (ctypes.c_float * 3)()
     assert L.spec_verify_timing_end(buf, 1) == 1       # nothing armed on this thread
     assert L.spec_verify_timing_end(None, -1) == 1
+
+
+def test_read_ceiling_host_errors():
+    assert L.spec_verify_read_ceiling(NULL, 1024, FAKE, NULL) == 1
+    assert L.spec_verify_read_ceiling(FAKE, 1024, NULL, NULL) == 1
+    assert L.spec_verify_read_ceiling(FAKE, 0, FAKE, NULL) == 1
+    assert L.spec_verify_read_ceiling(FAKE, 1000, FAKE, NULL) == 1      # not a multiple of 16
+    assert L.spec_verify_read_ceiling(FAKE_MIS, 1024, FAKE, NULL) == 1
 
 
 def test_workspace_size():

@@ -56,3 +56,14 @@ def test_check_mode_reports_bad_requests(monkeypatch):
         n = host(fn(bad)[1])
         torch.cuda.synchronize()
         assert n[3] == -1 and np.all(np.delete(n, 3) >= 0), name
+
+
+def test_read_ceiling_sizes():
+    import draft_verification_verify_amd as sv
+    note("read ceiling: whole blocks, a partial block and a vector tail")
+    for nbytes in (16, 4096, 4096 + 48, 8 * 4096 * 1024 + 16 * 37):
+        buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+        sink = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+        sv.read_ceiling(buf, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) == 5     # a fold of zeros never matches the stored value
