@@ -257,6 +257,25 @@ def test_ee_mixed_fp32_full_size():
     tal.assert_ok("mixed")
 
 
+def test_ee_maximum_sizes():
+    note("early-exit at the limits: B=4096 (K=3, V=17) and K=1024 (B=2, V=33)")
+    w = synth.random_case(31, B=4096, K=3, V=17, dtype="f32", temps=(0.0, 1.0), sigma=0.6)
+    ora = oracle_ee_sample(w)
+    tal = Tally()
+    for window in (1, 3):
+        compare_ee_sample(w, run_ee_sample(w, None, window), ora, None, tal)
+    og = oracle.verify_early_exit(w.target, w.tokens)
+    out, n = run_ee_greedy(w, None, 2)
+    assert np.array_equal(n, og["n"]) and np.array_equal(out, og["out"])
+    # low draft noise: long accepted prefixes over many windows
+    w2 = synth.random_case(32, B=2, K=1024, V=33, dtype="bf16", temps=(1.0,), sigma=0.05)
+    ora2 = oracle_ee_sample(w2)
+    assert ora2["n"].max() > 20
+    for window in (7, 100, 1024):
+        compare_ee_sample(w2, run_ee_sample(w2, None, window), ora2, None, tal)
+    tal.assert_ok("limits")
+
+
 def test_ee_workspace_reuse_and_alternating_calls():
     note("early-exit: one workspace across one-pass and early-exit calls of different shapes")
     import draft_verification_verify_amd as sv
