@@ -65,8 +65,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR")
-    ap.add_argument("--early-exit-window", type=int, default=0, metavar="W",
-                    help="time only early-exit calls with windows of W positions (for kernel traces)")
+    ap.add_argument("--early-exit-ends", default="", metavar="E1,E2,...",
+                    help="time only early-exit calls with these window ends (for kernel traces)")
     return ap.parse_args()
 
 
@@ -214,16 +214,16 @@ def main():
                           "calibration": f"torch.neg over {CALIB_BYTES} B of fp32 (reads and writes that many)"}))
         return
 
-    if args.early_exit_window > 0:
-        W = args.early_exit_window
+    if args.early_exit_ends:
+        ends = [int(x) for x in args.early_exit_ends.split(",")]
 
         def estep(i):
             t, d = copies[i % ncopy]
-            sv.verify_sample_early_exit(t, d, tok, T, ua, us, window=W, out_tokens=out, num_accepted=nacc,
+            sv.verify_sample_early_exit(t, d, tok, T, ua, us, ends=ends, out_tokens=out, num_accepted=nacc,
                                         p_draft=pd, q_draft=qd, workspace=ws, stream=stream)
         _, eper, _ = timed(estep, args.steps, args.warmup)
-        print(json.dumps({"early_exit_window": W, "ms_per_call": float(np.mean(eper)), "steps": args.steps,
-                          "windows": -(-K // W), "mean_accepted": float(nacc.float().mean().item())}))
+        print(json.dumps({"early_exit_ends": ends, "ms_per_call": float(np.mean(eper)), "steps": args.steps,
+                          "mean_accepted": float(nacc.float().mean().item())}))
         return
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
@@ -381,25 +381,26 @@ def main():
             "ms": float(np.mean(cper2)), "admitted": int((cdep > 0).sum().item()),
             "verify_slots": int(cdep.sum().item()),
             "note": "max_verify 96 in the table's cost units (1.0 at depth 1 ... 3.0 at depth 16); one workgroup; on these high-entropy drafts every request's best benefit/cost depth is 1"}
-        # early-exit verification of the same dense batch: windows of W
-        # positions, no row read after a request's first rejection; the
-        # committed tokens are those of the one-pass step
+        # early-exit verification of the same dense batch: windows ending at
+        # the given positions, no row read after a request's first rejection;
+        # the committed tokens are those of the one-pass step
         step(0)
         n_one = nacc.cpu().numpy().copy()
-        for W in (2, 4, 8):
-            def estep(i, W=W):
+        for ends in ([4, 16], [2, 6, 16], [1, 16], [8, 16], [4, 8, 12, 16]):
+            def estep(i, ends=ends):
                 t, d = copies[i % ncopy]
-                sv.verify_sample_early_exit(t, d, tok, T, ua, us, window=W, out_tokens=out, num_accepted=nacc,
+                sv.verify_sample_early_exit(t, d, tok, T, ua, us, ends=ends, out_tokens=out, num_accepted=nacc,
                                             p_draft=pd, q_draft=qd, workspace=ws, stream=stream)
             _, eper, _ = timed(estep, steps2, warm2)
             ems = float(np.mean(eper))
             en = nacc.cpu().numpy()
-            # positions whose target and draft rows the row passes stream
-            pos_read = [K if n >= K else min(K, (n // W + 1) * W) for n in en.tolist()]
-            sec[f"early_exit_window{W}_B64_K16"] = {
+            # positions whose target and draft rows the row passes stream:
+            # up to the end of the window in which the request stops
+            pos_read = [K if n >= K else min(K, next(e for e in ends if e > n)) for n in en.tolist()]
+            sec["early_exit_ends_" + "_".join(map(str, ends)) + "_B64_K16"] = {
                 "rows_per_s": rows / (ems * 1e-3), "ms": ems, "vs_one_pass_ms": ms / ems,
                 "row_pass_rows_per_step": 2 * int(sum(pos_read)), "one_pass_row_pass_rows": 2 * B * K,
-                "windows": -(-K // W), "same_num_accepted_as_one_pass": bool(np.array_equal(en, n_one)),
+                "windows": len(ends), "same_num_accepted_as_one_pass": bool(np.array_equal(en, n_one)),
                 "note": "rows_per_s counts the B*(K+1) rows the step decides, as the headline does; "
                         "the row passes stream the positions up to the end of each request's stopping "
                         "window"}

@@ -58,9 +58,10 @@ def _load() -> ctypes.CDLL:
     L.spec_verify_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, sz, vp]
     L.spec_verify_greedy_early_exit.restype = ctypes.c_int
-    L.spec_verify_greedy_early_exit.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.spec_verify_greedy_early_exit.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, sz,
+                                                vp]
     L.spec_verify_sample_early_exit.restype = ctypes.c_int
-    L.spec_verify_sample_early_exit.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+    L.spec_verify_sample_early_exit.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32,
                                                 vp, vp, vp, vp, vp, sz, vp]
     L.spec_draft_confidence.restype = ctypes.c_int
     L.spec_draft_confidence.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -265,10 +266,30 @@ def verify_sample(target, draft, tokens, temperature, u_accept, u_sample, depth=
     return out_tokens, num_accepted, p_draft, q_draft
 
 
-def verify_greedy_early_exit(target, tokens, depth=None, *, window: int = 8, out_tokens=None,
+def window_ends(K: int, window=None, ends=None):
+    """Window ends for the early-exit calls: ``ends`` as given, else fixed
+    windows of ``window`` positions (W, 2W, ... up to K), else a first
+    window of about K/4 positions and one window for the rest."""
+    if ends is not None:
+        return [int(e) for e in ends]
+    if window is not None:
+        W = int(window)
+        if W < 1:
+            raise ValueError("window must be >= 1")
+        return [W * i for i in range(1, max(1, -(-K // W)) + 1)]
+    first = max(1, (K + 3) // 4)
+    return [first, K] if first < K else [max(K, 1)]
+
+
+def _ends_arg(ends):
+    arr = (ctypes.c_int32 * len(ends))(*ends)
+    return ctypes.cast(arr, ctypes.c_void_p), len(ends), arr
+
+
+def verify_greedy_early_exit(target, tokens, depth=None, *, window=None, ends=None, out_tokens=None,
                              num_accepted=None, workspace=None, stream=None):
-    """verify_greedy that reads no row after a request's first rejection
-    (windows of ``window`` positions)."""
+    """verify_greedy that reads no row after a request's first rejection, in
+    windows (see ``window_ends``)."""
     torch = _torch()
     B, K1, V = target.shape
     K = K1 - 1
@@ -280,18 +301,19 @@ def verify_greedy_early_exit(target, tokens, depth=None, *, window: int = 8, out
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
     ws, nbytes = _ws(target.device, B, K, V, workspace)
+    ep, ne, _keep = _ends_arg(window_ends(K, window, ends))
     st = lib.spec_verify_greedy_early_exit(_ptr(target), _dtype_code(target), _ptr(tokens), _ptr(depth),
-                                           B, K, V, int(window), _ptr(out_tokens), _ptr(num_accepted),
+                                           B, K, V, ep, ne, _ptr(out_tokens), _ptr(num_accepted),
                                            _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_greedy_early_exit", st)
     return out_tokens, num_accepted
 
 
 def verify_sample_early_exit(target, draft, tokens, temperature, u_accept, u_sample, depth=None, *,
-                             window: int = 8, out_tokens=None, num_accepted=None, p_draft=None,
+                             window=None, ends=None, out_tokens=None, num_accepted=None, p_draft=None,
                              q_draft=None, want_probs: bool = True, workspace=None, stream=None):
-    """verify_sample that reads no row after a request's first rejection
-    (windows of ``window`` positions).  Returns (out_tokens, num_accepted,
+    """verify_sample that reads no row after a request's first rejection, in
+    windows (see ``window_ends``).  Returns (out_tokens, num_accepted,
     p_draft, q_draft)."""
     torch = _torch()
     B, K1, V = target.shape
@@ -313,9 +335,10 @@ def verify_sample_early_exit(target, draft, tokens, temperature, u_accept, u_sam
     if want_probs and q_draft is None:
         q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
     ws, nbytes = _ws(dev, B, K, V, workspace)
+    ep, ne, _keep = _ends_arg(window_ends(K, window, ends))
     st = lib.spec_verify_sample_early_exit(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens),
                                            _ptr(depth), _ptr(temperature), _ptr(u_accept), _ptr(u_sample),
-                                           B, K, V, int(window), _ptr(out_tokens), _ptr(num_accepted),
+                                           B, K, V, ep, ne, _ptr(out_tokens), _ptr(num_accepted),
                                            _ptr(p_draft), _ptr(q_draft), _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_sample_early_exit", st)
     return out_tokens, num_accepted, p_draft, q_draft

@@ -672,13 +672,17 @@ __device__ __forceinline__ int find_request(const int *row_off, int B, int r)
 
 // Chunking of the row pass: cpr chunks per row of nb batches each, with cpr
 // chosen so that every wave gets about eight tasks (bounded tail imbalance)
-// but a task is never shorter than one batch.
+// but a task covers at least two batches where the row has them: a wave
+// sets up its next task while its other buffer's batch is in flight, and a
+// run of one-batch tasks leaves that set-up exposed between loads (passes
+// over a few hundred rows ran about 12 % slower on MI355X).
 __device__ __forceinline__ void row_chunking(int R, int V, bool bf16, int64_t nwaves, int &cpr, int &nb)
 {
     const int64_t nv = nvec_max(V, bf16 ? 8 : 4);
     const int nbt = (int)ceil_div(nv, WVEC);
     const int64_t want = ceil_div(8 * nwaves, (int64_t)(R > 0 ? R : 1));
-    cpr = (int)std::min<int64_t>(std::max<int64_t>(want, 1), std::min(nbt, CPR_CAP));
+    cpr = (int)std::min<int64_t>(std::max<int64_t>(want, 1),
+                                 std::min<int64_t>(std::min(nbt, CPR_CAP), ceil_div(nbt, 2)));
     nb = (int)ceil_div(nbt, cpr);
     cpr = (int)ceil_div(nbt, nb);
 }
@@ -945,11 +949,13 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     k.vec = rv.vec;
     k.head = rv.head;
     k.nvec = rv.nvec;
-    // The accept test needs this row's logit at the drafted token x; every
-    // chunk reads it, so the finish kernel has it from the partials.  x
-    // outside [0, V) is clamped here and rejected as bad data by the scan.
-    k.zx = 0.0f;
-    if (kind == KIND_SAMPLED || kind == KIND_SAMPLED_R) {
+    // The accept test needs this row's logit at the drafted token x; the
+    // row's first chunk reads it (the others carry the merge identity, so
+    // only one task per row waits on these two loads), and the finish kernel
+    // has it from the merged partials.  x outside [0, V) is clamped here and
+    // rejected as bad data by the scan.
+    k.zx = __int_as_float(0x7fffffff);
+    if ((kind == KIND_SAMPLED || kind == KIND_SAMPLED_R) && c == 0) {
         const int x = min(max(ld_scalar_i32(P.tokens + (int64_t)b * P.K + kk), 0), P.V - 1);
         k.zx = ld_scalar_logit<BF16>(row_start, x);
     }
@@ -982,7 +988,8 @@ __device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, cons
     return st;
 }
 
-// Sampled rows carry the logit at the drafted token in the partial's index.
+// A sampled row's first chunk carries the logit at the drafted token in the
+// partial's index; the other chunks carry the merge identity.
 template <bool BF16>
 __device__ __forceinline__ Stat finish_task(const Task<BF16> &k, const ArgmaxLane &am, const LseLane &ls)
 {
@@ -1366,8 +1373,9 @@ __device__ void write_window(const Params &P, int b, const ReqPlan &q, const Req
 
 // Merge of two partial statistics of one row: (max, lowest argmax) with NaN
 // propagated, or (max, sum relative to the max) rescaled to the larger max.
-// Log-sum-exp partials carry the logit at the drafted token in idx (every
-// chunk the same value; the merge identity carries 0x7fffffff).
+// Log-sum-exp partials carry the logit at the drafted token in idx (the
+// row's first chunk; the other chunks and the merge identity carry
+// 0x7fffffff).
 __device__ __forceinline__ Stat merge2(Stat a, Stat b, bool lse, double cs, const double *tab)
 {
     if (!lse) {
@@ -2561,21 +2569,38 @@ sv_status launch(Params &P, hipStream_t stream)
     return hip_status("kernel launch");
 }
 
-// Early-exit verification: per window of `window` positions a row pass and
-// a finish kernel (merge, scan, outputs, draw record), back to back on the
-// stream (the host never waits); for sampled calls, after the last window,
-// the sampler units and the draw of every request that draws, whichever
-// window it ended in.  Window w verifies positions [w * window, (w + 1) *
-// window) of the requests that accepted every earlier position; the last
-// window reaches K.  The still-verifying flags alternate between two arrays
-// so that a window never overwrites what its own kernels read.
-sv_status launch_windows(Params &P, int window, hipStream_t stream)
+// Window ends of an early-exit call: strictly increasing, the first >= 1;
+// the list is cut after the first end that reaches K (no request is left
+// after it), and must contain one.  Ends are clipped to max(K, 1).
+bool window_plan(const int32_t *ends, int32_t n, int32_t K, std::vector<int> &out)
 {
-    const int nwin = P.K == 0 ? 1 : (int)ceil_div(P.K, window);
+    out.clear();
+    if (!ends || n < 1) return false;
+    int prev = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (ends[i] <= prev) return false;
+        prev = ends[i];
+        out.push_back(std::min(ends[i], std::max(K, 1)));
+        if (ends[i] >= K) return true;
+    }
+    return false;
+}
+
+// Early-exit verification: per window a row pass and a finish kernel
+// (merge, scan, outputs, draw record), back to back on the stream (the host
+// never waits); for sampled calls, after the last window, the sampler units
+// and the draw of every request that draws, whichever window it ended in.
+// Window w verifies positions [ends[w-1], ends[w]) (ends[-1] = 0) of the
+// requests that accepted every earlier position; the last window reaches K.
+// The still-verifying flags alternate between two arrays so that a window
+// never overwrites what its own kernels read.
+sv_status launch_windows(Params &P, const std::vector<int> &ends, hipStream_t stream)
+{
+    const int nwin = (int)ends.size();
     P.ee = 1;
     for (int w = 0; w < nwin; ++w) {
-        P.win_lo = w * window;
-        P.win_hi = P.win_lo + window;
+        P.win_lo = w == 0 ? 0 : ends[(size_t)w - 1];
+        P.win_hi = ends[(size_t)w];
         P.alive_in = P.ws.alive + (size_t)(w & 1) * (size_t)P.B;
         P.alive_out = P.ws.alive + (size_t)((w + 1) & 1) * (size_t)P.B;
         const sv_status st = launch(P, stream);
@@ -2742,14 +2767,16 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
 }
 
 sv_status spec_verify_greedy_early_exit(const void *target_logits, sv_dtype dt, const int32_t *draft_tokens,
-                                        const int32_t *depth, int32_t B, int32_t K, int32_t V, int32_t window,
-                                        int32_t *out_tokens, int32_t *num_accepted, void *workspace,
-                                        size_t ws_bytes, hipStream_t stream)
+                                        const int32_t *depth, int32_t B, int32_t K, int32_t V,
+                                        const int32_t *window_ends, int32_t n_windows, int32_t *out_tokens,
+                                        int32_t *num_accepted, void *workspace, size_t ws_bytes,
+                                        hipStream_t stream)
 {
     sv_status st = check_shape(B, K, V);
     if (st != SV_OK) return st;
     if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
-    if (window < 1) return SV_ERR_INVALID_ARG;
+    std::vector<int> ends;
+    if (!window_plan(window_ends, n_windows, K, ends)) return SV_ERR_INVALID_ARG;
     if (!target_logits || !out_tokens || !num_accepted || (K > 0 && !draft_tokens)) return SV_ERR_INVALID_ARG;
     if (!aligned16(target_logits)) return SV_ERR_INVALID_ARG;
     Layout L;
@@ -2761,21 +2788,23 @@ sv_status spec_verify_greedy_early_exit(const void *target_logits, sv_dtype dt, 
     P.depth = depth;
     P.out_tokens = out_tokens;
     P.num_accepted = num_accepted;
-    const sv_status ls = launch_windows(P, std::min(window, std::max(K, 1)), stream);
+    const sv_status ls = launch_windows(P, ends, stream);
     return checked(ls, num_accepted, B, stream, "spec_verify_greedy_early_exit");
 }
 
 sv_status spec_verify_sample_early_exit(const void *target_logits, const void *draft_logits, sv_dtype dt,
                                         const int32_t *draft_tokens, const int32_t *depth,
                                         const float *temperature, const float *u_accept, const float *u_sample,
-                                        int32_t B, int32_t K, int32_t V, int32_t window, int32_t *out_tokens,
-                                        int32_t *num_accepted, float *p_draft, float *q_draft, void *workspace,
-                                        size_t ws_bytes, hipStream_t stream)
+                                        int32_t B, int32_t K, int32_t V, const int32_t *window_ends,
+                                        int32_t n_windows, int32_t *out_tokens, int32_t *num_accepted,
+                                        float *p_draft, float *q_draft, void *workspace, size_t ws_bytes,
+                                        hipStream_t stream)
 {
     sv_status st = check_shape(B, K, V);
     if (st != SV_OK) return st;
     if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
-    if (window < 1) return SV_ERR_INVALID_ARG;
+    std::vector<int> ends;
+    if (!window_plan(window_ends, n_windows, K, ends)) return SV_ERR_INVALID_ARG;
     if (!target_logits || !temperature || !u_sample || !out_tokens || !num_accepted) return SV_ERR_INVALID_ARG;
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
     if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits))) return SV_ERR_INVALID_ARG;
@@ -2794,7 +2823,7 @@ sv_status spec_verify_sample_early_exit(const void *target_logits, const void *d
     P.num_accepted = num_accepted;
     P.p_draft = p_draft;
     P.q_draft = q_draft;
-    const sv_status ls = launch_windows(P, std::min(window, std::max(K, 1)), stream);
+    const sv_status ls = launch_windows(P, ends, stream);
     return checked(ls, num_accepted, B, stream, "spec_verify_sample_early_exit");
 }
 

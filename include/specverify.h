@@ -174,33 +174,41 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
  * length counts the drafted tokens approved before the first discrepancy
  * ([Remio], section "Come AngelSpec rende DFly più selettivo"), so no row
  * after a request's first rejection can change its output; these calls do
- * not read them.  The library verifies windows of `window` positions, one
- * launch sequence per window, back to back on the stream: window w reads
- * positions [w * window, (w + 1) * window) of the requests that accepted
- * every earlier position, and the rows a request reads end with the window
- * in which it stops.  The host never waits.
+ * not read them.  The library verifies the positions in windows, one launch
+ * sequence per window, back to back on the stream: window w reads positions
+ * [window_ends[w-1], window_ends[w]) (window_ends[-1] = 0) of the requests
+ * that accepted every earlier position, and the rows a request reads end
+ * with the window in which it stops.  The host never waits.
  * Results: on data with no bad values, out_tokens and num_accepted equal
  * those of the one-pass call on the same arguments (the accept decisions
  * take the same arithmetic; row statistics may round differently where the
- * window changes how rows are split into chunks).  Bad data is reported as
+ * windows change how rows are split into chunks).  Bad data is reported as
  * by the one-pass call, but only at positions up to and including the first
  * rejection, and for the rows and uniforms a draw reads: later positions are
  * not read.  p_draft / q_draft hold p_k(x_k), q_k(x_k) of sampled requests
  * at positions k <= min(n_b, d-1) and 0 elsewhere.
- *   window  positions per window, >= 1 (a window above K is K)
+ *   window_ends  HOST array of n_windows ints, read during the call:
+ *                strictly increasing, window_ends[0] >= 1, some entry >= K;
+ *                entries after the first one >= K are ignored
+ *                (SV_ERR_INVALID_ARG otherwise).  Fixed windows of W
+ *                positions are W, 2W, ...; fewer windows cost less fixed
+ *                latency, a short first window reads less when many
+ *                requests reject early.
  *   Other arguments as in spec_verify_greedy / spec_verify_sample.
  *   Timing instrumentation (spec_verify_timing_begin) does not record these
  *   calls. */
 sv_status spec_verify_greedy_early_exit(const void *target_logits, sv_dtype dt,
                                         const int32_t *draft_tokens, const int32_t *depth,
-                                        int32_t B, int32_t K, int32_t V, int32_t window,
+                                        int32_t B, int32_t K, int32_t V,
+                                        const int32_t *window_ends, int32_t n_windows,
                                         int32_t *out_tokens, int32_t *num_accepted,
                                         void *workspace, size_t ws_bytes, hipStream_t stream);
 sv_status spec_verify_sample_early_exit(const void *target_logits, const void *draft_logits,
                                         sv_dtype dt, const int32_t *draft_tokens,
                                         const int32_t *depth, const float *temperature,
                                         const float *u_accept, const float *u_sample,
-                                        int32_t B, int32_t K, int32_t V, int32_t window,
+                                        int32_t B, int32_t K, int32_t V,
+                                        const int32_t *window_ends, int32_t n_windows,
                                         int32_t *out_tokens, int32_t *num_accepted,
                                         float *p_draft, float *q_draft,
                                         void *workspace, size_t ws_bytes, hipStream_t stream);

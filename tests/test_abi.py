@@ -120,21 +120,30 @@ def test_sample_host_errors():
 def test_early_exit_host_errors():
     wsb = sv.workspace_size(4, 3, 1000)
 
-    def g(target=FAKE, dt=1, tokens=FAKE, B=4, K=3, V=1000, window=2, out=FAKE, num=FAKE, ws=FAKE,
-          n=wsb):
-        return L.spec_verify_greedy_early_exit(target, dt, tokens, NULL, B, K, V, window, out, num, ws, n,
-                                               NULL)
+    def ends_arg(ends):
+        if ends is None:
+            return NULL, 0
+        arr = (ctypes.c_int32 * max(len(ends), 1))(*ends)
+        return ctypes.cast(arr, ctypes.c_void_p), len(ends)
 
-    def s(target=FAKE, draft=FAKE, T=FAKE, ua=FAKE, us=FAKE, window=2, B=4, ws=FAKE, n=wsb):
-        return L.spec_verify_sample_early_exit(target, draft, 1, FAKE, NULL, T, ua, us, B, 3, 1000, window,
+    def g(target=FAKE, dt=1, tokens=FAKE, B=4, K=3, V=1000, ends=(2, 3), out=FAKE, num=FAKE, ws=FAKE, n=wsb):
+        ep, ne = ends_arg(ends)
+        return L.spec_verify_greedy_early_exit(target, dt, tokens, NULL, B, K, V, ep, ne, out, num, ws, n, NULL)
+
+    def s(target=FAKE, draft=FAKE, T=FAKE, ua=FAKE, us=FAKE, ends=(2, 3), B=4, ws=FAKE, n=wsb):
+        ep, ne = ends_arg(ends)
+        return L.spec_verify_sample_early_exit(target, draft, 1, FAKE, NULL, T, ua, us, B, 3, 1000, ep, ne,
                                                FAKE, FAKE, NULL, NULL, ws, n, NULL)
 
-    assert g(window=0) == 1 and g(window=-3) == 1
+    # window ends: null, empty, not increasing, a first end below 1, no end reaching K = 3
+    for bad in (None, (), (2, 2, 3), (2, 1, 3), (0, 3), (-1, 3), (1, 2)):
+        assert g(ends=bad) == 1, bad
+        assert s(ends=bad) == 1, bad
     assert g(target=NULL) == 1 and g(tokens=NULL) == 1 and g(out=NULL) == 1 and g(num=NULL) == 1
     assert g(dt=5) == 1 and g(B=0) == 1 and g(K=-1) == 1 and g(V=0) == 1
     assert g(B=5000) == 2 and g(target=FAKE_MIS) == 1
-    assert g(ws=NULL) == 3 and g(n=64) == 3
-    assert s(window=0) == 1
+    # valid ends reach the workspace check (entries after the first end >= K are ignored)
+    assert g(ws=NULL) == 3 and g(n=64) == 3 and g(ends=(3, 1, 0), ws=NULL) == 3 and g(ends=(9,), n=64) == 3
     assert s(target=NULL) == 1 and s(draft=NULL) == 1 and s(T=NULL) == 1
     assert s(ua=NULL) == 1 and s(us=NULL) == 1 and s(draft=FAKE_MIS) == 1
     assert s(B=0) == 1 and s(n=10) == 3

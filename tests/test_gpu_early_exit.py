@@ -33,11 +33,18 @@ def _setup():
     import draft_verification_verify_amd  # noqa: F401  (fails loudly if the library is missing)
 
 
+def _win(window):
+    """int: fixed windows of that many positions; list: window ends; None: the default."""
+    if isinstance(window, (list, tuple)):
+        return {"ends": list(window)}
+    return {"window": window}
+
+
 def run_ee_greedy(w, depth=None, window=4, tokens=None, target=None):
     import draft_verification_verify_amd as sv
     tok = w.tokens if tokens is None else tokens
     tgt = w.target if target is None else target
-    out, n = sv.verify_greedy_early_exit(dev(tgt), dev(tok), dev(depth), window=window)
+    out, n = sv.verify_greedy_early_exit(dev(tgt), dev(tok), dev(depth), **_win(window))
     torch.cuda.synchronize()
     return host(out), host(n)
 
@@ -45,7 +52,7 @@ def run_ee_greedy(w, depth=None, window=4, tokens=None, target=None):
 def run_ee_sample(w, depth=None, window=4):
     import draft_verification_verify_amd as sv
     out, n, p, q = sv.verify_sample_early_exit(dev(w.target), dev(w.draft), dev(w.tokens), dev(w.temperature),
-                                               dev(w.u_accept), dev(w.u_sample), dev(depth), window=window)
+                                               dev(w.u_accept), dev(w.u_sample), dev(depth), **_win(window))
     torch.cuda.synchronize()
     return host(out), host(n), host(p), host(q)
 
@@ -104,7 +111,7 @@ def test_ee_greedy_fuzz_shapes(dtype, V, K):
     depth = np.random.default_rng(V + 5 * K).integers(0, K + 1, B).astype(np.int32)
     ora = oracle.verify_early_exit(w.target, w.tokens, depth=depth)
     one_out, one_n = run_greedy(w, depth)
-    for window in (1, 2, 3, 16, 1000):
+    for window in (1, 2, 3, 16, 1000, None, [1, max(K, 1)], [2, 3, K + 4]):
         out, n = run_ee_greedy(w, depth, window)
         assert np.array_equal(n, ora["n"]) and np.array_equal(out, ora["out"]), (window, n, ora["n"])
         assert np.array_equal(n, one_n) and np.array_equal(out, one_out)
@@ -177,7 +184,7 @@ def test_ee_sample_fuzz_shapes(dtype, V, K):
     tal = Tally()
     for dep in (depth, None):
         ora = oracle_ee_sample(w, dep)
-        for window in (1, 3, 16):
+        for window in (1, 3, 16, None, [1, max(K, 1)], [2, 3, K + 4]):
             compare_ee_sample(w, run_ee_sample(w, dep, window), ora, dep, tal)
     tal.assert_ok(f"{dtype} V={V} K={K}")
 
@@ -231,7 +238,7 @@ def test_ee_sample_bad_inputs():
     tal.assert_ok("bad inputs")
 
 
-@pytest.mark.parametrize("window", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("window", [1, 2, 4, 8, 16, None, [1, 16], [2, 6, 16]])
 def test_ee_sample_full_size(window):
     note(f"early-exit sample dcut_ragged B=64 K=16 V=128000 bf16 T=1, window {window}")
     w = synth.dcut_ragged(0, T=1.0)
