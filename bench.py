@@ -51,8 +51,8 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "8a9a623218ee16b3a7781ff748039809c53d6ffe90c227913b822d216973d572",
-                    "fetch_bytes": 526028740, "write_bytes": 535102}
+ROW_PASS_TRAFFIC = {"source_sha256": "348a6c09a97b7e6b694e9f8703cc5461795908df2f38cb6baa69a7e31564b1bc",
+                    "fetch_bytes": 525245790, "write_bytes": 539456}
 
 
 def parse():
