@@ -386,7 +386,18 @@ def main():
         # the committed tokens are those of the one-pass step
         step(0)
         n_one = nacc.cpu().numpy().copy()
-        for ends in ([4, 16], [2, 6, 16], [1, 16], [8, 16], [4, 8, 12, 16]):
+        # the window ends planned from this batch's measured per-position
+        # acceptance (device counters -> spec_early_exit_plan, window cost
+        # 2.5 positions)
+        cnt = sv.accept_stats_update(nacc, K)
+        alpha = sv.accept_stats_summary(cnt, K)["alpha"]
+        planned = sv.early_exit_plan(alpha, 2.5)
+        schedules = [[4, 16], [2, 6, 16], [1, 16], [8, 16], [4, 8, 12, 16]]
+        if planned not in schedules:
+            schedules.append(planned)
+        sec["early_exit_planned_ends"] = {"ends": planned, "window_cost": 2.5,
+                                          "alpha": [round(a, 4) for a in alpha]}
+        for ends in schedules:
             def estep(i, ends=ends):
                 t, d = copies[i % ncopy]
                 sv.verify_sample_early_exit(t, d, tok, T, ua, us, ends=ends, out_tokens=out, num_accepted=nacc,

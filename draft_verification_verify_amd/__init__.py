@@ -76,6 +76,8 @@ def _load() -> ctypes.CDLL:
     L.spec_accept_stats_update.argtypes = [vp, vp, i32, i32, vp, vp]
     L.dcut_allocate.restype = ctypes.c_int
     L.dcut_allocate.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.spec_early_exit_plan.restype = ctypes.c_int
+    L.spec_early_exit_plan.argtypes = [vp, i32, ctypes.c_double, vp, vp]
     L.spec_verify_read_ceiling.restype = ctypes.c_int
     L.spec_verify_read_ceiling.argtypes = [vp, sz, vp, vp]
     L.spec_verify_timing_begin.restype = ctypes.c_int
@@ -94,7 +96,7 @@ EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
             "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
             "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit",
-            "spec_verify_read_ceiling")
+            "spec_verify_read_ceiling", "spec_early_exit_plan")
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
@@ -279,6 +281,22 @@ def window_ends(K: int, window=None, ends=None):
         return [W * i for i in range(1, max(1, -(-K // W)) + 1)]
     first = max(1, (K + 3) // 4)
     return [first, K] if first < K else [max(K, 1)]
+
+
+def early_exit_plan(alpha, window_cost: float = 2.5):
+    """Window ends minimising the expected cost for per-position acceptance
+    ``alpha`` (a sequence of K rates; NaN, a position no request reached,
+    counts as 0).  ``window_cost``: a window's fixed latency in units of
+    streaming one position of the batch."""
+    a = [0.0 if (x != x) else min(max(float(x), 0.0), 1.0) for x in alpha]
+    K = len(a)
+    arr = (ctypes.c_double * max(K, 1))(*a)
+    ends = (ctypes.c_int32 * max(K, 1))()
+    n = ctypes.c_int32(0)
+    st = lib.spec_early_exit_plan(ctypes.cast(arr, ctypes.c_void_p), K, float(window_cost),
+                                  ctypes.cast(ends, ctypes.c_void_p), ctypes.cast(ctypes.pointer(n), ctypes.c_void_p))
+    _raise("spec_early_exit_plan", st)
+    return [int(ends[i]) for i in range(n.value)]
 
 
 def _ends_arg(ends):

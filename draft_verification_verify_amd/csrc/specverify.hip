@@ -2901,6 +2901,44 @@ sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt, const int
     return launch(P, stream);
 }
 
+sv_status spec_early_exit_plan(const double *alpha, int32_t K, double window_cost, int32_t *ends,
+                               int32_t *n_windows)
+{
+    if (!ends || !n_windows || K < 0 || K > K_MAX || (K > 0 && !alpha)) return SV_ERR_INVALID_ARG;
+    if (!(window_cost >= 0.0) || window_cost > 1e30) return SV_ERR_INVALID_ARG;
+    for (int32_t k = 0; k < K; ++k)
+        if (!(alpha[k] >= 0.0 && alpha[k] <= 1.0)) return SV_ERR_INVALID_ARG;
+    if (K == 0) {
+        ends[0] = 1;
+        *n_windows = 1;
+        return SV_OK;
+    }
+    // live[p]: probability that a request still verifies position p
+    std::vector<double> live((size_t)K + 1), best((size_t)K + 1);
+    std::vector<int32_t> next((size_t)K + 1);
+    live[0] = 1.0;
+    for (int32_t p = 0; p < K; ++p) live[(size_t)p + 1] = live[(size_t)p] * alpha[p];
+    // best[p]: least expected cost of the windows covering positions p..K-1
+    best[(size_t)K] = 0.0;
+    for (int32_t p = K - 1; p >= 0; --p) {
+        double bc = 0.0;
+        int32_t bq = -1;
+        for (int32_t q = K; q > p; --q) {   // ties keep the longer window
+            const double c = window_cost + live[(size_t)p] * (double)(q - p) + best[(size_t)q];
+            if (bq < 0 || c < bc) {
+                bc = c;
+                bq = q;
+            }
+        }
+        best[(size_t)p] = bc;
+        next[(size_t)p] = bq;
+    }
+    int32_t n = 0;
+    for (int32_t p = 0; p < K; p = next[(size_t)p]) ends[n++] = next[(size_t)p];
+    *n_windows = n;
+    return SV_OK;
+}
+
 sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth, int32_t B, int32_t K,
                              const double *table_depth, const double *table_cost, int32_t table_n,
                              double max_verify, int32_t *depth_out, hipStream_t stream)

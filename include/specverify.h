@@ -213,6 +213,29 @@ sv_status spec_verify_sample_early_exit(const void *target_logits, const void *d
                                         float *p_draft, float *q_draft,
                                         void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Window ends for the early-exit calls from per-position acceptance rates
+ * (host computation; nothing is enqueued).  With live(p) = alpha[0] * ... *
+ * alpha[p-1] (live(0) = 1) the probability that a request still verifies
+ * position p, the plan minimises the expected cost
+ *     sum over its windows [lo, hi) of  window_cost + live(lo) * (hi - lo)
+ * over every list of ends, exactly (dynamic programming over the window
+ * starts, O(K^2)); among plans of equal cost the one with the longer
+ * window at each start wins.  The unit of cost is the time to stream one
+ * drafted position's rows for the whole batch, and window_cost is a window's
+ * fixed latency in that unit (on MI355X, about 13 us per window against
+ * about 5 us per position of a batch of 64 sampled requests at V = 128000
+ * in bf16: about 2.5).  alpha is what spec_accept_stats_update measures:
+ * per-position acceptance ([Hamidun], section "Comment fonctionne la voie
+ * MTP", reports these rates).
+ *   alpha       [K] double in [0, 1] (host), may be NULL when K = 0
+ *   window_cost finite, >= 0
+ *   ends        [max(K, 1)] int32 (host, out): the window ends, ready for
+ *               spec_verify_*_early_exit; n_windows (out): how many
+ *   Errors: SV_ERR_INVALID_ARG for a NULL output, K outside [0, 1024], an
+ *   alpha outside [0, 1] (NaN included) or a bad window_cost. */
+sv_status spec_early_exit_plan(const double *alpha, int32_t K, double window_cost, int32_t *ends,
+                               int32_t *n_windows);
+
 /* Draft confidence: conf[b,k] = max_v softmax(y_{b,k})_v at T = 1, the
  * per-position confidence whose running product is the prefix confidence
  * that drives D-cut ([Stack], section "What problem does it solve",
