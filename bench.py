@@ -311,6 +311,19 @@ def main():
                                        "pct_hbm_peak": 100 * gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                        "row_pass_ms": grp,
                                        "row_pass_GB_s": gbytes / (grp * 1e-3) / 1e9}
+        # the same greedy batch verified with early exit (default window ends)
+        gn_one = nacc.cpu().numpy().copy()
+        gends = sv.window_ends(K)
+
+        def gestep(i):
+            sv.verify_greedy_early_exit(gcopies[i % len(gcopies)], gtok, ends=gends, out_tokens=out,
+                                        num_accepted=nacc, workspace=ws, stream=stream)
+        _, geper, _ = timed(gestep, steps2, warm2)
+        gems = float(np.mean(geper))
+        sec["early_exit_greedy_ends_" + "_".join(map(str, gends)) + "_B64_K16"] = {
+            "rows_per_s": rows / (gems * 1e-3), "ms": gems, "vs_one_pass_ms": gms / gems,
+            "mean_accepted": float(nacc.float().mean().item()),
+            "same_num_accepted_as_one_pass": bool(np.array_equal(nacc.cpu().numpy(), gn_one))}
         del gcopies, gt
         # K=3 chat shape (B=4), sampled and greedy
         for mode in ("sample", "greedy"):

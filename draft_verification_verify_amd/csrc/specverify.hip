@@ -2070,39 +2070,35 @@ __device__ __forceinline__ float sanitize_conf(float c)
 // ---------------------------------------------------------------------------
 // Read ceiling (benchmark instrumentation): a plain stream over a buffer with
 // the row pass's load width and cache policy, every byte read once, against
-// which the row pass's bandwidth is compared.  A wave reads contiguous 4 KiB
-// blocks (UW 16-byte loads per lane, each load instruction 1 KiB), two blocks
-// in flight, handed out grid-stride; lanes fold what they read so the loads
-// stay live, and the fold reaches memory only in the unlikely case that it
-// equals a fixed value.
+// which the row pass's bandwidth is compared.  A workgroup reads 16 KiB
+// blocks, handed out grid-stride; each wave reads its 4 KiB quarter of a
+// block (UW 16-byte loads per lane, each load instruction 1 KiB).  Of the
+// shapes measured on MI355X (4 to 16 KiB per wave, per-wave or
+// per-workgroup blocks, 4 to 16 workgroups per CU, streaming or plain
+// loads) this one, at 16 workgroups per CU, was the fastest; the others
+// were within 2 % except plain loads (about 10 % slower).  Lanes fold what
+// they read so the loads stay live; the fold reaches memory only in the
+// unlikely case that it equals a fixed value.
 // ---------------------------------------------------------------------------
+
+constexpr int CEIL_WGS_PER_CU = 16;
 
 __global__ __launch_bounds__(WG) void read_ceiling_kernel(const uint4 *buf_, int64_t nvec, uint32_t *sink)
 {
     const gvec_t buf = (gvec_t)buf_;
-    const int64_t nwaves = (int64_t)gridDim.x * NWAVE;
-    const int64_t gw = (int64_t)blockIdx.x * NWAVE + wave_id();
-    const int lane = lane_id();
-    const int64_t nblk = nvec / WVEC;
+    const int64_t G = gridDim.x;
+    const int w = wave_id(), lane = lane_id();
+    const int64_t nblk = nvec / (NWAVE * WVEC);
     uint32_t acc = 0;
-    int64_t blk = gw;
-    for (; blk + nwaves < nblk; blk += 2 * nwaves) {
-        uint4 r0[UW], r1[UW];
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += G) {
+        uint4 r[UW];
 #pragma unroll
-        for (int j = 0; j < UW; ++j) r0[j] = ld_stream(buf + blk * WVEC + j * 64 + lane);
+        for (int j = 0; j < UW; ++j) r[j] = ld_stream(buf + blk * (NWAVE * WVEC) + (w * UW + j) * 64 + lane);
 #pragma unroll
-        for (int j = 0; j < UW; ++j) r1[j] = ld_stream(buf + (blk + nwaves) * WVEC + j * 64 + lane);
-#pragma unroll
-        for (int j = 0; j < UW; ++j) acc ^= r0[j].x ^ r0[j].y ^ r0[j].z ^ r0[j].w ^ r1[j].x ^ r1[j].y ^ r1[j].z ^ r1[j].w;
+        for (int j = 0; j < UW; ++j) acc ^= r[j].x ^ r[j].y ^ r[j].z ^ r[j].w;
     }
-    if (blk < nblk) {
-#pragma unroll
-        for (int j = 0; j < UW; ++j) {
-            const uint4 r = ld_stream(buf + blk * WVEC + j * 64 + lane);
-            acc ^= r.x ^ r.y ^ r.z ^ r.w;
-        }
-    }
-    for (int64_t v = nblk * WVEC + gw * 64 + lane; v < nvec; v += nwaves * 64) {
+    // the vectors after the last whole block
+    for (int64_t v = nblk * (NWAVE * WVEC) + (int64_t)blockIdx.x * WG + threadIdx.x; v < nvec; v += G * WG) {
         const uint4 r = ld_stream(buf + v);
         acc ^= r.x ^ r.y ^ r.z ^ r.w;
     }
@@ -2649,7 +2645,7 @@ extern "C" {
 sv_status spec_verify_read_ceiling(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream)
 {
     if (!buf || !sink || bytes < 16 || bytes % 16 != 0 || !aligned16(buf)) return SV_ERR_INVALID_ARG;
-    const int64_t grid = (int64_t)cu_count() * 8;
+    const int64_t grid = (int64_t)cu_count() * CEIL_WGS_PER_CU;
     (void)hipGetLastError();
     hipLaunchKernelGGL(read_ceiling_kernel, dim3((unsigned)grid), dim3(WG), 0, stream, (const uint4 *)buf,
                        (int64_t)(bytes / 16), sink);
