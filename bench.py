@@ -51,8 +51,8 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "348a6c09a97b7e6b694e9f8703cc5461795908df2f38cb6baa69a7e31564b1bc",
-                    "fetch_bytes": 525245790, "write_bytes": 539456}
+ROW_PASS_TRAFFIC = {"source_sha256": "1788431c2fa7a9b31ff944e6ef5a742d7415c2da2864f6827c3828a02b1d9685",
+                    "fetch_bytes": 525241640, "write_bytes": 536235}
 
 
 def parse():
