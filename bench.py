@@ -52,7 +52,10 @@ CALIB_KERNEL = "neg_kernel"
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
 ROW_PASS_TRAFFIC = {"source_sha256": "1788431c2fa7a9b31ff944e6ef5a742d7415c2da2864f6827c3828a02b1d9685",
-                    "fetch_bytes": 525241640, "write_bytes": 536235}
+                    "fetch_bytes": 525241640, "write_bytes": 536235,
+                    # SQ counters of the same source (one --pmc run of eight SQ counters):
+                    # VALU instructions and busy cycles per dispatch, summed over the device
+                    "sq_insts_valu": 30654851, "sq_busy_cycles": 5625106}
 
 
 def parse():
@@ -251,8 +254,13 @@ def main():
     del rbufs
     sha = source_sha256()
     traffic = None
+    valu_busy = None
     if ROW_PASS_TRAFFIC["source_sha256"] == sha and ROW_PASS_TRAFFIC["fetch_bytes"] is not None:
         traffic = float(ROW_PASS_TRAFFIC["fetch_bytes"] + ROW_PASS_TRAFFIC["write_bytes"])
+        # VALU-busy fraction: 4 cycles per wave64 instruction on each of the
+        # 1024 SIMDs, against the kernel's cycles (busy cycles summed over the
+        # 32 shader engines)
+        valu_busy = ROW_PASS_TRAFFIC["sq_insts_valu"] * 4.0 / (1024 * ROW_PASS_TRAFFIC["sq_busy_cycles"] / 32)
     result = {
         "metric": "verified logit rows/sec (B×(K+1) rows of V) + % of HBM peak, K=3 and K=16",
         "value": value,
@@ -281,7 +289,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ROW_PASS_KERNEL + "<bf16> (row statistics)",
                      "algorithmic_bytes_per_launch": rp_bytes,
-                     "avg_launch_ms": rp_ms},
+                     "avg_launch_ms": rp_ms, "valu_busy": valu_busy},
         "kernel_source_sha256": sha,
         "read_ceiling": {"GB_s": ceil_gbs, "ms": ceil_ms, "bytes": rp_bytes,
                          "row_pass_frac_of_ceiling": achieved / ceil_gbs,
@@ -302,7 +310,10 @@ def main():
         def gstep(i):
             sv.verify_greedy(gcopies[i % len(gcopies)], gtok, out_tokens=out, num_accepted=nacc, workspace=ws,
                              stream=stream)
-        _, gper, gst = timed(gstep, steps2, warm2, stages=True)
+        # the step without event markers, then again with the library's
+        # per-kernel events for the row pass's time
+        _, gper, _ = timed(gstep, steps2, warm2)
+        _, _, gst = timed(gstep, steps2, 2, stages=True)
         gms = float(np.mean(gper))
         gbytes = synth.algorithmic_bytes(wg, "greedy")
         grp = float(np.mean([s[0] for s in gst]))
