@@ -573,6 +573,10 @@ __device__ __forceinline__ bool temp_ok(float T)
     return T == 0.0f || (T >= 1e-6f && T <= 1e6f);   // excludes NaN, < 0, inf
 }
 
+// A readable word no kernel writes: the address an unused optional
+// argument's load goes to.
+__device__ int32_t k_stand_in = 0;
+
 struct ReqPlan {
     int d, kind, rows;
     float T;
@@ -583,25 +587,39 @@ struct ReqPlan {
 template <bool EE>
 __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
 {
+    // Every load first and unconditionally: an argument the call does not
+    // use is read from a valid stand-in address and its value discarded.
+    // (Loads issued under branches were each waited for at the branch's
+    // join, one after another.)
+    const int32_t *stand_in = &k_stand_in;
+    const int32_t *dp = P.mode == MODE_CONF ? (P.max_depth ? P.max_depth + b : stand_in)
+                                            : (P.depth ? P.depth + b : stand_in);
+    const float *tp = P.mode == MODE_SAMPLE ? P.temperature + b : (const float *)stand_in;
+    const int32_t *ap = (EE && P.win_lo > 0) ? P.alive_in + b : stand_in;
+    const int dv = *dp;
+    const float tv = *tp;
+    const int av = *ap;
+    const bool have_depth = P.mode == MODE_CONF ? P.max_depth != nullptr : P.depth != nullptr;
+
     ReqPlan q;
     q.T = 0.0f;
     q.lo = 0;
     q.fin = true;
     if (P.mode == MODE_CONF) {
-        q.d = P.max_depth ? P.max_depth[b] : P.K;
+        q.d = have_depth ? dv : P.K;
         const bool ok = q.d >= 0 && q.d <= P.K;
         q.kind = ok ? KIND_CONF : KIND_BAD;
         q.rows = ok ? q.d : 0;
     } else {
-        q.d = P.depth ? P.depth[b] : P.K;
-        q.T = (P.mode == MODE_SAMPLE) ? P.temperature[b] : 0.0f;
+        q.d = have_depth ? dv : P.K;
+        q.T = (P.mode == MODE_SAMPLE) ? tv : 0.0f;
         const bool ok = q.d >= 0 && q.d <= P.K && temp_ok(q.T);
         q.kind = !ok ? KIND_BAD : (q.T > 0.0f ? KIND_SAMPLED : KIND_GREEDY);
         if (q.kind == KIND_SAMPLED && P.dstats_in && q.T == 1.0f) q.kind = KIND_SAMPLED_R;
         q.rows = !ok ? 0 : (q.kind == KIND_SAMPLED ? 2 * q.d : q.kind == KIND_SAMPLED_R ? q.d : q.d + 1);
         if constexpr (EE) {
             q.lo = P.win_lo;
-            if (q.lo > 0 && !P.alive_in[b]) {
+            if (q.lo > 0 && !av) {
                 q.kind = KIND_DONE;
                 q.rows = 0;
             } else if (ok) {
@@ -1656,23 +1674,24 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     __builtin_amdgcn_s_setprio(3);
     // the request's plan and the row pass's chunking are read before the
     // table is built, so their loads overlap its arithmetic
+    const int cpr = P.ws.meta[0];
+    // the scan's inputs for positions lo..lo+63, issued with the plan's loads
+    // so their latencies overlap each other, the table and the merge; every
+    // wave loads them (no branch), from a stand-in where an argument is
+    // unused or absent, and only wave 0's are used
+    const int lo = EE ? P.win_lo : 0;
+    const int l = min(lo + lane_id(), max(P.K - 1, 0));
+    const bool has_tok = P.mode != MODE_CONF && P.K > 0;
+    const bool has_u = P.mode == MODE_SAMPLE && P.K > 0;
+    const int32_t *tokp = has_tok ? P.tokens + (int64_t)b * P.K + l : &k_stand_in;
+    const float *uap = has_u ? P.u_accept + (int64_t)b * P.K + l : (const float *)&k_stand_in;
+    const float *usp = P.mode == MODE_SAMPLE ? P.u_sample + b : (const float *)&k_stand_in;
+    const int x0 = *tokp;
+    const float ua0 = *uap, us0 = *usp;
     const ReqPlan q = plan_request<EE>(P, b);
     if (q.kind == KIND_DONE) {   // early-exit calls: ended in an earlier window
         if (c == 0 && tid == 0) P.alive_out[b] = 0;
         return;
-    }
-    const int cpr = P.ws.meta[0];
-    // the scan's inputs for positions lo..lo+63, loaded now so their latency
-    // overlaps the table and the merge
-    int x0 = 0;
-    float ua0 = 0.0f, us0 = 0.0f;
-    if (wave_id() == 0 && P.mode != MODE_CONF) {
-        const int l = q.lo + lane_id();
-        if (l < P.K) x0 = P.tokens[(int64_t)b * P.K + l];
-        if (P.mode == MODE_SAMPLE) {
-            if (l < P.K) ua0 = P.u_accept[(int64_t)b * P.K + l];
-            us0 = P.u_sample[b];
-        }
     }
     init_exp2_table(tab);
 
@@ -1857,9 +1876,12 @@ struct UnitPick {
 // Every wave of the draw workgroup, redundantly and with wave operations
 // only: the unit totals of the chosen distribution in unit order (lane-
 // strided, unit j = 64 h + lane), their total R, and the first unit whose
-// inclusive prefix exceeds u*R (else the last unit with mass).
+// inclusive prefix exceeds u*R (else the last unit with mass).  c0: the
+// lane's unit of the first 64 (j = lane), loaded by the caller ahead of
+// time; u: the draw uniform.
 template <bool BF16>
-__device__ UnitPick pick_unit(const Params &P, int b, const DrawRec &rec, const DrawRows<BF16> &dr, const double *tab)
+__device__ UnitPick pick_unit(const Params &P, int b, const DrawRec &rec, const DrawRows<BF16> &dr, const double *tab,
+                              const ChunkPart &c0, float u)
 {
     const int lane = lane_id();
     const ChunkPart *cp = P.ws.cp + (int64_t)b * P.cs;
@@ -1878,7 +1900,7 @@ __device__ UnitPick pick_unit(const Params &P, int b, const DrawRec &rec, const 
     for (int h = 0; h < H; ++h) {
         const int j = h * 64 + lane;
         if (j < ncs) {
-            const ChunkPart c = cp[j];
+            const ChunkPart c = h == 0 ? c0 : cp[j];
             lz += c.sz;
             ly += c.sy;
             lm = fmaxf(lm, c.m);
@@ -1894,7 +1916,7 @@ __device__ UnitPick pick_unit(const Params &P, int b, const DrawRec &rec, const 
         for (int h = 0; h < H; ++h) {
             const int j = h * 64 + lane;
             if (j < ncs) {
-                const ChunkPart c = cp[j];
+                const ChunkPart c = h == 0 ? c0 : cp[j];
                 lr += fmax(0.0, fma(rec.rho_hat - k.rho, c.bq, c.d));
             }
         }
@@ -1916,7 +1938,7 @@ __device__ UnitPick pick_unit(const Params &P, int b, const DrawRec &rec, const 
             const int j = h * 64 + lane;
             double t = 0.0;
             if (j < ncs) {
-                const ChunkPart c = cp[j];
+                const ChunkPart c = h == 0 ? c0 : cp[j];
                 if (resid) t = k.which == 0 ? fmax(0.0, fma(rec.rho_hat - k.rho, c.bq, c.d)) : c.sz;
                 else t = (c.m == -INFINITY || k.bad) ? 0.0 : c.sz * exp2_tab(((double)c.m - (double)k.Mb) * dr.cd, tab);
             }
@@ -1939,7 +1961,7 @@ __device__ UnitPick pick_unit(const Params &P, int b, const DrawRec &rec, const 
         if (pass == 0) {
             Rt = carry;
             if (!(Rt > 0.0)) k.bad = true;
-            k.target = (double)P.u_sample[b] * Rt;
+            k.target = (double)u * Rt;
         }
     }
     k.over = cand < 0;
@@ -1958,6 +1980,11 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
     __shared__ int sh_last[NWAVE];
     __shared__ int sh_first[NWAVE];
     const int b = blockIdx.x, w = wave_id(), lane = lane_id();
+    // the first 64 unit sums and the draw uniform are loaded with the record,
+    // so the three latencies overlap instead of following one another
+    // (clamped index, no branch: lanes past the units are never used)
+    const ChunkPart c0 = P.ws.cp[(int64_t)b * P.cs + min(lane, P.cs - 1)];
+    const float u0 = P.u_sample[b];
     const DrawRec rec = P.ws.rec[b];
     if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
     double *tab = tabs[w];
@@ -1965,7 +1992,7 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
     const bool resid = rec.state == SREQ_RESID;
     const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
     DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
-    const UnitPick k = pick_unit<BF16>(P, b, rec, dr, tab);
+    const UnitPick k = pick_unit<BF16>(P, b, rec, dr, tab, c0, u0);
     if (k.bad || k.cstar < 0) {   // the drawn row holds NaN, +inf or nothing but -inf
         if (w == 0) {
             const ReqDesc bd = {SREQ_BAD, 0, -1, rec.T};
