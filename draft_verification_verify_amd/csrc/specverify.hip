@@ -228,6 +228,7 @@ struct Params {
     // the requests still verifying (alive_in, read when win_lo > 0) and
     // records in alive_out which of them continue into the next window.
     int32_t ee;
+    int32_t ee_last;   // the call's last window: its finish kernel sums every drawn row pair
     int32_t win_lo, win_hi;
     const int32_t *alive_in;
     int32_t *alive_out;
@@ -1652,6 +1653,27 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
     return part;
 }
 
+// Early-exit calls, last window: the sampler units of a request that ended
+// in an earlier window, from the draw record that window wrote (workgroup
+// (c, b), unit 4c + wave, as in the finish kernel's unit part).
+template <bool BF16, bool ALIGNED>
+__device__ void units_from_record(const Params &P, int b, int c, double *tab)
+{
+    const DrawRec rec = P.ws.rec[b];
+    if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
+    // fp64 unit work: back to normal issue priority, so the merge and scan
+    // of the window's own requests are not held up
+    __builtin_amdgcn_s_setprio(0);
+    init_exp2_table(tab);
+    const int unit = c * NWAVE + wave_id();
+    if (unit >= P.cs) return;
+    const bool resid = rec.state == SREQ_RESID;
+    const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
+    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
+    const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rec.rho_hat, unit * unit_v<BF16>(), tab);
+    if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
+}
+
 // Workgroup (c, b):
 //  1. merges request b's row statistics from the row-pass partials (every
 //     workgroup of the request does this itself, so none waits on another);
@@ -1691,6 +1713,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     const ReqPlan q = plan_request<EE>(P, b);
     if (q.kind == KIND_DONE) {   // early-exit calls: ended in an earlier window
         if (c == 0 && tid == 0) P.alive_out[b] = 0;
+        if (EE && P.ee_last && P.mode == MODE_SAMPLE) units_from_record<BF16, ALIGNED>(P, b, c, tab);
         return;
     }
     init_exp2_table(tab);
@@ -1768,34 +1791,15 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
             P.ws.rec[b] = r;
         }
     }
-    // early-exit calls sum the drawn rows after the last window
-    if (!draw || EE) return;
+    // early-exit calls sum the drawn rows in the last window, for every
+    // request that draws, whichever window it ended in
+    if (!draw || (EE && !P.ee_last)) return;
     // this wave's unit of the drawn row pair (no workgroup barrier after here)
     const int unit = c * NWAVE + wave_id();
     if (unit >= P.cs) return;
     __builtin_amdgcn_s_setprio(0);
     const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, resid ? sz_row.m : 0.0f, resid ? sy_row.m : 0.0f);
     const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rho_hat, unit * unit_v<BF16>(), tab);
-    if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
-}
-
-// Early-exit calls: the sampler units of every request that draws, after the
-// last window, from the draw record the request's final window wrote (grid:
-// units / 4 by B, as the one-pass finish kernel's unit part).
-template <bool BF16, bool ALIGNED>
-__global__ __launch_bounds__(WG) void units_kernel(Params P)
-{
-    __shared__ double tab[EXP2_TAB];
-    const int b = blockIdx.y, c = blockIdx.x;
-    const DrawRec rec = P.ws.rec[b];
-    if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
-    init_exp2_table(tab);
-    const int unit = c * NWAVE + wave_id();
-    if (unit >= P.cs) return;
-    const bool resid = rec.state == SREQ_RESID;
-    const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
-    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
-    const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rec.rho_hat, unit * unit_v<BF16>(), tab);
     if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
 }
 
@@ -2560,7 +2564,7 @@ sv_status launch(Params &P, hipStream_t stream)
     grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div(rows_max * ceil_div(nv, WVEC), NWAVE)));
     const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1) + sizeof(float2) * (size_t)P.K;
     const bool sample = P.mode == MODE_SAMPLE;
-    const dim3 grid_b((unsigned)(sample && !P.ee ? ceil_div(P.cs, NWAVE) : 1), (unsigned)P.B);
+    const dim3 grid_b((unsigned)(sample && (!P.ee || P.ee_last) ? ceil_div(P.cs, NWAVE) : 1), (unsigned)P.B);
     const int tcall = (!P.ee && g_timing.used < g_timing.armed) ? g_timing.used++ : -1;
     (void)hipGetLastError();
 #define SV_MARK(s)                                                            \
@@ -2579,7 +2583,8 @@ sv_status launch(Params &P, hipStream_t stream)
             hipLaunchKernelGGL((finish_kernel<BF, AL, false>), grid_b, dim3(WG), lds_b, stream, P);           \
         }                                                                                                   \
         SV_MARK(2);                                                                                         \
-        if (sample && !P.ee) hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P); \
+        if (sample && (!P.ee || P.ee_last))                                                                 \
+            hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P);         \
         SV_MARK(3);                                                                                         \
     } while (0)
     if (P.bf16) {
@@ -2613,8 +2618,9 @@ bool window_plan(const int32_t *ends, int32_t n, int32_t K, std::vector<int> &ou
 
 // Early-exit verification: per window a row pass and a finish kernel
 // (merge, scan, outputs, draw record), back to back on the stream (the host
-// never waits); for sampled calls, after the last window, the sampler units
-// and the draw of every request that draws, whichever window it ended in.
+// never waits).  For sampled calls the last window's finish kernel also sums
+// the drawn row pair of every request that draws, whichever window it ended
+// in, and the draw kernel follows it.
 // Window w verifies positions [ends[w-1], ends[w]) (ends[-1] = 0) of the
 // requests that accepted every earlier position; the last window reaches K.
 // The still-verifying flags alternate between two arrays so that a window
@@ -2628,25 +2634,11 @@ sv_status launch_windows(Params &P, const std::vector<int> &ends, hipStream_t st
         P.win_hi = ends[(size_t)w];
         P.alive_in = P.ws.alive + (size_t)(w & 1) * (size_t)P.B;
         P.alive_out = P.ws.alive + (size_t)((w + 1) & 1) * (size_t)P.B;
+        P.ee_last = w == nwin - 1;
         const sv_status st = launch(P, stream);
         if (st != SV_OK) return st;
     }
-    if (P.mode != MODE_SAMPLE) return SV_OK;
-    const dim3 grid_u((unsigned)ceil_div(P.cs, NWAVE), (unsigned)P.B);
-#define SV_DRAW_PATH(BF, AL)                                                                          \
-    do {                                                                                              \
-        hipLaunchKernelGGL((units_kernel<BF, AL>), grid_u, dim3(WG), 0, stream, P);                   \
-        hipLaunchKernelGGL((draw_kernel<BF, AL>), dim3((unsigned)P.B), dim3(WG), 0, stream, P);       \
-    } while (0)
-    if (P.bf16) {
-        if (P.aligned) SV_DRAW_PATH(true, true);
-        else SV_DRAW_PATH(true, false);
-    } else {
-        if (P.aligned) SV_DRAW_PATH(false, true);
-        else SV_DRAW_PATH(false, false);
-    }
-#undef SV_DRAW_PATH
-    return hip_status("kernel launch");
+    return SV_OK;
 }
 
 Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const Layout &L, void *ws)
