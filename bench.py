@@ -8,16 +8,21 @@ D-cut workload at full depth: B=64 requests, K=16 drafted tokens, V=128000,
 bf16 logits, T=1, every request verified at depth 16 (B*(K+1) = 1088 verified
 target rows, 1024 draft rows).  Inputs are seeded synthetic logits already
 resident in HBM; input copies are rotated so the 256 MB memory-side cache
-cannot serve a step from the previous one.
+cannot serve a step from the previous one.  The K timed steps run back to
+back between two events on the launch stream (an event after every call
+would add about 2.5 us to each; the spread is taken in a separate pass).
 
 Printed: one JSON line with the verified-rows/s metric, the roofline of the
 dominant kernel (the row-statistics pass; its duration from HIP events that
 the library records on the launch stream around each kernel of every timed
 call), the oracle CPU baseline on a bounded sample, and secondary
 measurements (greedy, the K=3 chat shape, the D-cut pipeline, the mixed fp32
-batch).
+batch, early exit).
 
 Profiling helpers (run under rocprofv3; see the summaries under profiles/):
+    python bench.py --early-exit-ends 4,16
+                                          times only early-exit calls with those
+                                          window ends (for kernel traces)
     python bench.py --pmc-pass            a few headline steps, then a plain
                                           device copy of 512 MiB (counter
                                           calibration); prints the kernel names
@@ -62,7 +67,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
@@ -184,24 +189,34 @@ def main():
         sv.verify_sample(t, d, tok, T, ua, us, out_tokens=out, num_accepted=nacc, p_draft=pd,
                          q_draft=qd, workspace=ws, stream=stream)
 
-    def timed(fn, steps, warmup, stages=False):
+    def timed(fn, steps, warmup, stages=False, per_step=False):
         """Warm up, then time exactly `steps` calls between two events on the
-        launch stream (synchronised on both sides).  With `stages`, the library
-        also records its per-kernel events for every timed call."""
+        launch stream (synchronised on both sides), back to back; the mean
+        step is returned for every step.  With `per_step`, an event also
+        follows every call (about 2.5 us each on MI355X, so only for
+        percentiles).  With `stages`, the library also records its per-kernel
+        events for every timed call."""
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        n_ev = steps + 1 if per_step else 2
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         if stages:
             sv.timing_begin(steps)
         t0 = time.perf_counter()
         evs[0].record(stream)
         for i in range(steps):
             fn(i)
-            evs[i + 1].record(stream)
+            if per_step:
+                evs[i + 1].record(stream)
+        if not per_step:
+            evs[1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        if per_step:
+            per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        else:
+            per = [evs[0].elapsed_time(evs[1]) / steps] * steps
         st = sv.timing_end(steps) if stages else None
         return wall, per, st
 
@@ -231,6 +246,8 @@ def main():
 
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     wall, per, _ = timed(step, args.steps, args.warmup)
+    # the same steps with an event after each, for the spread only
+    _, per_ev, _ = timed(step, args.steps, 2, per_step=True)
     ms = float(np.mean(per))
     value = rows / (ms * 1e-3)
     # the same steps again with the library's per-kernel events armed (the
@@ -279,7 +296,9 @@ def main():
                    "global_batch": B, "K": K, "V": V, "rows_per_step": rows, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": 100.0 * algo_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": algo_bytes,
-        "ms_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
+        "ms_p10_p50_p90": [float(np.percentile(per_ev, q)) for q in (10, 50, 90)],
+        "ms_p10_p50_p90_note": "a second pass of the same steps with an event after each call "
+                               "(the events add about 2.5 us per step; ms_per_step has none)",
         "stage_ms": {"row_pass": rp_ms, "finish": float(stage_ms[1]), "draw": float(stage_ms[2]),
                      "step_with_events": float(np.mean(sper))},
         "wall_s_timed": wall,
