@@ -221,6 +221,7 @@ struct Params {
     int32_t mode;
     int32_t cpr_max;
     int32_t cs;        // sampler units per row (this call's dtype)
+    int32_t usplit;    // waves per sampler unit (1, 2 or 4)
     int32_t aligned;   // V * element size is a multiple of 16: every row starts 16-byte aligned
     int32_t row_cus;   // compute units the row-pass grid is spread over
     float row_skew;    // row pass: task-count slope across dispatch slots
@@ -1559,14 +1560,15 @@ __device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int b, cons
     return r;
 }
 
-// One wave's unit of the drawn row pair (vectors vu .. vu + UNIT_V - 1).
-// Residual draw: the sums d, bq, sz, sy (rho_hat from the row pass).  Bonus
-// draw: the unit's maximum and the sum of P relative to it (each lane keeps a
-// running maximum; the wave rescales to the unit's).
-template <bool BF16, bool ALIGNED>
+// One wave's run of the drawn row pair: NSTEP steps of NV vectors per lane
+// from vector vu (a whole unit by default, UNIT_V vectors).  Residual draw:
+// the sums d, bq, sz, sy (rho_hat from the row pass).  Bonus draw: the run's
+// maximum and the sum of P relative to it (each lane keeps a running
+// maximum; the wave rescales to the run's).
+template <bool BF16, bool ALIGNED, int NSTEP = SUB, int NV = sampler_nv<BF16>()>
 __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_hat, int vu, const double *tab)
 {
-    constexpr int EPV = RowView<BF16>::EPV, NV = sampler_nv<BF16>();
+    constexpr int EPV = RowView<BF16>::EPV;
     const int lane = lane_id();
     ChunkPart part;
     part.pad[0] = part.pad[1] = 0;
@@ -1575,14 +1577,14 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
         double dsum = 0.0, bq = 0.0, sz = 0.0, sy = 0.0;
         // every step's loads are issued before the first step's arithmetic, so
         // the second step's memory latency hides under the first's fp64 work
-        uint4 rz[SUB][NV], ry[SUB][NV];
+        uint4 rz[NSTEP][NV], ry[NSTEP][NV];
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) {
+        for (int u = 0; u < NSTEP; ++u) {
             issue_vecs<BF16, NV>(dr.rz, vu + u * NV * 64 + lane, 64, rz[u]);
             if (ALIGNED) issue_vecs<BF16, NV>(dr.dc.ry, vu + u * NV * 64 + lane, 64, ry[u]);
         }
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) {
+        for (int u = 0; u < NSTEP; ++u) {
             const int v0 = vu + u * NV * 64 + lane;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
@@ -1616,11 +1618,11 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
     } else {
         float m = -INFINITY;
         double s = 0.0;
-        uint4 rz[SUB][NV];
+        uint4 rz[NSTEP][NV];
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) issue_vecs<BF16, NV>(dr.rz, vu + u * NV * 64 + lane, 64, rz[u]);
+        for (int u = 0; u < NSTEP; ++u) issue_vecs<BF16, NV>(dr.rz, vu + u * NV * 64 + lane, 64, rz[u]);
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) {
+        for (int u = 0; u < NSTEP; ++u) {
             const int v0 = vu + u * NV * 64 + lane;
             float f[NV][EPV];
             float ml = -INFINITY;
@@ -1653,11 +1655,70 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
     return part;
 }
 
+// A unit's sums by S = P.usplit waves of one workgroup (S in {1, 2, 4}, a
+// divisor of the four waves): wave slot c * 4 + w takes part slot % S of unit
+// slot / S.  Small batches split their units so that more waves share the
+// fp64 work and the latency of one unit's pass shrinks.  The parts meet in
+// LDS: residual sums add; bonus parts rescale to the largest maximum.  Every
+// wave of the workgroup must call this (it holds a workgroup barrier when
+// S > 1); waves past the last unit contribute nothing.  Without SPLIT the
+// unit is wave slot c * 4 + w itself, S = 1, and the caller has already
+// retired the waves past the last unit.
+template <bool BF16, bool ALIGNED, bool SPLIT>
+__device__ void unit_sums_store(const Params &P, int b, int c, const DrawRows<BF16> &dr, bool resid, double rho_hat,
+                                const double *tab, ChunkPart *sh)
+{
+    constexpr int UV = unit_v<BF16>(), NV = sampler_nv<BF16>();
+    static_assert(SUB == 2 && NV % 2 == 0, "a unit splits into halves and quarters of its steps");
+    if constexpr (!SPLIT) {
+        const int unit = c * NWAVE + wave_id();
+        const ChunkPart pp = unit_sums<BF16, ALIGNED>(dr, resid, rho_hat, unit * UV, tab);
+        if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = pp;
+        return;
+    }
+    const int S = P.usplit, w = wave_id(), lane = lane_id();
+    const int slot = c * NWAVE + w, unit = slot / S, part = slot - unit * S;
+    const bool active = unit < P.cs;
+    ChunkPart pp = {};
+    if (active) {
+        const int vu = unit * UV + part * (UV / S);
+        if (S == 2) pp = unit_sums<BF16, ALIGNED, 1, NV>(dr, resid, rho_hat, vu, tab);
+        else pp = unit_sums<BF16, ALIGNED, 1, NV / 2>(dr, resid, rho_hat, vu, tab);
+    }
+    ChunkPart *dst = P.ws.cp + (int64_t)b * P.cs + unit;
+    if (lane == 0) sh[w] = pp;
+    __syncthreads();
+    if (!active || part != 0 || lane != 0) return;
+    ChunkPart t = sh[w];
+    for (int i = 1; i < S; ++i) {
+        const ChunkPart o = sh[w + i];
+        if (resid) {
+            t.d += o.d;
+            t.bq += o.bq;
+            t.sz += o.sz;
+            t.sy += o.sy;
+        } else {
+            t.bad |= o.bad;
+            if (o.m == -INFINITY) continue;
+            if (t.m == -INFINITY) {
+                t.m = o.m;
+                t.sz = o.sz;
+            } else if (o.m > t.m) {
+                t.sz = t.sz * exp2_tab(((double)t.m - (double)o.m) * dr.cd, tab) + o.sz;
+                t.m = o.m;
+            } else {
+                t.sz += o.sz * exp2_tab(((double)o.m - (double)t.m) * dr.cd, tab);
+            }
+        }
+    }
+    *dst = t;
+}
+
 // Early-exit calls, last window: the sampler units of a request that ended
 // in an earlier window, from the draw record that window wrote (workgroup
 // (c, b), unit 4c + wave, as in the finish kernel's unit part).
-template <bool BF16, bool ALIGNED>
-__device__ void units_from_record(const Params &P, int b, int c, double *tab)
+template <bool BF16, bool ALIGNED, bool SPLIT>
+__device__ void units_from_record(const Params &P, int b, int c, double *tab, ChunkPart *sh)
 {
     const DrawRec rec = P.ws.rec[b];
     if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
@@ -1665,13 +1726,11 @@ __device__ void units_from_record(const Params &P, int b, int c, double *tab)
     // of the window's own requests are not held up
     __builtin_amdgcn_s_setprio(0);
     init_exp2_table(tab);
-    const int unit = c * NWAVE + wave_id();
-    if (unit >= P.cs) return;
+    if (!SPLIT && c * NWAVE + wave_id() >= P.cs) return;
     const bool resid = rec.state == SREQ_RESID;
     const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
     const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
-    const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rec.rho_hat, unit * unit_v<BF16>(), tab);
-    if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
+    unit_sums_store<BF16, ALIGNED, SPLIT>(P, b, c, dr, resid, rec.rho_hat, tab, sh);
 }
 
 // Workgroup (c, b):
@@ -1682,12 +1741,13 @@ __device__ void units_from_record(const Params &P, int b, int c, double *tab)
 //     draw kernel) and the record the draw kernel reads;
 //  3. for a request that draws a token (sampled calls), each wave sums one
 //     unit of the drawn row pair in fp64 (unit 4c + wave).
-template <bool BF16, bool ALIGNED, bool EE>
+template <bool BF16, bool ALIGNED, bool EE, bool SPLIT>
 __global__ __launch_bounds__(WG) void finish_kernel(Params P)
 {
     extern __shared__ Stat rows_s[];   // [2K + 1] merged row statistics, then [K] (p, q) pairs
     __shared__ double tab[EXP2_TAB];
     __shared__ ReqDesc sh_desc;
+    __shared__ ChunkPart sh_parts[NWAVE];
     float2 *pq_s = (float2 *)(rows_s + 2 * P.K + 1);
     const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
     // The merge and the scan are a short latency chain that every unit of the
@@ -1713,7 +1773,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     const ReqPlan q = plan_request<EE>(P, b);
     if (q.kind == KIND_DONE) {   // early-exit calls: ended in an earlier window
         if (c == 0 && tid == 0) P.alive_out[b] = 0;
-        if (EE && P.ee_last && P.mode == MODE_SAMPLE) units_from_record<BF16, ALIGNED>(P, b, c, tab);
+        if (EE && P.ee_last && P.mode == MODE_SAMPLE) units_from_record<BF16, ALIGNED, SPLIT>(P, b, c, tab, sh_parts);
         return;
     }
     init_exp2_table(tab);
@@ -1794,13 +1854,11 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // early-exit calls sum the drawn rows in the last window, for every
     // request that draws, whichever window it ended in
     if (!draw || (EE && !P.ee_last)) return;
-    // this wave's unit of the drawn row pair (no workgroup barrier after here)
-    const int unit = c * NWAVE + wave_id();
-    if (unit >= P.cs) return;
+    // this wave's unit of the drawn row pair (SPLIT: its part of one)
+    if (!SPLIT && c * NWAVE + wave_id() >= P.cs) return;
     __builtin_amdgcn_s_setprio(0);
     const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, resid ? sz_row.m : 0.0f, resid ? sy_row.m : 0.0f);
-    const ChunkPart part = unit_sums<BF16, ALIGNED>(dr, resid, rho_hat, unit * unit_v<BF16>(), tab);
-    if (lane_id() == 0) P.ws.cp[(int64_t)b * P.cs + unit] = part;
+    unit_sums_store<BF16, ALIGNED, SPLIT>(P, b, c, dr, resid, rho_hat, tab, sh_parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -2564,7 +2622,9 @@ sv_status launch(Params &P, hipStream_t stream)
     grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div(rows_max * ceil_div(nv, WVEC), NWAVE)));
     const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1) + sizeof(float2) * (size_t)P.K;
     const bool sample = P.mode == MODE_SAMPLE;
-    const dim3 grid_b((unsigned)(sample && (!P.ee || P.ee_last) ? ceil_div(P.cs, NWAVE) : 1), (unsigned)P.B);
+    const bool split = sample && P.usplit > 1;
+    const dim3 grid_b((unsigned)(sample && (!P.ee || P.ee_last) ? ceil_div((int64_t)P.cs * P.usplit, NWAVE) : 1),
+                      (unsigned)P.B);
     const int tcall = (!P.ee && g_timing.used < g_timing.armed) ? g_timing.used++ : -1;
     (void)hipGetLastError();
 #define SV_MARK(s)                                                            \
@@ -2576,11 +2636,13 @@ sv_status launch(Params &P, hipStream_t stream)
         SV_MARK(0);                                                                                         \
         if (P.ee) {                                                                                         \
             hipLaunchKernelGGL((row_pass_kernel<BF, true>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
-            hipLaunchKernelGGL((finish_kernel<BF, AL, true>), grid_b, dim3(WG), lds_b, stream, P);            \
+            if (split) hipLaunchKernelGGL((finish_kernel<BF, AL, true, true>), grid_b, dim3(WG), lds_b, stream, P); \
+            else hipLaunchKernelGGL((finish_kernel<BF, AL, true, false>), grid_b, dim3(WG), lds_b, stream, P); \
         } else {                                                                                            \
             hipLaunchKernelGGL((row_pass_kernel<BF, false>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
             SV_MARK(1);                                                                                     \
-            hipLaunchKernelGGL((finish_kernel<BF, AL, false>), grid_b, dim3(WG), lds_b, stream, P);           \
+            if (split) hipLaunchKernelGGL((finish_kernel<BF, AL, false, true>), grid_b, dim3(WG), lds_b, stream, P); \
+            else hipLaunchKernelGGL((finish_kernel<BF, AL, false, false>), grid_b, dim3(WG), lds_b, stream, P); \
         }                                                                                                   \
         SV_MARK(2);                                                                                         \
         if (sample && (!P.ee || P.ee_last))                                                                 \
@@ -2654,6 +2716,10 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
     P.row_cus = cu_count();
     P.row_skew = mode == MODE_GREEDY ? ROW_SKEW_GREEDY : ROW_SKEW_LSE;
     P.cs = (int)ceil_div(nvec_max(V, P.bf16 ? 8 : 4), (int64_t)UNIT_E / (P.bf16 ? 8 : 4));
+    // A batch whose units would fill few wave slots splits each unit over two
+    // or four waves (measured on MI355X on the B = 4, K = 3 shape).
+    const int64_t units = (int64_t)B * P.cs;
+    P.usplit = units >= 2048 ? 1 : units >= 1024 ? 2 : 4;
     P.aligned = ((int64_t)V * (P.bf16 ? 2 : 4)) % 16 == 0;
     P.ws = carve(ws, L, B);
     return P;
