@@ -1418,6 +1418,8 @@ __device__ __forceinline__ Stat merge2(Stat a, Stat b, bool lse, double cs, cons
     return a;
 }
 
+constexpr int MERGE_LOADS = 4;   // row-pass partials loaded at once per merging thread
+
 // Merges the row-pass partials of request b's rows into rows_s (all threads;
 // tpr threads per row, each folding every tpr-th partial, then a butterfly
 // over the tpr lanes).  Every workgroup of a request performs the same
@@ -1434,8 +1436,17 @@ __device__ void merge_rows(const Params &P, int pre, int rows, int cpr, bool lse
         const int r = g0 + tid / tpr, l = tid & (tpr - 1);
         Stat acc = ident;
         if (r < rows) {
+            // MERGE_LOADS partials in flight per thread (clamped index, no
+            // branch), then folded in chunk order j = l, l + tpr, ...
             const Stat *pp = P.ws.part + (int64_t)(pre + r) * P.cpr_max;
-            for (int j = l; j < cpr; j += tpr) acc = merge2(acc, pp[j], lse, cs, tab);
+            for (int j0 = l; j0 < cpr; j0 += MERGE_LOADS * tpr) {
+                Stat v[MERGE_LOADS];
+#pragma unroll
+                for (int i = 0; i < MERGE_LOADS; ++i) v[i] = pp[min(j0 + i * tpr, cpr - 1)];
+#pragma unroll
+                for (int i = 0; i < MERGE_LOADS; ++i)
+                    if (j0 + i * tpr < cpr) acc = merge2(acc, v[i], lse, cs, tab);
+            }
         }
         // butterfly over the tpr lanes of the row (levels with 2^L < tpr;
         // every workgroup of the request runs the same sequence)
