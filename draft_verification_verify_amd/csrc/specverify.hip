@@ -572,7 +572,7 @@ __device__ __forceinline__ double exp2_tab(double x, const double *tab) { return
 
 __device__ __forceinline__ bool temp_ok(float T)
 {
-    return T == 0.0f || (T >= 1e-6f && T <= 1e6f);   // excludes NaN, < 0, inf
+    return T == 0.0f || (T > 0.0f && T <= 3.40282347e38f);   // excludes NaN, < 0, inf
 }
 
 // A readable word no kernel writes: the address an unused optional
@@ -805,27 +805,76 @@ __device__ __forceinline__ void argmax_batch(const RowView<BF16> &rv, int vbeg, 
     }
 }
 
+// Exponent scale of a row's log-sum-exp statistics.  Every exponent of the
+// row statistics and of the accept test is (v - M) * c with c = c32 * 2^sh:
+// c32 = fl(log2(e)/T), which differs from log2(e)/T by at most 6e-8
+// relative, and sh = 0; only when log2(e)/T exceeds 2^100 (T below about
+// 1.1e-30, down to the smallest positive fp32 value) is c32 the rounded
+// quotient times 2^-64 and sh = 64, so that c32 stays a finite fp32 number
+// for every finite T > 0.
+struct LseScale {
+    float c32;
+    int sh;   // 0 or 64
+};
+
+constexpr double SCALE_SHIFT_AT = 0x1p100;
+
+__device__ __forceinline__ LseScale scale_of(int kind, float T)
+{
+    const double c = LOG2E / (double)(kind == KIND_CONF ? 1.0f : T);
+    LseScale sc;
+    sc.sh = c > SCALE_SHIFT_AT ? 64 : 0;
+    sc.c32 = (float)(sc.sh ? c * 0x1p-64 : c);
+    return sc;
+}
+
+// The scale as a double, exactly c32 * 2^sh.
+__device__ __forceinline__ double scale_d(const LseScale &sc) { return sc.sh ? (double)sc.c32 * 0x1p64 : (double)sc.c32; }
+
+// fp32 exponent d * c for a difference d = v - M <= 0 (rounded twice at
+// most; a product past the fp32 range is -inf, whose exp2 is the exact 0).
+__device__ __forceinline__ float scaled_exp(float d, const LseScale &sc)
+{
+    return sc.sh ? (d * 0x1p64f) * sc.c32 : d * sc.c32;
+}
+
+// 2^-dl for the residual dl of an fp32 product (|dl| <= 64): the second-order
+// series where its truncation (below 2e-16 relative) vanishes in double, the
+// fp64 exp2 otherwise.
+__device__ __forceinline__ double offset_factor(float dl)
+{
+    if (__builtin_fabsf(dl) <= 0x1p-16f) {
+        const double x = (double)dl * LN2;
+        return 1.0 - x + 0.5 * x * x;
+    }
+    return exp2(-(double)dl);
+}
+
 // Sampled / confidence rows: the lane's running max M and
-// s = sum exp2((v - M) * c32) with c32 = fl(log2(e)/T) (every exponent of the
-// row statistics and of the accept test uses this same fp32 scale, which
-// differs from log2(e)/T by at most 6e-8 relative), s kept in double.  Each
-// term's exponent is one FMA, v*c32 - fl(M*c32); the constant offset
-// delta = M*c32 - fl(M*c32) is exact (FMA residual) and is taken out of every
-// batch sum by the factor 2^-delta = 1 - delta*ln2 + (delta*ln2)^2/2 (|delta|
-// is below 1e-5, so the series is exact in double).  When a batch raises M,
-// s is rescaled once by 2^((M_old - M_new)*c32) (fp32 exp2, within 2 ulp).
-// Terms are summed in fp32 per vector (a short tree) and the vector sums in
-// a second short tree.
+// s = sum 2^((v - M) * c) (scale as above), s kept in double.  Terms are
+// summed in fp32 per vector (a short tree) and the vector sums in a second
+// short tree.  Two ways to form each term's exponent:
+//  * the FMA form (the normal case): one FMA, v*c32 - fl(M*c32).  The
+//    offset dl = M*c32 - fl(M*c32) is exact (the FMA residual of the
+//    product) and is taken out of every batch sum by the factor 2^-dl
+//    (offset_factor), computed when M changes.  It needs sh = 0 and
+//    |fl(M*c32)| < 2^31, so that |dl| <= 64 keeps every term inside the fp32
+//    range;
+//  * the difference form: (v - M) * c, two operations, valid for every
+//    finite M and every scale.  A wave takes it for a batch when any of its
+//    lanes is outside the FMA form's range (very large |M| / T).
+// When a batch raises M, s is rescaled once by 2^((M_old - M_new) * c)
+// (fp32 exp2, within 2 ulp).
 struct LseLane {
     float M = -INFINITY;
     float mc = 0.0f;      // fl(M*c32)
-    double corr = 1.0;    // 2^-delta
+    double corr = 1.0;    // 2^-dl
     double s = 0.0;
 };
 
 template <bool BF16, bool EDGE>
-__device__ __forceinline__ void lse_batch(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW], float c32,
-                                          LseLane &st)
+__device__ __forceinline__ void lse_batch(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW],
+                                          const LseScale &sc, LseLane &st)
 {
     constexpr int EPV = RowView<BF16>::EPV;
     const int lane = lane_id();
@@ -838,11 +887,10 @@ __device__ __forceinline__ void lse_batch(const RowView<BF16> &rv, int vbeg, con
         for (int e = 0; e < EPV; ++e) bm = fmaxf(bm, f[e]);
     }
     if (bm > st.M) {
-        if (st.M != -INFINITY) st.s *= (double)__builtin_amdgcn_exp2f((st.M - bm) * c32);
+        if (st.M != -INFINITY) st.s *= (double)__builtin_amdgcn_exp2f(scaled_exp(st.M - bm, sc));
         st.M = bm;
-        st.mc = bm * c32;
-        const double dl = (double)__builtin_fmaf(bm, c32, -st.mc) * LN2;
-        st.corr = 1.0 - dl + 0.5 * dl * dl;
+        st.mc = bm * sc.c32;
+        st.corr = offset_factor(__builtin_fmaf(bm, sc.c32, -st.mc));
     }
     if (st.M == -INFINITY) {
         // nothing but -inf / masked so far; a NaN must still poison the sum
@@ -857,45 +905,57 @@ __device__ __forceinline__ void lse_batch(const RowView<BF16> &rv, int vbeg, con
         if (un) st.s = NAN;
         return;
     }
+    const bool diff_form = sc.sh != 0 || __ballot(!(__builtin_fabsf(st.mc) < 0x1p31f)) != 0;
     float vs[UW];
+    if (!diff_form) {
 #pragma unroll
-    for (int j = 0; j < UW; ++j) {
-        float f[EPV];
-        widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
-        float t[EPV];
+        for (int j = 0; j < UW; ++j) {
+            float f[EPV];
+            widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
+            float t[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c32, -st.mc));
+            for (int e = 0; e < EPV; ++e) t[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.c32, -st.mc));
 #pragma unroll
-        for (int w = EPV / 2; w > 0; w >>= 1)
+            for (int w = EPV / 2; w > 0; w >>= 1)
 #pragma unroll
-            for (int e = 0; e < w; ++e) t[e] += t[e + w];
-        vs[j] = t[0];
+                for (int e = 0; e < w; ++e) t[e] += t[e + w];
+            vs[j] = t[0];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < UW; ++j) {
+            float f[EPV];
+            widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
+            float t[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) t[e] = __builtin_amdgcn_exp2f(scaled_exp(f[e] - st.M, sc));
+#pragma unroll
+            for (int w = EPV / 2; w > 0; w >>= 1)
+#pragma unroll
+                for (int e = 0; e < w; ++e) t[e] += t[e + w];
+            vs[j] = t[0];
+        }
     }
 #pragma unroll
     for (int w = UW / 2; w > 0; w >>= 1)
 #pragma unroll
         for (int j = 0; j < w; ++j) vs[j] += vs[j + w];
-    st.s += (double)vs[0] * st.corr;
+    st.s += diff_form ? (double)vs[0] : (double)vs[0] * st.corr;
 }
 
 template <bool BF16, bool LSE, typename State>
-__device__ __forceinline__ void process_batch(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW], float c32,
-                                              State &st)
+__device__ __forceinline__ void process_batch(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW],
+                                              const LseScale &sc, State &st)
 {
     if constexpr (LSE) {
-        if (rv.batch_edge(vbeg, WVEC)) lse_batch<BF16, true>(rv, vbeg, raw, c32, st);
-        else lse_batch<BF16, false>(rv, vbeg, raw, c32, st);
+        if (rv.batch_edge(vbeg, WVEC)) lse_batch<BF16, true>(rv, vbeg, raw, sc, st);
+        else lse_batch<BF16, false>(rv, vbeg, raw, sc, st);
     } else {
         if (rv.batch_edge(vbeg, WVEC)) argmax_batch<BF16, true>(rv, vbeg, raw, st);
         else argmax_batch<BF16, false>(rv, vbeg, raw, st);
     }
 }
 
-// Exponent scale of a row's log-sum-exp statistics.
-__device__ __forceinline__ float c32_of(int kind, float T)
-{
-    return (float)(LOG2E / (double)(kind == KIND_CONF ? 1.0f : T));
-}
 
 // One chunk of one row: its row view and the end b1 of the batches
 // [c * nb, b1) it covers.  A chunk past the end of a short row (rows whose
@@ -909,9 +969,9 @@ struct Task {
     int slot;      // partial slot row: request * (2K + 1) + row within the request
     int k;         // the wave's round of this task
     uint32_t pre;  // first task index of round k
-    float c32;     // log-sum-exp scale; 0 marks a greedy (argmax) row
+    LseScale sc;   // log-sum-exp scale; c32 = 0 marks a greedy (argmax) row
     float zx;      // sampled rows: the row's logit at the drafted token
-    __device__ __forceinline__ bool lse() const { return c32 != 0.0f; }
+    __device__ __forceinline__ bool lse() const { return sc.c32 != 0.0f; }
     __device__ __forceinline__ RowView<BF16> view(int V) const
     {
         RowView<BF16> rv;
@@ -964,7 +1024,14 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     else if (kind == KIND_SAMPLED_R) { is_draft = false; kk = local; lse = true; }
     else { is_draft = true; kk = local; lse = true; }   // KIND_CONF
     if constexpr (EE) kk += P.win_lo;   // the window's first position
-    k.c32 = lse ? c32_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b])))) : 0.0f;
+    if (lse) {
+        k.sc = scale_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b]))));
+        k.sc.c32 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(k.sc.c32)));
+        k.sc.sh = __builtin_amdgcn_readfirstlane(k.sc.sh);
+    } else {
+        k.sc.c32 = 0.0f;
+        k.sc.sh = 0;
+    }
     const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
     const char *row_start = (const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4);
     const RowView<BF16> rv(row_start, P.V);
@@ -987,7 +1054,7 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     return k;
 }
 
-__device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, const LseLane &ls, float c32)
+__device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, const LseLane &ls, const LseScale &sc)
 {
     Stat st;
     if (!lse) {
@@ -1001,7 +1068,7 @@ __device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, cons
     } else {
         const float M = wave_max(ls.M);
         double sl = 0.0;
-        if (ls.M != -INFINITY) sl = ls.s * (double)__builtin_amdgcn_exp2f((ls.M - M) * c32);
+        if (ls.M != -INFINITY) sl = ls.s * (double)__builtin_amdgcn_exp2f(scaled_exp(ls.M - M, sc));
         else if (ls.s != ls.s) sl = ls.s;
         st.m = M;
         st.idx = 0;
@@ -1015,7 +1082,7 @@ __device__ __forceinline__ Stat finish_task(bool lse, const ArgmaxLane &am, cons
 template <bool BF16>
 __device__ __forceinline__ Stat finish_task(const Task<BF16> &k, const ArgmaxLane &am, const LseLane &ls)
 {
-    Stat st = finish_task(k.lse(), am, ls, k.c32);
+    Stat st = finish_task(k.lse(), am, ls, k.sc);
     if (k.lse()) st.idx = __float_as_int(k.zx);
     return st;
 }
@@ -1032,8 +1099,8 @@ template <bool BF16>
 __device__ __forceinline__ void consume(const Params &P, const Task<BF16> &k, int i, const uint4 (&raw)[UW],
                                         ArgmaxLane &am, LseLane &ls)
 {
-    if (k.lse()) process_batch<BF16, true>(k.view(P.V), i * WVEC, raw, k.c32, ls);
-    else process_batch<BF16, false>(k.view(P.V), i * WVEC, raw, 0.0f, am);
+    if (k.lse()) process_batch<BF16, true>(k.view(P.V), i * WVEC, raw, k.sc, ls);
+    else process_batch<BF16, false>(k.view(P.V), i * WVEC, raw, k.sc, am);
     Stat st;
     if (i + 1 >= k.b1) {
         st = finish_task<BF16>(k, am, ls);
@@ -1234,10 +1301,10 @@ __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const 
 
     // Sampled request (T > 0): accept k iff u_k < min(1, p_k(x)/q_k(x)), in
     // double from the row statistics and the two logits at x, with the same
-    // exponent scale c32 as the statistics.
+    // exponent scale as the statistics.
     int bad = unif_ok(us0) ? 0 : 1;
     int n = d;
-    const double c2 = (double)c32_of(q.kind, q.T);
+    const double c2 = scale_d(scale_of(q.kind, q.T));
     for (int k0 = 0; k0 < d; k0 += 64) {
         const int k = k0 + lane;
         const bool active = k < d;
@@ -1308,7 +1375,7 @@ __device__ ReqDesc scan_window(const Params &P, int b, const ReqPlan &q, const S
     if (q.kind == KIND_BAD) return desc;
     if (q.kind == KIND_DONE) return {SREQ_DONE, 0, -1, q.T};
     const bool greedy = q.kind == KIND_GREEDY;
-    const double c2 = greedy ? 0.0 : (double)c32_of(q.kind, q.T);
+    const double c2 = greedy ? 0.0 : scale_d(scale_of(q.kind, q.T));
     int stop = nd;          // first position (relative) that rejects or is bad
     bool stop_bad = false;
     for (int k0 = 0; k0 < nd; k0 += 64) {
@@ -1542,12 +1609,23 @@ __device__ __forceinline__ void draft_vec(const DraftChunk<BF16> &dc, const RowV
 
 // Drawn row pair of a request: target row n (and draft row n for a residual
 // draw), with the exponent constants of P = 2^((z - Mz) cd), Q = 2^((y - My) cd).
+// Two forms of the exponent, used alike by the unit sums and the rescan:
+//  * z * cd - fl(Mz * cd) (one FMA): the rounding of fl(Mz * cd) is one
+//    offset common to every term of the row, which cancels between the row's
+//    terms and its sum; it stays negligible next to the row pass's estimate
+//    of Sz/Sy while |Mz cd|, |My cd| < 2^28;
+//  * (z - Mz) * cd (exact): the difference of two widened fp32 values is exact
+//    in double wherever the term is not vanishingly small.  Taken when either
+//    |M cd| reaches 2^28 (very large |M| / T), and always for a bonus draw,
+//    whose unit sums offset each lane by its own running maximum.
 template <bool BF16>
 struct DrawRows {
     RowView<BF16> rz;
     DraftChunk<BF16> dc;
     double cd, mzc, myc;     // log2(e)/T and the row maxima times it
     double cd5, mzc5, myc5;  // the same times 512 (arguments of exp2_512)
+    double mz, my;           // the row maxima
+    bool exact;              // exact-difference exponents
     __device__ void scale()
     {
         cd5 = cd * EXP2_TAB;
@@ -1555,6 +1633,15 @@ struct DrawRows {
         myc5 = myc * EXP2_TAB;
     }
 };
+
+constexpr double EXACT_EXP_AT = 0x1p28;
+
+template <bool EXACT>
+__device__ __forceinline__ double draw_exp_arg(float v, double m, double mc5, double cd5)
+{
+    if constexpr (EXACT) return ((double)v - m) * cd5;
+    else return fma((double)v, cd5, -mc5);
+}
 
 template <bool BF16>
 __device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int b, const ReqDesc &desc, float Mz, float My)
@@ -1565,10 +1652,47 @@ __device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int b, cons
     r.dc.yrow = (const char *)P.draft + ((int64_t)b * P.K + desc.n) * P.V * esz;
     r.dc.ry = RowView<BF16>(r.dc.yrow, P.V);
     r.cd = LOG2E / (double)desc.T;
-    r.mzc = (double)Mz * r.cd;
-    r.myc = (double)My * r.cd;
+    r.mz = (double)Mz;
+    r.my = (double)My;
+    r.mzc = r.mz * r.cd;
+    r.myc = r.my * r.cd;
+    r.exact = __builtin_fmax(__builtin_fabs(r.mzc), __builtin_fabs(r.myc)) >= EXACT_EXP_AT;
     r.scale();
     return r;
+}
+
+// Residual sums over a wave's run (loads already issued into rz / ry).
+template <bool BF16, bool ALIGNED, bool EXACT, int NSTEP, int NV>
+__device__ __forceinline__ void resid_terms(const DrawRows<BF16> &dr, double rho_hat, int vu, const double *tab,
+                                            const uint4 (&rz)[NSTEP][NV], const uint4 (&ry)[NSTEP][NV], int &flag,
+                                            double &dsum, double &bq, double &sz, double &sy)
+{
+    constexpr int EPV = RowView<BF16>::EPV;
+    const int lane = lane_id();
+#pragma unroll
+    for (int u = 0; u < NSTEP; ++u) {
+        const int v0 = vu + u * NV * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int vi = v0 + j * 64;
+            float f[EPV], g[EPV];
+            // one vector at a time: unbounded interleaving of the fp64
+            // exponentials would cost occupancy
+            __builtin_amdgcn_sched_barrier(0);
+            chunk_vec<BF16, ALIGNED>(dr.rz, vi, rz[u][j], f, flag);
+            draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry[u][j], g);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const double p = exp2_512(draw_exp_arg<EXACT>(f[e], dr.mz, dr.mzc5, dr.cd5), tab);
+                const double q = exp2_512(draw_exp_arg<EXACT>(g[e], dr.my, dr.myc5, dr.cd5), tab);
+                sz += p;
+                sy += q;
+                const double t = fma(-rho_hat, q, p);
+                dsum += __builtin_fmax(t, 0.0);
+                bq += (t > 0.0) ? q : 0.0;
+            }
+        }
+    }
 }
 
 // One wave's run of the drawn row pair: NSTEP steps of NV vectors per lane
@@ -1594,32 +1718,8 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
             issue_vecs<BF16, NV>(dr.rz, vu + u * NV * 64 + lane, 64, rz[u]);
             if (ALIGNED) issue_vecs<BF16, NV>(dr.dc.ry, vu + u * NV * 64 + lane, 64, ry[u]);
         }
-#pragma unroll
-        for (int u = 0; u < NSTEP; ++u) {
-            const int v0 = vu + u * NV * 64 + lane;
-#pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const int vi = v0 + j * 64;
-                float f[EPV], g[EPV];
-                // one vector at a time: unbounded interleaving of the fp64
-                // exponentials would cost occupancy
-                __builtin_amdgcn_sched_barrier(0);
-                // the 64 vectors of this slot lie inside the row except near
-                // its ends (uniform test; the masking selects are skipped)
-                chunk_vec<BF16, ALIGNED>(dr.rz, vi, rz[u][j], f, flag);
-                draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry[u][j], g);
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const double p = exp2_512(fma((double)f[e], dr.cd5, -dr.mzc5), tab);
-                    const double q = exp2_512(fma((double)g[e], dr.cd5, -dr.myc5), tab);
-                    sz += p;
-                    sy += q;
-                    const double t = fma(-rho_hat, q, p);
-                    dsum += __builtin_fmax(t, 0.0);
-                    bq += (t > 0.0) ? q : 0.0;
-                }
-            }
-        }
+        if (dr.exact) resid_terms<BF16, ALIGNED, true, NSTEP, NV>(dr, rho_hat, vu, tab, rz, ry, flag, dsum, bq, sz, sy);
+        else resid_terms<BF16, ALIGNED, false, NSTEP, NV>(dr, rho_hat, vu, tab, rz, ry, flag, dsum, bq, sz, sy);
         part.d = wave_sum(dsum);
         part.bq = wave_sum(bq);
         part.sz = wave_sum(sz);
@@ -1648,11 +1748,11 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
                 m = ml;
             }
             if (m != -INFINITY && m != INFINITY) {
-                const double mc5 = (double)m * dr.cd5;
+                const double md = (double)m;
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) s += exp2_512(fma((double)f[j][e], dr.cd5, -mc5), tab);
+                    for (int e = 0; e < EPV; ++e) s += exp2_512(draw_exp_arg<true>(f[j][e], md, 0.0, dr.cd5), tab);
             }
         }
         const float M = wave_max(m);
@@ -1806,7 +1906,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
             rows_s[q.d + k] = st;
         }
     }
-    merge_rows(P, pre, q.rows, cpr, lse, lse ? (double)c32_of(q.kind, q.T) : 0.0, tab, rows_s);
+    merge_rows(P, pre, q.rows, cpr, lse, lse ? scale_d(scale_of(q.kind, q.T)) : 0.0, tab, rows_s);
 
     if (P.mode == MODE_CONF) {
         for (int k = tid; k < P.K; k += WG) {
@@ -1902,9 +2002,11 @@ __device__ __forceinline__ void slot_terms(const DrawRows<BF16> &dr, int which, 
     if (which == 0) draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry, g);
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-        const double p = exp2_512(fma((double)f[e], dr.cd5, -dr.mzc5), tab);
+        const double p = exp2_512(dr.exact ? draw_exp_arg<true>(f[e], dr.mz, dr.mzc5, dr.cd5)
+                                           : draw_exp_arg<false>(f[e], dr.mz, dr.mzc5, dr.cd5), tab);
         if (which == 0) {
-            const double q = exp2_512(fma((double)g[e], dr.cd5, -dr.myc5), tab);
+            const double q = exp2_512(dr.exact ? draw_exp_arg<true>(g[e], dr.my, dr.myc5, dr.cd5)
+                                               : draw_exp_arg<false>(g[e], dr.my, dr.myc5, dr.cd5), tab);
             const double t = fma(-rho, q, p);
             val[e] = t > 0.0 ? t : 0.0;
         } else {
@@ -2074,7 +2176,11 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
         return;
     }
     if (!resid) {
-        dr.mzc = (double)k.Mb * dr.cd;
+        // the bonus rescan offsets by the row maximum, in the exact form (as
+        // the unit sums it is compared with)
+        dr.mz = (double)k.Mb;
+        dr.mzc = dr.mz * dr.cd;
+        dr.exact = true;
         dr.scale();
     }
     const int wsel = resid ? k.which : 1;

@@ -42,8 +42,8 @@
  *     alignment, workspace size, budget) are rejected with a status before
  *     anything is enqueued.  Bad DATA is found on the device and reported per
  *     request as num_accepted[b] = -1 with out_tokens[b, :] = -1: a depth
- *     outside [0, K], a temperature that is not 0 and not a number in
- *     [1e-6, 1e6] (so NaN, negatives and infinities), a drafted token outside
+ *     outside [0, K], a temperature that is neither 0 nor a finite number
+ *     above 0 (so NaN, negatives and infinities), a drafted token outside
  *     [0, V), a uniform outside [0, 1), or a row that is read and holds a NaN
  *     or +inf, or only -inf.  -inf logits (masked tokens) are allowed
  *     otherwise.  No C++ exception crosses this interface.
@@ -154,7 +154,8 @@ sv_status spec_verify_greedy(const void *target_logits, sv_dtype dt,
  *   "Qu'est-ce que le speculative decoding"; [Remio], section "Cosa non
  *   dimostrano i numeri di AngelSpec").
  *   draft_logits  [B, K, V] of dt (read: rows 0..d-1 of requests with T > 0)
- *   temperature   [B] float: 0 (greedy rule) or in [1e-6, 1e6]
+ *   temperature   [B] float: 0 (greedy rule) or any finite T > 0 (fp32
+ *     denormals included)
  *   u_accept      [B, K] float in [0, 1);  u_sample [B] float in [0, 1)
  *   p_draft, q_draft  [B, K] float or NULL  out: p_k(x_k), q_k(x_k) for every
  *     k < d of requests with T > 0; 0 elsewhere.

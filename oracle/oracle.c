@@ -247,10 +247,12 @@ int oracle_verify_greedy(const void *target, int dtype, const int32_t *tokens,
 
 static int bad_uniform(float u) { return !(u >= 0.0f && u < 1.0f); }
 
-/* Temperatures the contract accepts: 0 (the greedy rule) or a finite value in
- * [1e-6, 1e6]; NaN, negatives, infinities and values in (0, 1e-6) are bad
- * data (the last keep log2(e)/T finite in single precision). */
-static int bad_temperature(float T) { return !(T == 0.0f || (T >= 1e-6f && T <= 1e6f)); }
+/* Temperatures the contract accepts: 0 (the greedy rule, the limit of
+ * softmax(z/T) as T falls to 0) or any finite T > 0, for which softmax(z/T)
+ * is defined for every row of finite and -inf logits.  NaN is no number;
+ * a negative T would reverse the ranking of the tokens; T = +inf would make
+ * (z - M)/T the undefined -inf/inf at a masked token.  Those are bad data. */
+static int bad_temperature(float T) { return !(T == 0.0f || (T > 0.0f && isfinite(T))); }
 
 /* Sampled verification (rejection sampling) of a batch.
  *
@@ -273,7 +275,7 @@ static int bad_temperature(float T) { return !(T == 0.0f || (T >= 1e-6f && T <= 
  * every k < d of sampled requests, 0 elsewhere.  ratio_out [B, K] (may be
  * NULL) receives the ratio, NaN where none is computed.
  *
- * Bad data (depth outside [0,K], T outside {0} u [1e-6, 1e6], token outside [0,V), a
+ * Bad data (depth outside [0,K], T not 0 and not a finite T > 0, token outside [0,V), a
  * uniform outside [0,1), NaN or all -inf in a row that is read) gives
  * num_accepted = -1 and out_tokens = -1 for that request.  The rows read
  * are target and draft rows 0..d-1, plus target row d only when nothing

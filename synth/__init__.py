@@ -262,13 +262,19 @@ def mixed(seed: int = 0, B: int = 64, K: int = 16, V: int = 152064, budget: int 
 
 
 def random_case(seed: int, B: int, K: int, V: int, dtype: str = "bf16", temps=(1.0,),
-                scale: float = 3.0, sigma: float = 0.7, wid: int = W_FUZZ) -> Workload:
-    """Generic case for parity sweeps: N(0, scale^2) targets, draft noise sigma,
-    per-request T drawn from `temps`."""
+                scale: float = 3.0, sigma: float = 0.7, wid: int = W_FUZZ, shift: float = 0.0,
+                temperature=None) -> Workload:
+    """Generic case for parity sweeps: N(0, scale^2) targets plus a constant
+    `shift` (rounded to the storage type with each logit), draft noise sigma,
+    per-request T drawn from `temps` (or given per request as `temperature`)."""
     gp = rng(wid, S_PARAMS, seed)
-    T = gp.choice(np.asarray(temps, np.float32), B).astype(np.float32)
+    if temperature is None:
+        T = gp.choice(np.asarray(temps, np.float32), B).astype(np.float32)
+    else:
+        T = np.asarray(temperature, np.float32).reshape(B)
+    sh = np.float32(shift)
     return build(f"random_{dtype}_{B}x{K}x{V}", dtype, B, K, V, wid=wid, seed=seed,
-                 target_fn=lambda b, g: _normal_target(g, V, scale),
+                 target_fn=lambda b, g: _normal_target(g, V, scale) + sh,
                  sigma_fn=lambda b, k: sigma, temperature=T)
 
 

@@ -423,9 +423,13 @@ def test_sample_bad_inputs_and_window():
     assert res["n"].tolist()[:3] == [-1, -1, -1]
     assert res["n"][3] >= 0 and res["n"][4] == -1 and res["n"][5] == -1
     T2 = w.temperature.copy()
-    T2[:4] = [np.inf, 1e-7, 2e6, 1e-6]    # outside [1e-6, 1e6] is bad; 1e-6 itself is fine
+    # +-inf and -0.5 are bad; every finite T > 0 is a temperature, fp32
+    # denormals and the largest fp32 value included
+    T2[:6] = [np.inf, -np.inf, -0.5, 1e-7, 2e6, np.float32(1e-45)]
     res2 = oracle.verify_sample(w.target, w.draft, w.tokens, T2, w.u_accept, w.u_sample)
-    assert res2["n"].tolist()[:3] == [-1, -1, -1] and res2["n"][3] >= 0
+    assert res2["n"].tolist()[:3] == [-1, -1, -1] and np.all(res2["n"][3:6] >= 0)
+    T3 = np.full_like(T2, np.float32(3.4028235e38))
+    assert np.all(oracle.verify_sample(w.target, w.draft, w.tokens, T3, w.u_accept, w.u_sample)["n"] >= 0)
     assert np.all(res["out"][[0, 1, 2, 4, 5]] == -1)
     assert np.all(res["p_draft"][3, 1:] == 0)
 
@@ -743,3 +747,49 @@ def test_dcut_cost_budget_fill_order_and_skip():
     dep = oracle.dcut_allocate_cost(conf, 30.0)
     costs = [oracle.dcut_cost(d) for d in dep if d > 0]
     assert sum(costs) <= 30.0 and min(dep) >= 0
+
+
+# --------------------------------------------------------------------------
+# temperature range and large logits: the definition has no bound on T > 0
+# and is invariant to a constant shift of a row
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1e-30, 1e-40, 1e-45])
+def test_sample_vanishing_temperature_is_greedy(T):
+    # softmax(z / T) tends to the indicator of the argmax as T falls to 0, so
+    # with distinct row maxima the sampled rule accepts exactly the argmax
+    # drafts, and the correction or bonus token is the target argmax: the
+    # greedy continuation.  Draft tokens are the draft argmax (q(x) = 1).
+    w = synth.random_case(21, B=16, K=4, V=3000, dtype="f32", temps=(1.0,), sigma=2.0)
+    vals = synth.as_f64(w.target)
+    srt = np.sort(vals, axis=2)
+    assert np.all(srt[..., -1] > srt[..., -2])
+    tok = np.argmax(synth.as_f64(w.draft), axis=2).astype(np.int32)
+    Tz = np.full(w.B, np.float32(T), np.float32)
+    res = oracle.verify_sample(w.target, w.draft, tok, Tz, w.u_accept, w.u_sample)
+    out, n = oracle.verify_greedy(w.target, tok)
+    assert np.array_equal(res["out"], out) and np.array_equal(res["n"], n)
+    assert set(np.unique(res["p_draft"][res["p_draft"] != 0]).tolist()) <= {1.0}
+    assert 0 < n.mean() < w.K
+
+
+@pytest.mark.parametrize("shift", [2.0 ** 20, -(2.0 ** 20)])
+def test_sample_shift_invariance(shift):
+    # logits on a grid of 1/8 with |z| < 64 stay exact in fp32 after adding
+    # +-2^20, so the shifted rows hold the same distribution exactly; softmax
+    # is invariant to a constant added to a row, and an oracle that
+    # exponentiates without first subtracting the row maximum would overflow
+    g = np.random.default_rng(5)
+    B, K, V = 12, 3, 2000
+    z = np.clip(np.round(g.standard_normal((B, K + 1, V)) * 24) / 8, -63, 63).astype(np.float32)
+    y = np.clip(np.round((z[:, :K] + g.standard_normal((B, K, V)) * 0.4) * 8) / 8, -63, 63).astype(np.float32)
+    tok = np.argmax(y.astype(np.float64) + g.gumbel(size=y.shape), axis=2).astype(np.int32)
+    T = g.choice(np.array([1.0, 0.7, 2.0], np.float32), B)
+    ua, us = g.random((B, K), dtype=np.float32), g.random(B, dtype=np.float32)
+    base = oracle.verify_sample(z, y, tok, T, ua, us)
+    zs, ys = (z + np.float32(shift)).astype(np.float32), (y + np.float32(shift)).astype(np.float32)
+    assert np.array_equal(zs.astype(np.float64) - shift, z.astype(np.float64))
+    moved = oracle.verify_sample(zs, ys, tok, T, ua, us)
+    for key in ("out", "n", "p_draft", "q_draft"):
+        assert np.array_equal(base[key], moved[key]), key
+    assert np.all(base["n"] >= 0)
