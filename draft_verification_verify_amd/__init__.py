@@ -57,6 +57,9 @@ def _load() -> ctypes.CDLL:
     L.spec_verify_sample.restype = ctypes.c_int
     L.spec_verify_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_sample_noalloc.restype = ctypes.c_int
+    L.spec_verify_sample_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32,
+                                             vp, vp, vp, vp, vp]
     L.spec_verify_greedy_early_exit.restype = ctypes.c_int
     L.spec_verify_greedy_early_exit.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, sz,
                                                 vp]
@@ -96,7 +99,10 @@ EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
             "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
             "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit",
-            "spec_verify_read_ceiling", "spec_early_exit_plan")
+            "spec_verify_read_ceiling", "spec_early_exit_plan", "spec_verify_sample_noalloc")
+
+# Bytes of the static scratch array behind spec_verify_sample_noalloc.
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def workspace_size(B: int, K: int, V: int) -> int:
@@ -212,7 +218,8 @@ def _ws(device, B, K, V, workspace):
 
 def _raise(fn, st):
     if st != 0:
-        detail = lib.spec_verify_last_error().decode() if st in (5, 6) else ""
+        named = st in (5, 6) or (st == 2 and fn == "spec_verify_sample_noalloc")
+        detail = lib.spec_verify_last_error().decode() if named else ""
         raise SpecVerifyError(fn, st, detail)
 
 
@@ -265,6 +272,33 @@ def verify_sample(target, draft, tokens, temperature, u_accept, u_sample, depth=
                                 _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft),
                                 _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_sample", st)
+    return out_tokens, num_accepted, p_draft, q_draft
+
+
+def verify_sample_noalloc(target, draft, tokens, temperature, u_accept, u_sample, depth=None, *,
+                          out_tokens, num_accepted, p_draft=None, q_draft=None, stream=None):
+    """verify_sample without a workspace: the library's static device scratch
+    serves instead, and the call allocates nothing (the caller passes every
+    output).  Calls that may overlap on one GPU must be serialised."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check(target, "target")
+    _check(draft, "draft", target.dtype, (B, K, V))
+    _check(tokens, "tokens", torch.int32, (B, K))
+    _check(temperature, "temperature", torch.float32, (B,))
+    _check(u_accept, "u_accept", torch.float32, (B, K))
+    _check(u_sample, "u_sample", torch.float32, (B,))
+    _check(depth, "depth", torch.int32, (B,))
+    _check(out_tokens, "out_tokens", torch.int32, (B, K + 1))
+    _check(num_accepted, "num_accepted", torch.int32, (B,))
+    _check(p_draft, "p_draft", torch.float32, (B, K))
+    _check(q_draft, "q_draft", torch.float32, (B, K))
+    st = lib.spec_verify_sample_noalloc(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens), _ptr(depth),
+                                        _ptr(temperature), _ptr(u_accept), _ptr(u_sample), B, K, V,
+                                        _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft),
+                                        _stream(stream))
+    _raise("spec_verify_sample_noalloc", st)
     return out_tokens, num_accepted, p_draft, q_draft
 
 

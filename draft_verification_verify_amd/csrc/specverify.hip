@@ -51,6 +51,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -2820,6 +2821,50 @@ sv_status launch_windows(Params &P, const std::vector<int> &ends, hipStream_t st
     return SV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free sampled verification: a file-scope
+// device array, one copy per GPU, held until the process ends.  In host
+// code its name is only a stand-in: its device address is taken once per
+// device with hipGetSymbolAddress (with that device current) and kept here,
+// and only that address reaches kernels.  Every call on a GPU shares the
+// array, so calls that overlap on one GPU race; the verify kernels write
+// every part of their workspace before reading it, so nothing needs
+// clearing between calls.
+// ---------------------------------------------------------------------------
+
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+
+// The current device's address of the scratch array, or nullptr (with the
+// last error set) when it cannot be had.
+void *static_scratch()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hip_status("hipGetDevice");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        snprintf(g_last_error, sizeof g_last_error, "device %d beyond the %d this library tracks", dev, MAX_DEVICES);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            snprintf(g_last_error, sizeof g_last_error, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const Layout &L, void *ws)
 {
     Params P;
@@ -2964,6 +3009,43 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     P.p_draft = p_draft;
     P.q_draft = q_draft;
     return checked(launch(P, stream), num_accepted, B, stream, "spec_verify_sample");
+}
+
+sv_status spec_verify_sample_noalloc(const void *target_logits, const void *draft_logits, sv_dtype dt,
+                                     const int32_t *draft_tokens, const int32_t *depth, const float *temperature,
+                                     const float *u_accept, const float *u_sample, int32_t B, int32_t K, int32_t V,
+                                     int32_t *out_tokens, int32_t *num_accepted, float *p_draft, float *q_draft,
+                                     hipStream_t stream)
+{
+    sv_status st = check_shape(B, K, V);
+    if (st != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (!target_logits || !temperature || !u_sample || !out_tokens || !num_accepted) return SV_ERR_INVALID_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+    if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits))) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K, V, L);
+    if (L.total > STATIC_SCRATCH_BYTES) {
+        snprintf(g_last_error, sizeof g_last_error,
+                 "spec_verify_sample_noalloc: B=%d K=%d V=%d needs %zu bytes of scratch, above its %zu-byte static array",
+                 (int)B, (int)K, (int)V, L.total, STATIC_SCRATCH_BYTES);
+        return SV_ERR_UNSUPPORTED;
+    }
+    void *ws = static_scratch();
+    if (!ws) return SV_ERR_HIP;
+    Params P = base_params(B, K, V, dt, MODE_SAMPLE, L, ws);
+    P.target = target_logits;
+    P.draft = draft_logits;
+    P.tokens = draft_tokens;
+    P.depth = depth;
+    P.temperature = temperature;
+    P.u_accept = u_accept;
+    P.u_sample = u_sample;
+    P.out_tokens = out_tokens;
+    P.num_accepted = num_accepted;
+    P.p_draft = p_draft;
+    P.q_draft = q_draft;
+    return launch(P, stream);
 }
 
 sv_status spec_verify_greedy_early_exit(const void *target_logits, sv_dtype dt, const int32_t *draft_tokens,

@@ -170,6 +170,32 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
                              float *p_draft, float *q_draft,
                              void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Allocation-free variant of spec_verify_sample, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, rules, outputs and
+ * kernels as spec_verify_sample, without the workspace: the library's own
+ * static device scratch array (8 MiB = 8388608 bytes, one per GPU, held
+ * until the process ends) serves as the workspace.
+ * The call allocates nothing and frees nothing.
+ *   Limits.  Shapes whose workspace (spec_verify_workspace_size) exceeds the
+ *     array are rejected with SV_ERR_UNSUPPORTED before anything is enqueued
+ *     (spec_verify_last_error gives the sizes); B=64, K=16 fits up to
+ *     V=152064 in fp32 or bf16.
+ *   Concurrency.  Every call on a GPU uses that GPU's one array: calls that
+ *     may overlap on one GPU (different streams, different threads) race and
+ *     must be serialised by the caller.  Nothing in the array needs clearing
+ *     between calls.
+ *   Errors.  As spec_verify_sample; SV_ERR_HIP if the array's device address
+ *     cannot be obtained.  SPECVERIFY_CHECK does not apply (it would copy to
+ *     the host and wait). */
+sv_status spec_verify_sample_noalloc(const void *target_logits, const void *draft_logits,
+                                     sv_dtype dt, const int32_t *draft_tokens,
+                                     const int32_t *depth, const float *temperature,
+                                     const float *u_accept, const float *u_sample,
+                                     int32_t B, int32_t K, int32_t V,
+                                     int32_t *out_tokens, int32_t *num_accepted,
+                                     float *p_draft, float *q_draft, hipStream_t stream);
+
 /* Early-exit verification: the rules of spec_verify_greedy and
  * spec_verify_sample, with positions examined in order.  The accepted
  * length counts the drafted tokens approved before the first discrepancy

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -224,3 +224,19 @@ def test_binding_shares_torch_hip_runtime():
     maps = open("/proc/self/maps").read()
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+def test_noalloc_host_errors():
+    # argument and size checks that precede any HIP call
+    def call(B=4, K=3, V=1000, target=FAKE, draft=FAKE, temp=FAKE, us=FAKE, out=FAKE, num=FAKE, dt=1):
+        return L.spec_verify_sample_noalloc(target, draft, dt, FAKE, NULL, temp, FAKE, us, B, K, V, out, num,
+                                            NULL, NULL, NULL)
+    assert call(target=NULL) == 1 and call(temp=NULL) == 1 and call(out=NULL) == 1 and call(num=NULL) == 1
+    assert call(draft=NULL) == 1 and call(dt=7) == 1 and call(target=FAKE_MIS) == 1
+    assert call(B=0) == 1 and call(B=4097) == 2
+    # the workspace of B=256, K=64, V=128000 exceeds the 8 MiB static array
+    assert sv.workspace_size(256, 64, 128000) > sv.NOALLOC_SCRATCH_BYTES
+    assert call(B=256, K=64, V=128000) == 2
+    assert "static array" in L.spec_verify_last_error().decode()
+    # the headline shapes fit
+    assert sv.workspace_size(64, 16, 152064) <= sv.NOALLOC_SCRATCH_BYTES
