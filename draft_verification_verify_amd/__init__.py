@@ -73,6 +73,9 @@ def _load() -> ctypes.CDLL:
     L.spec_verify_sample_reuse.restype = ctypes.c_int
     L.spec_verify_sample_reuse.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                            vp, vp, vp, vp, vp, sz, vp]
+    L.spec_accept_stats_summary.restype = ctypes.c_int
+    L.spec_accept_stats_summary.argtypes = [vp, i32, vp, ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_double)]
     L.dcut_allocate_cost.restype = ctypes.c_int
     L.dcut_allocate_cost.argtypes = [vp, vp, i32, i32, vp, vp, i32, ctypes.c_double, vp, vp]
     L.spec_accept_stats_update.restype = ctypes.c_int
@@ -99,7 +102,8 @@ EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify
             "spec_verify_greedy", "spec_verify_sample", "spec_draft_confidence", "dcut_allocate",
             "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
             "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit",
-            "spec_verify_read_ceiling", "spec_early_exit_plan", "spec_verify_sample_noalloc")
+            "spec_verify_read_ceiling", "spec_early_exit_plan", "spec_verify_sample_noalloc",
+            "spec_accept_stats_summary")
 
 # Bytes of the static scratch array behind spec_verify_sample_noalloc.
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -113,9 +117,8 @@ def read_ceiling(buf, sink=None, stream=None):
     """Benchmark instrumentation: one plain read of every byte of ``buf`` (a
     contiguous CUDA tensor) with the row-statistics kernel's load width."""
     torch = _torch()
+    _validate((buf, "buf", None, None), (sink, "sink", torch.int32, (1,)))
     nbytes = buf.numel() * buf.element_size()
-    if not buf.is_cuda or not buf.is_contiguous():
-        raise ValueError("buf must be a contiguous GPU tensor")
     if sink is None:
         sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
     st = lib.spec_verify_read_ceiling(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
@@ -168,26 +171,50 @@ def _dtype_code(t) -> int:
     raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
 
 
-def _check(t, name, dtype=None, shape=None):
+def _shape3(t, name):
+    """(B, rows, V) of a 3-D logits tensor."""
     torch = _torch()
-    if t is None:
-        return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    _ = torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D [B, rows, V], got shape {tuple(t.shape)}")
+    return tuple(int(x) for x in t.shape)
+
+
+def _validate(*specs, device=None):
+    """Checks every tensor argument of a call before any pointer is taken.
+
+    specs: (tensor or None, name, dtype or None, shape or None).  First the
+    dtype, shape and contiguity of every argument, then that every one is a
+    GPU tensor on ``device`` (default: the first argument's).  A wrong-sized
+    output or a host tensor would otherwise become an out-of-bounds or
+    host-address device write."""
+    torch = _torch()
+    present = [sp for sp in specs if sp[0] is not None]
+    for t, name, dtype, shape in present:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if device is None and present:
+        device = present[0][0].device
+    for t, name, _, _ in present:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}; the call's tensors are on {device}")
 
 
 class Workspace:
     """A device buffer reused across calls on one device (grown on demand).
 
-    Each call clears the counters it uses, so contents never matter.  Calls
-    that share a workspace must be ordered on one stream."""
+    Each call writes every part of the workspace it later reads, so contents
+    never matter.  Calls that share a workspace must be ordered on one
+    stream."""
 
     def __init__(self):
         self._buf = {}
@@ -208,11 +235,14 @@ _default_ws = Workspace()
 
 
 def _ws(device, B, K, V, workspace):
+    """(buffer, byte count) of the workspace: the caller's (a contiguous GPU
+    tensor on the call's device, any dtype) or the shared default."""
     n = workspace_size(B, K, V)
     if n == 0:
         raise SpecVerifyError("spec_verify_workspace_size", 2)
     if workspace is None:
         return _default_ws.get(device, n), n
+    _validate((workspace, "workspace", None, None), device=device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -223,21 +253,45 @@ def _raise(fn, st):
         raise SpecVerifyError(fn, st, detail)
 
 
+def _sample_specs(target, draft, tokens, temperature, u_accept, u_sample, depth, B, K, V):
+    torch = _torch()
+    return [(target, "target", None, None), (draft, "draft", target.dtype, (B, K, V)),
+            (tokens, "tokens", torch.int32, (B, K)), (temperature, "temperature", torch.float32, (B,)),
+            (u_accept, "u_accept", torch.float32, (B, K)), (u_sample, "u_sample", torch.float32, (B,)),
+            (depth, "depth", torch.int32, (B,))]
+
+
+def _out_specs(B, K, out_tokens, num_accepted, p_draft=None, q_draft=None):
+    torch = _torch()
+    return [(out_tokens, "out_tokens", torch.int32, (B, K + 1)), (num_accepted, "num_accepted", torch.int32, (B,)),
+            (p_draft, "p_draft", torch.float32, (B, K)), (q_draft, "q_draft", torch.float32, (B, K))]
+
+
+def _new_outputs(dev, B, K, out_tokens, num_accepted, p_draft=None, q_draft=None, want_probs=False):
+    torch = _torch()
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if want_probs and p_draft is None:
+        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if want_probs and q_draft is None:
+        q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
+    return out_tokens, num_accepted, p_draft, q_draft
+
+
 def verify_greedy(target, tokens, depth=None, *, out_tokens=None, num_accepted=None,
                   workspace=None, stream=None):
     """Greedy (T=0) verification.  target [B,K+1,V] bf16/fp32, tokens [B,K] int32."""
     torch = _torch()
-    B, K1, V = target.shape
+    B, K1, V = _shape3(target, "target")
     K = K1 - 1
-    _check(target, "target")
-    _check(tokens, "tokens", torch.int32, (B, K))
-    _check(depth, "depth", torch.int32, (B,))
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=target.device)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
+    dt = _dtype_code(target)
+    _validate((target, "target", None, None), (tokens, "tokens", torch.int32, (B, K)),
+              (depth, "depth", torch.int32, (B,)), *_out_specs(B, K, out_tokens, num_accepted))
+    out_tokens, num_accepted, _, _ = _new_outputs(target.device, B, K, out_tokens, num_accepted)
     ws, nbytes = _ws(target.device, B, K, V, workspace)
-    st = lib.spec_verify_greedy(_ptr(target), _dtype_code(target), _ptr(tokens), _ptr(depth), B, K, V,
+    st = lib.spec_verify_greedy(_ptr(target), dt, _ptr(tokens), _ptr(depth), B, K, V,
                                 _ptr(out_tokens), _ptr(num_accepted), _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_greedy", st)
     return out_tokens, num_accepted
@@ -247,27 +301,15 @@ def verify_sample(target, draft, tokens, temperature, u_accept, u_sample, depth=
                   out_tokens=None, num_accepted=None, p_draft=None, q_draft=None,
                   want_probs: bool = True, workspace=None, stream=None):
     """Rejection-sampling verification.  Returns (out_tokens, num_accepted, p_draft, q_draft)."""
-    torch = _torch()
-    B, K1, V = target.shape
+    B, K1, V = _shape3(target, "target")
     K = K1 - 1
-    _check(target, "target")
-    _check(draft, "draft", target.dtype, (B, K, V))
-    _check(tokens, "tokens", torch.int32, (B, K))
-    _check(temperature, "temperature", torch.float32, (B,))
-    _check(u_accept, "u_accept", torch.float32, (B, K))
-    _check(u_sample, "u_sample", torch.float32, (B,))
-    _check(depth, "depth", torch.int32, (B,))
-    dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    if want_probs and p_draft is None:
-        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
-    if want_probs and q_draft is None:
-        q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
-    ws, nbytes = _ws(dev, B, K, V, workspace)
-    st = lib.spec_verify_sample(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens), _ptr(depth),
+    dt = _dtype_code(target)
+    _validate(*_sample_specs(target, draft, tokens, temperature, u_accept, u_sample, depth, B, K, V),
+              *_out_specs(B, K, out_tokens, num_accepted, p_draft, q_draft))
+    out_tokens, num_accepted, p_draft, q_draft = _new_outputs(target.device, B, K, out_tokens, num_accepted,
+                                                              p_draft, q_draft, want_probs)
+    ws, nbytes = _ws(target.device, B, K, V, workspace)
+    st = lib.spec_verify_sample(_ptr(target), _ptr(draft), dt, _ptr(tokens), _ptr(depth),
                                 _ptr(temperature), _ptr(u_accept), _ptr(u_sample), B, K, V,
                                 _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft),
                                 _ptr(ws), nbytes, _stream(stream))
@@ -280,21 +322,14 @@ def verify_sample_noalloc(target, draft, tokens, temperature, u_accept, u_sample
     """verify_sample without a workspace: the library's static device scratch
     serves instead, and the call allocates nothing (the caller passes every
     output).  Calls that may overlap on one GPU must be serialised."""
-    torch = _torch()
-    B, K1, V = target.shape
+    B, K1, V = _shape3(target, "target")
     K = K1 - 1
-    _check(target, "target")
-    _check(draft, "draft", target.dtype, (B, K, V))
-    _check(tokens, "tokens", torch.int32, (B, K))
-    _check(temperature, "temperature", torch.float32, (B,))
-    _check(u_accept, "u_accept", torch.float32, (B, K))
-    _check(u_sample, "u_sample", torch.float32, (B,))
-    _check(depth, "depth", torch.int32, (B,))
-    _check(out_tokens, "out_tokens", torch.int32, (B, K + 1))
-    _check(num_accepted, "num_accepted", torch.int32, (B,))
-    _check(p_draft, "p_draft", torch.float32, (B, K))
-    _check(q_draft, "q_draft", torch.float32, (B, K))
-    st = lib.spec_verify_sample_noalloc(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens), _ptr(depth),
+    dt = _dtype_code(target)
+    if out_tokens is None or num_accepted is None:
+        raise ValueError("verify_sample_noalloc allocates nothing: pass out_tokens and num_accepted")
+    _validate(*_sample_specs(target, draft, tokens, temperature, u_accept, u_sample, depth, B, K, V),
+              *_out_specs(B, K, out_tokens, num_accepted, p_draft, q_draft))
+    st = lib.spec_verify_sample_noalloc(_ptr(target), _ptr(draft), dt, _ptr(tokens), _ptr(depth),
                                         _ptr(temperature), _ptr(u_accept), _ptr(u_sample), B, K, V,
                                         _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft),
                                         _stream(stream))
@@ -319,10 +354,10 @@ def window_ends(K: int, window=None, ends=None):
 
 def early_exit_plan(alpha, window_cost: float = 2.5):
     """Window ends minimising the expected cost for per-position acceptance
-    ``alpha`` (a sequence of K rates; NaN, a position no request reached,
-    counts as 0).  ``window_cost``: a window's fixed latency in units of
-    streaming one position of the batch."""
-    a = [0.0 if (x != x) else min(max(float(x), 0.0), 1.0) for x in alpha]
+    ``alpha`` (a sequence of K rates in [0, 1]; NaN, a position no request
+    reached, counts as 0).  ``window_cost``: a window's fixed latency in
+    units of streaming one position of the batch."""
+    a = [float(x) for x in alpha]
     K = len(a)
     arr = (ctypes.c_double * max(K, 1))(*a)
     ends = (ctypes.c_int32 * max(K, 1))()
@@ -343,18 +378,15 @@ def verify_greedy_early_exit(target, tokens, depth=None, *, window=None, ends=No
     """verify_greedy that reads no row after a request's first rejection, in
     windows (see ``window_ends``)."""
     torch = _torch()
-    B, K1, V = target.shape
+    B, K1, V = _shape3(target, "target")
     K = K1 - 1
-    _check(target, "target")
-    _check(tokens, "tokens", torch.int32, (B, K))
-    _check(depth, "depth", torch.int32, (B,))
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=target.device)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
+    dt = _dtype_code(target)
+    _validate((target, "target", None, None), (tokens, "tokens", torch.int32, (B, K)),
+              (depth, "depth", torch.int32, (B,)), *_out_specs(B, K, out_tokens, num_accepted))
+    out_tokens, num_accepted, _, _ = _new_outputs(target.device, B, K, out_tokens, num_accepted)
     ws, nbytes = _ws(target.device, B, K, V, workspace)
     ep, ne, _keep = _ends_arg(window_ends(K, window, ends))
-    st = lib.spec_verify_greedy_early_exit(_ptr(target), _dtype_code(target), _ptr(tokens), _ptr(depth),
+    st = lib.spec_verify_greedy_early_exit(_ptr(target), dt, _ptr(tokens), _ptr(depth),
                                            B, K, V, ep, ne, _ptr(out_tokens), _ptr(num_accepted),
                                            _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_greedy_early_exit", st)
@@ -367,28 +399,16 @@ def verify_sample_early_exit(target, draft, tokens, temperature, u_accept, u_sam
     """verify_sample that reads no row after a request's first rejection, in
     windows (see ``window_ends``).  Returns (out_tokens, num_accepted,
     p_draft, q_draft)."""
-    torch = _torch()
-    B, K1, V = target.shape
+    B, K1, V = _shape3(target, "target")
     K = K1 - 1
-    _check(target, "target")
-    _check(draft, "draft", target.dtype, (B, K, V))
-    _check(tokens, "tokens", torch.int32, (B, K))
-    _check(temperature, "temperature", torch.float32, (B,))
-    _check(u_accept, "u_accept", torch.float32, (B, K))
-    _check(u_sample, "u_sample", torch.float32, (B,))
-    _check(depth, "depth", torch.int32, (B,))
-    dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    if want_probs and p_draft is None:
-        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
-    if want_probs and q_draft is None:
-        q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
-    ws, nbytes = _ws(dev, B, K, V, workspace)
+    dt = _dtype_code(target)
+    _validate(*_sample_specs(target, draft, tokens, temperature, u_accept, u_sample, depth, B, K, V),
+              *_out_specs(B, K, out_tokens, num_accepted, p_draft, q_draft))
+    out_tokens, num_accepted, p_draft, q_draft = _new_outputs(target.device, B, K, out_tokens, num_accepted,
+                                                              p_draft, q_draft, want_probs)
+    ws, nbytes = _ws(target.device, B, K, V, workspace)
     ep, ne, _keep = _ends_arg(window_ends(K, window, ends))
-    st = lib.spec_verify_sample_early_exit(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens),
+    st = lib.spec_verify_sample_early_exit(_ptr(target), _ptr(draft), dt, _ptr(tokens),
                                            _ptr(depth), _ptr(temperature), _ptr(u_accept), _ptr(u_sample),
                                            B, K, V, ep, ne, _ptr(out_tokens), _ptr(num_accepted),
                                            _ptr(p_draft), _ptr(q_draft), _ptr(ws), nbytes, _stream(stream))
@@ -399,13 +419,14 @@ def verify_sample_early_exit(target, draft, tokens, temperature, u_accept, u_sam
 def draft_confidence(draft, max_depth=None, *, conf=None, workspace=None, stream=None):
     """conf[b,k] = max softmax(draft[b,k]) at T=1 (0 beyond max_depth[b])."""
     torch = _torch()
-    B, K, V = draft.shape
-    _check(draft, "draft")
-    _check(max_depth, "max_depth", torch.int32, (B,))
+    B, K, V = _shape3(draft, "draft")
+    dt = _dtype_code(draft)
+    _validate((draft, "draft", None, None), (max_depth, "max_depth", torch.int32, (B,)),
+              (conf, "conf", torch.float32, (B, K)))
     if conf is None:
         conf = torch.empty((B, K), dtype=torch.float32, device=draft.device)
     ws, nbytes = _ws(draft.device, B, K, V, workspace)
-    st = lib.spec_draft_confidence(_ptr(draft), _dtype_code(draft), _ptr(max_depth), B, K, V, _ptr(conf),
+    st = lib.spec_draft_confidence(_ptr(draft), dt, _ptr(max_depth), B, K, V, _ptr(conf),
                                    _ptr(ws), nbytes, _stream(stream))
     _raise("spec_draft_confidence", st)
     return conf
@@ -417,16 +438,16 @@ def draft_confidence_stats(draft, max_depth=None, *, conf=None, want_conf: bool 
     records, returned as a float64 tensor [B, K, 2]: see row_stat_fields).
     Returns (conf or None, stats)."""
     torch = _torch()
-    B, K, V = draft.shape
-    _check(draft, "draft")
-    _check(max_depth, "max_depth", torch.int32, (B,))
+    B, K, V = _shape3(draft, "draft")
+    dt = _dtype_code(draft)
+    _validate((draft, "draft", None, None), (max_depth, "max_depth", torch.int32, (B,)),
+              (conf, "conf", torch.float32, (B, K)), (stats, "stats", torch.float64, (B, K, 2)))
     if want_conf and conf is None:
         conf = torch.empty((B, K), dtype=torch.float32, device=draft.device)
     if stats is None:
         stats = torch.empty((B, K, 2), dtype=torch.float64, device=draft.device)
-    _check(stats, "stats", torch.float64, (B, K, 2))
     ws, nbytes = _ws(draft.device, B, K, V, workspace)
-    st = lib.spec_draft_confidence_stats(_ptr(draft), _dtype_code(draft), _ptr(max_depth), B, K, V,
+    st = lib.spec_draft_confidence_stats(_ptr(draft), dt, _ptr(max_depth), B, K, V,
                                          _ptr(conf), _ptr(stats), _ptr(ws), nbytes, _stream(stream))
     _raise("spec_draft_confidence_stats", st)
     return conf, stats
@@ -443,27 +464,16 @@ def verify_sample_reuse(target, draft, tokens, temperature, u_accept, u_sample, 
     """verify_sample with the draft rows' statistics from draft_confidence_stats
     (used for requests at temperature 1)."""
     torch = _torch()
-    B, K1, V = target.shape
+    B, K1, V = _shape3(target, "target")
     K = K1 - 1
-    _check(target, "target")
-    _check(draft, "draft", target.dtype, (B, K, V))
-    _check(tokens, "tokens", torch.int32, (B, K))
-    _check(temperature, "temperature", torch.float32, (B,))
-    _check(u_accept, "u_accept", torch.float32, (B, K))
-    _check(u_sample, "u_sample", torch.float32, (B,))
-    _check(draft_stats, "draft_stats", torch.float64, (B, K, 2))
-    _check(depth, "depth", torch.int32, (B,))
-    dev = target.device
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
-    if want_probs and p_draft is None:
-        p_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
-    if want_probs and q_draft is None:
-        q_draft = torch.empty((B, K), dtype=torch.float32, device=dev)
-    ws, nbytes = _ws(dev, B, K, V, workspace)
-    st = lib.spec_verify_sample_reuse(_ptr(target), _ptr(draft), _dtype_code(target), _ptr(tokens), _ptr(depth),
+    dt = _dtype_code(target)
+    _validate(*_sample_specs(target, draft, tokens, temperature, u_accept, u_sample, depth, B, K, V),
+              (draft_stats, "draft_stats", torch.float64, (B, K, 2)),
+              *_out_specs(B, K, out_tokens, num_accepted, p_draft, q_draft))
+    out_tokens, num_accepted, p_draft, q_draft = _new_outputs(target.device, B, K, out_tokens, num_accepted,
+                                                              p_draft, q_draft, want_probs)
+    ws, nbytes = _ws(target.device, B, K, V, workspace)
+    st = lib.spec_verify_sample_reuse(_ptr(target), _ptr(draft), dt, _ptr(tokens), _ptr(depth),
                                       _ptr(temperature), _ptr(u_accept), _ptr(u_sample), _ptr(draft_stats),
                                       B, K, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft),
                                       _ptr(q_draft), _ptr(ws), nbytes, _stream(stream))
@@ -475,13 +485,22 @@ def verify_sample_reuse(target, draft, tokens, temperature, u_accept, u_sample, 
 DEFAULT_COST_TABLE = ((1.0, 1.0), (2.0, 1.2), (4.0, 1.5), (8.0, 2.0), (16.0, 3.0))
 
 
+def _conf_shape(conf):
+    torch = _torch()
+    if not isinstance(conf, torch.Tensor):
+        raise TypeError(f"conf must be a torch tensor, got {type(conf).__name__}")
+    if conf.dim() != 2:
+        raise ValueError(f"conf must be 2-D [B, K], got shape {tuple(conf.shape)}")
+    return int(conf.shape[0]), int(conf.shape[1])
+
+
 def dcut_allocate_cost(conf, max_verify: float, max_depth=None, table=DEFAULT_COST_TABLE, *,
                        depth_out=None, stream=None):
     """Cost-aware D-cut (per-request best benefit/cost depth, greedy budget fill)."""
     torch = _torch()
-    B, K = conf.shape
-    _check(conf, "conf", torch.float32)
-    _check(max_depth, "max_depth", torch.int32, (B,))
+    B, K = _conf_shape(conf)
+    _validate((conf, "conf", torch.float32, (B, K)), (max_depth, "max_depth", torch.int32, (B,)),
+              (depth_out, "depth_out", torch.int32, (B,)))
     if depth_out is None:
         depth_out = torch.empty((B,), dtype=torch.int32, device=conf.device)
     n = len(table)
@@ -498,34 +517,42 @@ def accept_stats_update(num_accepted, K: int, depth=None, counters=None, *, stre
     """Adds one call's acceptance statistics into counters (int64 [2K + 4] on
     the device; created zeroed when None) and returns them."""
     torch = _torch()
-    B = num_accepted.shape[0]
-    _check(num_accepted, "num_accepted", torch.int32, (B,))
-    _check(depth, "depth", torch.int32, (B,))
+    if not isinstance(num_accepted, torch.Tensor) or num_accepted.dim() != 1:
+        raise ValueError("num_accepted must be a 1-D int32 tensor [B]")
+    B = int(num_accepted.shape[0])
+    _validate((num_accepted, "num_accepted", torch.int32, (B,)), (depth, "depth", torch.int32, (B,)),
+              (counters, "counters", torch.int64, (2 * K + 4,)))
     if counters is None:
         counters = torch.zeros(2 * K + 4, dtype=torch.int64, device=num_accepted.device)
-    _check(counters, "counters", torch.int64, (2 * K + 4,))
     st = lib.spec_accept_stats_update(_ptr(num_accepted), _ptr(depth), B, K, _ptr(counters), _stream(stream))
     _raise("spec_accept_stats_update", st)
     return counters
 
 
 def accept_stats_summary(counters, K: int) -> dict:
-    """Per-position acceptance, mean accepted length and tau from the counters."""
-    c = counters.cpu().tolist() if hasattr(counters, "cpu") else list(counters)
-    reached, accepted = c[:K], c[K:2 * K]
-    req = c[2 * K]
-    return {"alpha": [a / r if r else float("nan") for a, r in zip(accepted, reached)],
-            "reached": reached, "accepted": accepted, "requests": req, "bad": c[2 * K + 1],
-            "mean_accepted": c[2 * K + 2] / req if req else float("nan"),
-            "tau": c[2 * K + 3] / req if req else float("nan")}
+    """Per-position acceptance, mean accepted length and tau from the counters
+    (spec_accept_stats_summary on a host copy of them)."""
+    torch = _torch()
+    c = counters.detach().cpu() if isinstance(counters, torch.Tensor) else torch.tensor(list(counters))
+    c = c.to(torch.int64).contiguous()
+    if c.numel() != 2 * K + 4:
+        raise ValueError(f"counters must hold 2K + 4 = {2 * K + 4} values, got {c.numel()}")
+    alpha = (ctypes.c_double * max(K, 1))()
+    mean, tau = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    st = lib.spec_accept_stats_summary(ctypes.c_void_p(c.data_ptr()), K, ctypes.cast(alpha, ctypes.c_void_p),
+                                       ctypes.byref(mean), ctypes.byref(tau))
+    _raise("spec_accept_stats_summary", st)
+    v = c.tolist()
+    return {"alpha": [alpha[k] for k in range(K)], "reached": v[:K], "accepted": v[K:2 * K],
+            "requests": v[2 * K], "bad": v[2 * K + 1], "mean_accepted": mean.value, "tau": tau.value}
 
 
 def dcut_allocate(conf, budget: int, max_depth=None, *, depth_out=None, stream=None):
     """D-cut depth allocation (global top-k of fp32 prefix confidence)."""
     torch = _torch()
-    B, K = conf.shape
-    _check(conf, "conf", torch.float32)
-    _check(max_depth, "max_depth", torch.int32, (B,))
+    B, K = _conf_shape(conf)
+    _validate((conf, "conf", torch.float32, (B, K)), (max_depth, "max_depth", torch.int32, (B,)),
+              (depth_out, "depth_out", torch.int32, (B,)))
     if depth_out is None:
         depth_out = torch.empty((B,), dtype=torch.int32, device=conf.device)
     st = lib.dcut_allocate(_ptr(conf), _ptr(max_depth), B, K, int(budget), _ptr(depth_out), _stream(stream))

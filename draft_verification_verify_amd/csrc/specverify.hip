@@ -3188,8 +3188,9 @@ sv_status spec_early_exit_plan(const double *alpha, int32_t K, double window_cos
 {
     if (!ends || !n_windows || K < 0 || K > K_MAX || (K > 0 && !alpha)) return SV_ERR_INVALID_ARG;
     if (!(window_cost >= 0.0) || window_cost > 1e30) return SV_ERR_INVALID_ARG;
+    // a NaN rate is a position no request reached: it counts as 0
     for (int32_t k = 0; k < K; ++k)
-        if (!(alpha[k] >= 0.0 && alpha[k] <= 1.0)) return SV_ERR_INVALID_ARG;
+        if (!(alpha[k] >= 0.0 && alpha[k] <= 1.0) && alpha[k] == alpha[k]) return SV_ERR_INVALID_ARG;
     if (K == 0) {
         ends[0] = 1;
         *n_windows = 1;
@@ -3199,7 +3200,7 @@ sv_status spec_early_exit_plan(const double *alpha, int32_t K, double window_cos
     std::vector<double> live((size_t)K + 1), best((size_t)K + 1);
     std::vector<int32_t> next((size_t)K + 1);
     live[0] = 1.0;
-    for (int32_t p = 0; p < K; ++p) live[(size_t)p + 1] = live[(size_t)p] * alpha[p];
+    for (int32_t p = 0; p < K; ++p) live[(size_t)p + 1] = live[(size_t)p] * (alpha[p] == alpha[p] ? alpha[p] : 0.0);
     // best[p]: least expected cost of the windows covering positions p..K-1
     best[(size_t)K] = 0.0;
     for (int32_t p = K - 1; p >= 0; --p) {
@@ -3218,6 +3219,20 @@ sv_status spec_early_exit_plan(const double *alpha, int32_t K, double window_cos
     int32_t n = 0;
     for (int32_t p = 0; p < K; p = next[(size_t)p]) ends[n++] = next[(size_t)p];
     *n_windows = n;
+    return SV_OK;
+}
+
+sv_status spec_accept_stats_summary(const unsigned long long *counters, int32_t K, double *alpha,
+                                    double *mean_accepted, double *tau)
+{
+    if (!counters || K < 0 || K > K_MAX || (K > 0 && !alpha) || !mean_accepted || !tau) return SV_ERR_INVALID_ARG;
+    for (int32_t k = 0; k < K; ++k) {
+        const unsigned long long reached = counters[k], accepted = counters[K + k];
+        alpha[k] = reached ? (double)accepted / (double)reached : NAN;
+    }
+    const unsigned long long req = counters[2 * K];
+    *mean_accepted = req ? (double)counters[2 * K + 2] / (double)req : NAN;
+    *tau = req ? (double)counters[2 * K + 3] / (double)req : NAN;
     return SV_OK;
 }
 

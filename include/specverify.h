@@ -254,12 +254,13 @@ sv_status spec_verify_sample_early_exit(const void *target_logits, const void *d
  * in bf16: about 2.5).  alpha is what spec_accept_stats_update measures:
  * per-position acceptance ([Hamidun], section "Comment fonctionne la voie
  * MTP", reports these rates).
- *   alpha       [K] double in [0, 1] (host), may be NULL when K = 0
+ *   alpha       [K] double in [0, 1] or NaN (host), may be NULL when K = 0;
+ *     NaN, a position no request reached, counts as 0
  *   window_cost finite, >= 0
  *   ends        [max(K, 1)] int32 (host, out): the window ends, ready for
  *               spec_verify_*_early_exit; n_windows (out): how many
  *   Errors: SV_ERR_INVALID_ARG for a NULL output, K outside [0, 1024], an
- *   alpha outside [0, 1] (NaN included) or a bad window_cost. */
+ *   alpha outside [0, 1] (other than NaN) or a bad window_cost. */
 sv_status spec_early_exit_plan(const double *alpha, int32_t K, double window_cost, int32_t *ends,
                                int32_t *n_windows);
 
@@ -375,6 +376,17 @@ sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth,
 sv_status spec_accept_stats_update(const int32_t *num_accepted, const int32_t *depth,
                                    int32_t B, int32_t K, unsigned long long *counters,
                                    hipStream_t stream);
+
+/* Summary of the acceptance counters (host memory: the caller copies the
+ * [2K + 4] counters from the device first).  For each position k,
+ * alpha[k] = accepted[k] / reached[k] (NaN where no request reached k);
+ * *mean_accepted = sum n / requests and *tau = sum (n + 1) / requests, the
+ * mean accepted length counted with the bonus token as [Hamidun] reports it
+ * (section "Comment fonctionne la voie MTP"); NaN when no request was
+ * counted.  Divisions in double.  SV_ERR_INVALID_ARG for a null pointer or
+ * K outside [0, 1024]. */
+sv_status spec_accept_stats_summary(const unsigned long long *counters, int32_t K, double *alpha,
+                                    double *mean_accepted, double *tau);
 
 /* D-cut verification-depth allocation: verification compute is a shared
  * batch-level budget that is moved toward the requests whose drafted

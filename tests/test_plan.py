@@ -48,6 +48,7 @@ def test_plan_closed_forms():
     assert sv.early_exit_plan([0.5] * K, 0.0) == list(range(1, K + 1))   # free windows: one per position
     assert sv.early_exit_plan([], 3.0) == [1]                   # K = 0
     assert sv.early_exit_plan([float("nan")] * 3, 1.0) == [1, 3]   # unreached positions count as 0
+    assert sv.early_exit_plan([0.9, float("nan"), 0.7], 1.0) == sv.early_exit_plan([0.9, 0.0, 0.7], 1.0)
 
 
 def test_plan_argument_errors():
@@ -64,6 +65,6 @@ def test_plan_argument_errors():
     assert L.spec_early_exit_plan(A, 3, -0.5, E, N) == 1
     assert L.spec_early_exit_plan(A, 3, float("nan"), E, N) == 1
     assert L.spec_early_exit_plan(A, 3, float("inf"), E, N) == 1
-    for bad in (float("nan"), 1.5, -0.1):
+    for bad in (1.5, -0.1, float("inf")):
         b = (ctypes.c_double * 3)(0.5, bad, 0.5)
         assert L.spec_early_exit_plan(ctypes.cast(b, ctypes.c_void_p), 3, 1.0, E, N) == 1
