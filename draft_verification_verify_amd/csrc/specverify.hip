@@ -226,6 +226,7 @@ struct Params {
     int32_t aligned;   // V * element size is a multiple of 16: every row starts 16-byte aligned
     int32_t row_cus;   // compute units the row-pass grid is spread over
     float row_skew;    // row pass: task-count slope across dispatch slots
+    int32_t chunks;    // row pass: chunks per row forced by SPECVERIFY_CHUNK (0: chosen from the grid)
     // Early-exit calls: this launch verifies positions [win_lo, win_hi) of
     // the requests still verifying (alive_in, read when win_lo > 0) and
     // records in alive_out which of them continue into the next window.
@@ -699,13 +700,16 @@ __device__ __forceinline__ int find_request(const int *row_off, int B, int r)
 // sets up its next task while its other buffer's batch is in flight, and a
 // run of one-batch tasks leaves that set-up exposed between loads (passes
 // over a few hundred rows ran about 12 % slower on MI355X).
-__device__ __forceinline__ void row_chunking(int R, int V, bool bf16, int64_t nwaves, int &cpr, int &nb)
+// A positive `forced` (SPECVERIFY_CHUNK, a test and tuning override) asks for
+// that many chunks per row instead, within [1, min(batches, 256)].
+__device__ __forceinline__ void row_chunking(int R, int V, bool bf16, int64_t nwaves, int forced, int &cpr, int &nb)
 {
     const int64_t nv = nvec_max(V, bf16 ? 8 : 4);
     const int nbt = (int)ceil_div(nv, WVEC);
     const int64_t want = ceil_div(8 * nwaves, (int64_t)(R > 0 ? R : 1));
     cpr = (int)std::min<int64_t>(std::max<int64_t>(want, 1),
                                  std::min<int64_t>(std::min(nbt, CPR_CAP), ceil_div(nbt, 2)));
+    if (forced > 0) cpr = std::min(forced, std::min(nbt, CPR_CAP));
     nb = (int)ceil_div(nbt, cpr);
     cpr = (int)ceil_div(nbt, nb);
 }
@@ -1131,7 +1135,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int R = __builtin_amdgcn_readfirstlane(pl.row_off[P.B]);
     const uint32_t nwaves = gridDim.x * NWAVE;
     int cpr, nb;
-    row_chunking(R, P.V, BF16, nwaves, cpr, nb);
+    row_chunking(R, P.V, BF16, nwaves, P.chunks, cpr, nb);
     // The divisions above run on the vector unit; their (uniform) results
     // are moved to scalar registers so everything derived stays scalar.
     cpr = __builtin_amdgcn_readfirstlane(cpr);
@@ -2315,11 +2319,20 @@ __global__ __launch_bounds__(WG) void read_ceiling_kernel(const uint4 *buf_, int
 }
 
 // ---------------------------------------------------------------------------
-// Cost-aware D-cut: one workgroup of 1024 threads.  Per request the depth with
-// the best benefit (prefix confidence times depth over the interpolated cost,
-// in double), then candidates ranked by (benefit desc, request asc) by
-// counting, then one thread fills the cost budget in rank order.  LDS:
-// benefit (8 B), chosen depth and rank (2 B each) per request, cost per depth.
+// Cost-aware D-cut: one workgroup of 1024 threads.
+//  1. cost(d) for every depth into LDS: the latency table read as linear
+//     between neighbouring points, constant outside them.
+//  2. one thread per request: the value (P(d) * d) / cost(d) of each depth,
+//     the prefix product P in order in double; the request bids its best
+//     depth (smallest on ties).  Confidence loads go out eight at a time.
+//  3. the bids are sorted in LDS by (value desc, request asc): a bitonic
+//     sort over the next power of two, requests without a bid last.
+//  4. wave 0 offers the budget in that order: lane l holds the cost of bid
+//     64 h + l, and the running total is advanced one bid at a time on
+//     wave-uniform values (the total's rounding is the sequential sum's), a
+//     bid that does not fit being passed over; once even the cheapest depth
+//     cannot fit, the offer stops.
+// Arithmetic in double without contraction, in the order written.
 // ---------------------------------------------------------------------------
 
 constexpr int COST_TAB_MAX = 32;
@@ -2332,21 +2345,20 @@ struct CostTable {
     int n;
 };
 
-// Piecewise-linear cost, first segment holding d; no contraction so the
-// rounding is that of the written operations.
 __device__ double table_cost(const CostTable &T, double d)
 {
 #pragma clang fp contract(off)
-    if (d <= T.t[0]) return T.c[0];
-    if (d >= T.t[T.n - 1]) return T.c[T.n - 1];
-    for (int i = 0; i + 1 < T.n; ++i) {
-        if (T.t[i] <= d && d <= T.t[i + 1]) {
-            const double r = (d - T.t[i]) / (T.t[i + 1] - T.t[i]);
-            return T.c[i] + r * (T.c[i + 1] - T.c[i]);
-        }
-    }
-    return T.c[T.n - 1];
+    int above = 0;   // table points at or below d
+    while (above < T.n && T.t[above] <= d) ++above;
+    if (above == 0) return T.c[0];
+    if (above == T.n) return T.c[T.n - 1];
+    const double w = (d - T.t[above - 1]) / (T.t[above] - T.t[above - 1]);
+    return T.c[above - 1] + w * (T.c[above] - T.c[above - 1]);
 }
+
+// Sort key of a bid: the value's bits (values are >= 0, so their bits order
+// like them); 0 for a request without a bid.
+__device__ __forceinline__ uint64_t bid_key(double v) { return (uint64_t)__double_as_longlong(v) + 1ull; }
 
 __global__ __launch_bounds__(COST_WG) void dcut_cost_kernel(const float *conf, const int32_t *max_depth, int B,
                                                             int K, CostTable T, double max_verify,
@@ -2354,63 +2366,112 @@ __global__ __launch_bounds__(COST_WG) void dcut_cost_kernel(const float *conf, c
 {
 #pragma clang fp contract(off)
     extern __shared__ double cost_smem[];
-    double *costd = cost_smem;                       // [K + 1] cost(d)
-    double *ben = cost_smem + (K + 1);               // [B] best benefit, -1 for no candidate
-    uint16_t *dst = (uint16_t *)(ben + B);           // [B] chosen depth (0 none)
-    uint16_t *order = dst + B;                       // [B] request at each rank
-    __shared__ int sh_cand[COST_WG / 64];
-    __shared__ uint8_t bad_req[COST_B_MAX];
+    int N = 1;
+    while (N < B) N <<= 1;
+    double *costd = cost_smem;                          // [K + 1]
+    uint64_t *key = (uint64_t *)(costd + (K + 1));      // [N] sort keys
+    uint16_t *who = (uint16_t *)(key + N);              // [N] request of each key
+    uint16_t *bid = who + N;                            // [B] bid depth (0: none)
+    __shared__ int8_t state[COST_B_MAX];                // -1 bad K_b, 0 no grant, 1 granted
+    __shared__ double sh_min;
     const int tid = threadIdx.x;
+
     for (int d = tid; d <= K; d += COST_WG) costd[d] = d == 0 ? 0.0 : table_cost(T, (double)d);
     __syncthreads();
-    int cand = 0;
-    for (int b = tid; b < B; b += COST_WG) {
-        const int Kb = max_depth ? max_depth[b] : K;
-        bad_req[b] = (Kb < 0 || Kb > K) ? 1 : 0;
-        double best = -1.0;
-        int dbest = 0;
-        if (Kb >= 1 && Kb <= K) {
-            double P = 1.0;
-            for (int d = 1; d <= Kb; ++d) {
-                P = P * (double)sanitize_conf(conf[(int64_t)b * K + d - 1]);
-                const double v = (P * (double)d) / costd[d];
-                if (v > best) { best = v; dbest = d; }
+    if (tid < 64) {
+        // the cheapest depth's cost: once it cannot fit, nothing can
+        double m = INFINITY;
+        for (int d = 1 + tid; d <= K; d += 64) m = fmin(m, costd[d]);
+        m = fmin(m, xchg_d<0>(m));
+        m = fmin(m, xchg_d<1>(m));
+        m = fmin(m, xchg_d<2>(m));
+        m = fmin(m, xchg_d<3>(m));
+        m = fmin(m, xchg_d<4>(m));
+        m = fmin(m, xchg_d<5>(m));
+        if (tid == 0) sh_min = m;
+    }
+
+    for (int b = tid; b < N; b += COST_WG) {
+        uint64_t kb = 0;
+        if (b < B) {
+            const int Kb = max_depth ? max_depth[b] : K;
+            const bool ok = Kb >= 0 && Kb <= K;
+            state[b] = ok ? 0 : -1;
+            double P = 1.0, best = 0.0;
+            int dbest = 0;
+            const float *cb = conf + (int64_t)b * K;
+            const int dn = ok ? Kb : 0;
+            for (int d0 = 0; d0 < dn; d0 += 8) {
+                float c8[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c8[i] = cb[min(d0 + i, dn - 1)];   // all eight in flight
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int d = d0 + i + 1;
+                    if (d <= dn) {
+                        P = P * (double)sanitize_conf(c8[i]);
+                        const double v = (P * (double)d) / costd[d];
+                        if (d == 1 || v > best) { best = v; dbest = d; }
+                    }
+                }
             }
-            ++cand;
+            bid[b] = (uint16_t)dbest;
+            if (dbest > 0) kb = bid_key(best);
         }
-        ben[b] = best;
-        dst[b] = (uint16_t)dbest;
-    }
-    cand = wave_sum_i(cand);
-    if (lane_id() == 0) sh_cand[wave_id()] = cand;
-    __syncthreads();
-    int ncand = 0;
-    for (int w = 0; w < COST_WG / 64; ++w) ncand += sh_cand[w];
-    // rank of each candidate: how many candidates precede it
-    for (int b = tid; b < B; b += COST_WG) {
-        if (dst[b] == 0) continue;
-        const double v = ben[b];
-        int r = 0;
-        for (int o = 0; o < B; ++o) {
-            const double w = ben[o];
-            r += (dst[o] != 0) && (w > v || (w == v && o < b));
-        }
-        order[r] = (uint16_t)b;
+        key[b] = kb;
+        who[b] = (uint16_t)min(b, B - 1);
     }
     __syncthreads();
-    // fill the budget in rank order (sequential: a candidate that does not fit
-    // is skipped and a later, cheaper one may still fit)
-    if (tid == 0) {
-        double total = 0.0;
-        for (int i = 0; i < ncand; ++i) {
-            const int b = order[i];
-            const double c = costd[dst[b]];
-            if (total + c <= max_verify) total = total + c;
-            else dst[b] = 0;
+
+    // bitonic sort: descending by key, ascending by request on equal keys
+    for (int size = 2; size <= N; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < N / 2; t += COST_WG) {
+                const int lo = 2 * t - (t & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a = key[lo], c = key[hi];
+                const int wa = who[lo], wc = who[hi];
+                const bool lo_first = a > c || (a == c && wa < wc);
+                if (lo_first != desc) {
+                    key[lo] = c;
+                    key[hi] = a;
+                    who[lo] = (uint16_t)wc;
+                    who[hi] = (uint16_t)wa;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    if (tid < 64) {
+        const int lane = tid;
+        const double minc = sh_min;
+        double spent = 0.0;
+        bool open = true;
+        for (int h0 = 0; h0 < B && open; h0 += 64) {
+            const int r = h0 + lane;
+            const bool has = r < B && key[r] != 0;
+            const int req = has ? who[r] : 0;
+            const double c = has ? costd[bid[req]] : 0.0;
+            const uint64_t bids = __ballot(has);   // a prefix of the lanes: bids sort first
+            uint64_t granted = 0;
+            for (int i = 0; i < 64; ++i) {
+                if (!((bids >> i) & 1ull) || !(spent + minc <= max_verify)) {
+                    open = false;
+                    break;
+                }
+                const double ci = readlane_d(c, i);
+                if (spent + ci <= max_verify) {
+                    spent = spent + ci;
+                    granted |= 1ull << i;
+                }
+            }
+            if ((granted >> lane) & 1ull) state[req] = 1;
         }
     }
     __syncthreads();
-    for (int b = tid; b < B; b += COST_WG) depth_out[b] = bad_req[b] ? -1 : (int32_t)dst[b];
+    for (int b = tid; b < B; b += COST_WG) depth_out[b] = state[b] < 0 ? -1 : (state[b] ? (int32_t)bid[b] : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -2877,6 +2938,10 @@ Params base_params(int32_t B, int32_t K, int32_t V, sv_dtype dt, int mode, const
     P.cpr_max = L.cpr_max;
     P.row_cus = cu_count();
     P.row_skew = mode == MODE_GREEDY ? ROW_SKEW_GREEDY : ROW_SKEW_LSE;
+    // SPECVERIFY_CHUNK=n: force n chunks per logit row in the row pass (a
+    // different decomposition of the same work; outputs must not change)
+    const char *ce = getenv("SPECVERIFY_CHUNK");
+    P.chunks = ce ? std::max(0, atoi(ce)) : 0;
     P.cs = (int)ceil_div(nvec_max(V, P.bf16 ? 8 : 4), (int64_t)UNIT_E / (P.bf16 ? 8 : 4));
     // A batch whose units would fill few wave slots splits each unit over two
     // or four waves (measured on MI355X on the B = 4, K = 3 shape).
@@ -3254,8 +3319,11 @@ sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth, int32_
         T.t[i] = t;
         T.c[i] = c;
     }
-    const size_t lds = sizeof(double) * (size_t)(K + 1 + B) + 2 * sizeof(uint16_t) * (size_t)B;
-    if (lds > 60 * 1024) return SV_ERR_UNSUPPORTED;
+    int64_t N = 1;
+    while (N < B) N <<= 1;
+    const size_t lds = sizeof(double) * (size_t)(K + 1) + (sizeof(uint64_t) + sizeof(uint16_t)) * (size_t)N +
+                       sizeof(uint16_t) * (size_t)B;
+    if (lds > 58 * 1024) return SV_ERR_UNSUPPORTED;
     (void)hipGetLastError();
     hipLaunchKernelGGL(dcut_cost_kernel, dim3(1), dim3(COST_WG), lds, stream, conf, max_depth, B, K, T, max_verify,
                        depth_out);

@@ -53,6 +53,12 @@
  *     depth_out[b] = -1; spec_verify_last_error names the first such
  *     request).  A debugging aid: it synchronises the stream, so it is not
  *     for graph capture.
+ *   Decomposition override.  SPECVERIFY_CHUNK=n (n > 0) makes the row
+ *     statistics pass split every logit row into n chunks (at most one per
+ *     4 KiB batch and 256 per row) instead of the count it picks from the
+ *     grid.  A test and tuning aid: greedy outputs, dcut depths and sampled
+ *     tokens do not depend on it; sampled p/q and the confidence move by
+ *     rounding only.
  *   Limits.  1 <= B <= 4096, 0 <= K <= 1024, 1 <= V <= 2000000.
  */
 #ifndef SPECVERIFY_H
@@ -329,28 +335,29 @@ sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_
  * of keeping more drafted positions against a profiled runtime cost and
  * steering verification toward high-confidence prefixes under a shared
  * budget ([Remio], section "Come AngelSpec rende DFly più selettivo").
- * Built as a per-request choice of depth followed by a greedy fill of a cost
- * budget (all arithmetic in double, in the order written):
- *   cost(d)  piecewise-linear in the latency table (table_depth[i],
- *            table_cost[i]): table_cost[0] for d <= table_depth[0],
- *            table_cost[n-1] for d >= table_depth[n-1], else on the first
- *            segment i with table_depth[i] <= d <= table_depth[i+1]:
- *            table_cost[i] + r * (table_cost[i+1] - table_cost[i]),
- *            r = (d - table_depth[i]) / (table_depth[i+1] - table_depth[i]);
- *   per request b with K_b = max_depth[b] (NULL => K) in [1, K]:
- *            P_d = P_{d-1} * s(conf[b, d-1]) from P_0 = 1 (s as in
- *            dcut_allocate), benefit(d) = (P_d * d) / cost(d), and d*_b =
- *            the smallest d in [1, K_b] with the largest benefit;
- *   candidates in order of benefit descending, then b ascending, each
- *   admitted iff the admitted costs so far plus cost(d*_b) <= max_verify.
- *   depth_out[b] = d*_b when admitted, 0 when not (or K_b = 0), -1 when K_b
- *   is outside [0, K].
+ * Each request bids one depth, and a cost budget is spent on the best bids
+ * (all arithmetic in double, in the order written):
+ *   cost(d)  the latency table (table_depth[i], table_cost[i]) read as a
+ *            function of depth: linear between neighbouring points,
+ *            table_cost[0] before the first point and table_cost[n-1] from
+ *            the last one on; at a table depth, that point's own cost;
+ *   request b with K_b = max_depth[b] (NULL => K) in [1, K] bids the depth d
+ *            in [1, K_b] with the largest value (P(d) * d) / cost(d), where
+ *            P(d) is the product of s(conf[b, 0..d-1]) in order (s as in
+ *            dcut_allocate); the smallest such d on ties;
+ *   the budget is offered to the bids by value descending, then b
+ *   ascending: a bid is granted iff the costs granted so far plus its own
+ *   stay <= max_verify; a bid that does not fit is passed over (a later,
+ *   cheaper one may still fit).
+ *   depth_out[b] = the granted depth, 0 when not granted (or K_b = 0), -1
+ *   when K_b is outside [0, K].
  *   conf         [B, K] float (device)
  *   table_depth, table_cost  HOST arrays of table_n (1..32) doubles: depths
  *                strictly increasing, costs finite and > 0 (copied into the
  *                launch; the call keeps no reference)
  *   max_verify   finite, >= 0
- *   B <= 4096 and B*8 + K*8 + B*4 <= 60 KiB of LDS (SV_ERR_UNSUPPORTED). */
+ *   B <= 4096 and 8 (K + 1) + 10 P + 2 B <= 58 KiB of LDS, P the power of two
+ *   at or above B (SV_ERR_UNSUPPORTED). */
 sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth,
                              int32_t B, int32_t K,
                              const double *table_depth, const double *table_cost,

@@ -580,50 +580,38 @@ int oracle_accept_stats(const int32_t *num_accepted, const int32_t *depth, int32
     return 0;
 }
 
-/* Cost-aware D-cut: the pages describe D-cut as weighing the expected value
- * of keeping more drafted positions against a profiled runtime cost
- * ([Remio], section "Come AngelSpec rende DFly più selettivo").  Built here
- * as a per-request benefit/cost choice followed by a greedy fill of a cost
- * budget:
- *   cost(d): piecewise-linear in the latency table (tdepth[i], tcost[i]),
- *     tdepth strictly increasing; cost(d) = tcost[0] for d <= tdepth[0],
- *     tcost[n-1] for d >= tdepth[n-1], else on the first segment i with
- *     tdepth[i] <= d <= tdepth[i+1]: tcost[i] + r*(tcost[i+1] - tcost[i]),
- *     r = (d - tdepth[i]) / (tdepth[i+1] - tdepth[i])  (all in double);
- *   for request b with K_b = max_depth[b] (NULL => K) in [1, K]:
- *     P_d = P_{d-1} * s(conf[b, d-1]) in double from P_0 = 1 (s as in
- *     oracle_dcut_allocate), benefit(d) = (P_d * d) / cost(d), and
- *     d*_b = the smallest d in [1, K_b] with the largest benefit;
- *   candidates in order of benefit descending, then b ascending, each
- *   admitted iff total + cost(d*_b) <= max_verify (then total += cost);
- *   depth_out[b] = d*_b if admitted, 0 if not or K_b = 0, -1 if K_b is
- *   outside [0, K].
+/* Cost-aware D-cut.  [Remio] (section "Come AngelSpec rende DFly più
+ * selettivo") has D-cut weigh the expected value of more drafted positions
+ * against a profiled runtime cost, and [DeepDive] sketches a scheduler that
+ * scores each request's depth by benefit per unit of cost and then spends a
+ * verification budget on the best scores.  The rule built here:
+ *
+ *   cost(d): the latency table (tdepth[i], tcost[i]), tdepth strictly
+ *     increasing, read as a function of depth that is linear between
+ *     neighbouring table points and constant before the first point and
+ *     after the last.  At a table depth it is that point's own cost.
+ *   value of request b at depth d: V_b(d) = (P_b(d) * d) / cost(d), where
+ *     P_b(d) = s(conf[b,0]) * ... * s(conf[b,d-1]) multiplied in order in
+ *     double (s as in oracle_dcut_allocate).
+ *   request b (K_b = max_depth[b], NULL => K, in [1, K]) bids the depth in
+ *     [1, K_b] with the largest value, the smallest such depth on ties.
+ *   The budget max_verify is then offered to the bids one at a time, in
+ *     order of value (highest first, lower request index on ties).  A bid
+ *     whose cost fits in what is left (spent + cost <= max_verify, spent
+ *     summed in offer order) is granted its depth; one that does not fit
+ *     gets 0 and the offer moves on, so a later, cheaper bid may still fit.
+ *   depth_out[b] = the granted depth, 0 (not granted, or K_b = 0), or -1
+ *     (K_b outside [0, K]).
  * Returns 1 for B < 1, K < 0 or n < 1. */
 double oracle_dcut_cost(const double *tdepth, const double *tcost, int32_t n, double d)
 {
-    if (d <= tdepth[0]) return tcost[0];
-    if (d >= tdepth[n - 1]) return tcost[n - 1];
-    for (int32_t i = 0; i + 1 < n; ++i) {
-        if (tdepth[i] <= d && d <= tdepth[i + 1]) {
-            double r = (d - tdepth[i]) / (tdepth[i + 1] - tdepth[i]);
-            return tcost[i] + r * (tcost[i + 1] - tcost[i]);
-        }
-    }
-    return tcost[n - 1];
-}
-
-typedef struct {
-    double benefit;
-    double cost;
-    int32_t b, d;
-} cost_cand;
-
-static int cost_cmp(const void *pa, const void *pb)
-{
-    const cost_cand *a = (const cost_cand *)pa, *b = (const cost_cand *)pb;
-    if (a->benefit > b->benefit) return -1;
-    if (a->benefit < b->benefit) return 1;
-    return (a->b < b->b) ? -1 : (a->b > b->b);
+    int32_t above = 0;                 /* table points at or below d */
+    while (above < n && tdepth[above] <= d) ++above;
+    if (above == 0) return tcost[0];
+    if (above == n) return tcost[n - 1];
+    /* tdepth[above - 1] <= d < tdepth[above] */
+    double w = (d - tdepth[above - 1]) / (tdepth[above] - tdepth[above - 1]);
+    return tcost[above - 1] + w * (tcost[above] - tcost[above - 1]);
 }
 
 int oracle_dcut_allocate_cost(const float *conf, const int32_t *max_depth, int32_t B, int32_t K,
@@ -631,35 +619,36 @@ int oracle_dcut_allocate_cost(const float *conf, const int32_t *max_depth, int32
                               int32_t *depth_out)
 {
     if (B < 1 || K < 0 || n < 1) return 1;
-    cost_cand *c = (cost_cand *)malloc(sizeof(cost_cand) * (size_t)B);
-    int64_t nc = 0;
+    double *value = (double *)malloc(sizeof(double) * (size_t)B);
+    int32_t *bid = (int32_t *)malloc(sizeof(int32_t) * (size_t)B);
+    char *open_bid = (char *)calloc((size_t)B, 1);
     for (int64_t b = 0; b < B; ++b) {
         int32_t Kb = max_depth ? max_depth[b] : K;
-        if (Kb < 0 || Kb > K) { depth_out[b] = -1; continue; }
-        depth_out[b] = 0;
-        if (Kb == 0) continue;
-        double P = 1.0, best = -1.0;
-        int32_t dbest = 1;
+        depth_out[b] = (Kb < 0 || Kb > K) ? -1 : 0;
+        if (Kb < 1 || Kb > K) continue;
+        double P = 1.0;
         for (int32_t d = 1; d <= Kb; ++d) {
             P = P * (double)sanitize_conf(conf[b * K + d - 1]);
             double v = (P * (double)d) / oracle_dcut_cost(tdepth, tcost, n, (double)d);
-            if (v > best) { best = v; dbest = d; }
+            if (d == 1 || v > value[b]) { value[b] = v; bid[b] = d; }
         }
-        c[nc].benefit = best;
-        c[nc].cost = oracle_dcut_cost(tdepth, tcost, n, (double)dbest);
-        c[nc].b = (int32_t)b;
-        c[nc].d = dbest;
-        ++nc;
+        open_bid[b] = 1;
     }
-    qsort(c, (size_t)nc, sizeof(cost_cand), cost_cmp);
-    double total = 0.0;
-    for (int64_t i = 0; i < nc; ++i) {
-        if (total + c[i].cost <= max_verify) {
-            total = total + c[i].cost;
-            depth_out[c[i].b] = c[i].d;
+    double spent = 0.0;
+    for (;;) {
+        int64_t best = -1;             /* highest open bid, lowest index on ties */
+        for (int64_t b = 0; b < B; ++b)
+            if (open_bid[b] && (best < 0 || value[b] > value[best])) best = b;
+        if (best < 0) break;
+        open_bid[best] = 0;
+        double c = oracle_dcut_cost(tdepth, tcost, n, (double)bid[best]);
+        if (spent + c <= max_verify) {
+            spent = spent + c;
+            depth_out[best] = bid[best];
         }
     }
-    free(c);
+    free(value);
+    free(bid);
+    free(open_bid);
     return 0;
 }
-

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 from parity import dev, host
 
 pytestmark = pytest.mark.gpu
@@ -80,18 +81,26 @@ def _rand_table(g, n):
     return tuple(zip(t.tolist(), c.tolist()))
 
 
-@pytest.mark.parametrize("B,K", [(1, 1), (5, 3), (64, 16), (300, 64), (4096, 16)])
+def _int_table(g, n):
+    """Integer table depths, so that integer d lands on table points."""
+    t = np.cumsum(g.integers(1, 4, n)).astype(np.float64)
+    c = np.cumsum(g.uniform(0.05, 1.0, n))
+    return tuple(zip(t.tolist(), c.tolist()))
+
+
+@pytest.mark.parametrize("B,K", [(1, 1), (5, 3), (64, 16), (300, 64), (4096, 16), (4096, 1024)])
 def test_dcut_cost_random_bit_exact(B, K):
     print(f"\n[case] dcut_allocate_cost random B={B} K={K}", flush=True)
     import draft_verification_verify_amd as sv
     g = np.random.default_rng(B * 7 + K)
-    for trial in range(3):
+    for trial in range(4):
         conf = g.uniform(0.0, 1.0, (B, K)).astype(np.float32)
         conf[g.random((B, K)) < 0.05] = np.float32("nan")
         conf[g.random((B, K)) < 0.03] = 1.5
         conf[g.random((B, K)) < 0.03] = 1.0
         md = g.integers(-1, K + 2, B).astype(np.int32) if trial != 1 else None
-        table = oracle.DEFAULT_COST_TABLE if trial == 0 else _rand_table(g, int(g.integers(1, 33)))
+        table = (oracle.DEFAULT_COST_TABLE if trial == 0 else
+                 _int_table(g, int(g.integers(1, 33))) if trial == 3 else _rand_table(g, int(g.integers(1, 33))))
         budget = float(g.uniform(0.0, 3.0 * B))
         want = oracle.dcut_allocate_cost(conf, budget, md, table)
         got = host(sv.dcut_allocate_cost(dev(conf), budget, dev(md), table))
@@ -108,3 +117,53 @@ def test_dcut_cost_ties_and_budget_edges():
         assert np.array_equal(got, want), budget
     # equal benefits go in request order
     assert host(sv.dcut_allocate_cost(dev(conf), 9.0)).tolist()[:4] == [16, 16, 16, 0]
+
+
+# ------------------------------------ GPU confidence -> GPU D-cut, end to end ----
+
+def _prefix_conf(conf, max_depth):
+    """fp32 running products of the sanitised confidence (the D-cut rule),
+    0 outside each request's window."""
+    B, K = conf.shape
+    c = np.nan_to_num(conf.astype(np.float32), nan=0.0)
+    c = np.clip(c, np.float32(0.0), np.float32(1.0)).astype(np.float32)
+    out = np.zeros((B, K), np.float32)
+    for b in range(B):
+        Kb = K if max_depth is None else int(max_depth[b])
+        run = np.float32(1.0)
+        for k in range(max(0, min(Kb, K))):
+            run = c[b, k] if k == 0 else np.float32(run * c[b, k])
+            out[b, k] = run
+    return out
+
+
+def _taken(depth):
+    """Entries (b, k), 1 <= k < d_b, that a depth vector takes beyond the floor."""
+    return {(b, k) for b, d in enumerate(depth.tolist()) for k in range(1, max(d, 0))}
+
+
+@pytest.mark.parametrize("name,seed", [("dcut_ragged", 0), ("dcut_ragged", 1), ("dcut_ragged", 2), ("mixed", 0)])
+def test_dcut_from_gpu_confidence_end_to_end(name, seed):
+    print(f"\n[case] GPU confidence -> GPU dcut_allocate -> ragged sample: {name} seed {seed}", flush=True)
+    import draft_verification_verify_amd as sv
+    from parity import compare_sample
+    w = synth.dcut_ragged(seed, T=1.0) if name == "dcut_ragged" else synth.mixed(seed)
+    md = None if name == "dcut_ragged" else w.max_depth
+    conf_g = sv.draft_confidence(dev(w.draft), dev(md))
+    depth_g = host(sv.dcut_allocate(conf_g, w.budget, dev(md)))
+    conf_o = oracle.draft_confidence(w.draft, md)
+    depth_o = oracle.dcut_allocate(conf_o, w.budget, md)
+    assert int(depth_g.sum()) == int(depth_o.sum())
+    c = _prefix_conf(conf_o, md).astype(np.float64)
+    extra, missing = _taken(depth_g) - _taken(depth_o), _taken(depth_o) - _taken(depth_g)
+    assert len(extra) == len(missing)
+    # a difference is allowed only between entries whose prefix confidence
+    # (the oracle's) differs by less than 1e-6 relative
+    for e in extra:
+        for f in missing:
+            assert abs(c[e] - c[f]) < 1e-6 * max(c[e], c[f]), (e, f, c[e], c[f])
+    # the verify the bench times, on the GPU's own depths
+    out, n, p, q = sv.verify_sample(dev(w.target), dev(w.draft), dev(w.tokens), dev(w.temperature),
+                                    dev(w.u_accept), dev(w.u_sample), dev(depth_g))
+    torch.cuda.synchronize()
+    compare_sample(w, host(out), host(n), host(p), host(q), depth_g).assert_ok(f"{name} ragged")

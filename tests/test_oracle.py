@@ -710,6 +710,26 @@ def test_dcut_cost_interpolation_hand_values():
         assert abs(oracle.dcut_cost(d) - c) < 1e-15, (d, oracle.dcut_cost(d), c)
 
 
+def test_dcut_cost_table_points_and_segments():
+    # at a table depth the cost is that point's own value, bit for bit; between two
+    # points it lies on the chord (checked against a fraction computed separately)
+    from fractions import Fraction
+    g = np.random.default_rng(17)
+    for trial in range(20):
+        n = int(g.integers(1, 12))
+        t = np.cumsum(g.integers(1, 5, n)).astype(np.float64)
+        c = np.cumsum(g.uniform(0.05, 2.0, n))
+        table = tuple(zip(t.tolist(), c.tolist()))
+        for ti, ci in table:
+            assert oracle.dcut_cost(ti, table) == ci
+        assert oracle.dcut_cost(t[0] - 0.5, table) == c[0] and oracle.dcut_cost(t[-1] + 3, table) == c[-1]
+        for i in range(n - 1):
+            d = float(t[i] + 0.5 * (t[i + 1] - t[i]))
+            exact = Fraction(c[i]) + (Fraction(d) - Fraction(t[i])) / (Fraction(t[i + 1]) - Fraction(t[i])) \
+                * (Fraction(c[i + 1]) - Fraction(c[i]))
+            assert abs(oracle.dcut_cost(d, table) - float(exact)) <= 4e-16 * float(exact)
+
+
 def test_dcut_cost_choices_closed_forms():
     # confidence 1 everywhere: benefit d / cost(d) grows with d on this table, so the
     # whole window is chosen (16 / 3.0 at K_b = 16; 5 / 1.625 beats 4 / 1.5 at K_b = 5)
@@ -740,6 +760,8 @@ def test_dcut_cost_budget_fill_order_and_skip():
     conf[1, 0] = 0.5
     assert oracle.dcut_allocate_cost(conf, 2.5).tolist() == [0, 1]
     assert oracle.dcut_allocate_cost(conf, 4.0).tolist() == [16, 1]
+    # with room for one of the two, the higher value (request 0) is offered first
+    assert oracle.dcut_allocate_cost(conf, 3.0).tolist() == [16, 0]
     # invariant on random inputs: admitted cost within budget, and every candidate left
     # out met a budget too small for it
     g = np.random.default_rng(11)

@@ -43,6 +43,18 @@ MUTATIONS = {
     "ee_greedy_bonus_row_unchecked": ("if (row_check(zr, dtype, V) != ROW_OK) bad = 1;\n                else emit",
                                       "if (0) bad = 1;\n                else emit"),
     "ee_draw_uniform_unchecked": ("if (!bad && bad_uniform(u_sample[b])) bad = 1;", "if (0) bad = 1;"),
+    # temperature range and large logits
+    "softmax_without_max_shift": ("    double M = -INFINITY;\n    for (int64_t v = 0; v < V; ++v) {\n"
+                                  "        double z = logit_at(row, dtype, v);\n        if (z > M) M = z;\n    }",
+                                  "    double M = 0.0;"),
+    "temperature_floor_1e_6": ("(T > 0.0f && isfinite(T))", "(T >= 1e-6f && isfinite(T))"),
+    # cost-aware D-cut
+    "cost_segment_start_shifted": ("return tcost[above - 1] + w * (tcost[above] - tcost[above - 1]);",
+                                   "return tcost[above] + w * (tcost[above] - tcost[above - 1]);"),
+    "cost_bid_ties_to_largest_depth": ("if (d == 1 || v > value[b])", "if (d == 1 || v >= value[b])"),
+    "cost_offer_lowest_value_first": ("(best < 0 || value[b] > value[best])", "(best < 0 || value[b] < value[best])"),
+    "cost_unfit_bid_ends_offer": ("        if (spent + c <= max_verify) {\n            spent = spent + c;",
+                                  "        if (!(spent + c <= max_verify)) break;\n        {\n            spent = spent + c;"),
 }
 
 
