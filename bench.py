@@ -130,6 +130,7 @@ def pmc_summary(dirs):
     for ctr, kernels in per.items():
         row = [v for n, v in kernels.items() if ROW_PASS_KERNEL in n]
         cal = [v for n, v in kernels.items() if CALIB_KERNEL in n]
+        rdc = [v for n, v in kernels.items() if "read_ceiling_kernel" in n]
         if not row or not cal:
             continue
         row_kib = float(np.mean([x for v in row for x in v.values()]))
@@ -138,6 +139,12 @@ def pmc_summary(dirs):
         res["counters"][ctr] = {"row_pass_kib_per_dispatch": row_kib, "copy_kib_per_dispatch": cal_kib,
                                 "copy_known_bytes": CALIB_BYTES, "scale": factor,
                                 "row_pass_bytes_per_launch": row_kib * 1024.0 * factor}
+        if rdc:
+            # the read-ceiling kernel reads CALIB_BYTES with the row pass's loads
+            rd_kib = float(np.mean([x for v in rdc for x in v.values()]))
+            res["counters"][ctr]["read_ceiling_kib_per_dispatch"] = rd_kib
+            if rd_kib > 0:
+                res["counters"][ctr]["read_scale"] = CALIB_BYTES / (rd_kib * 1024.0)
     res["source_sha256"] = source_sha256()
     print(json.dumps(res, indent=1))
 
@@ -231,9 +238,15 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.neg(src, out=dst)
+        # a second calibration read with the row pass's own load instruction
+        # (16-byte nontemporal loads): the read-ceiling kernel over the same bytes
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            sv.read_ceiling(src, sink, stream)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_pass": "done", "row_pass_kernel": ROW_PASS_KERNEL,
-                          "calibration": f"torch.neg over {CALIB_BYTES} B of fp32 (reads and writes that many)"}))
+                          "calibration": f"torch.neg over {CALIB_BYTES} B of fp32 (reads and writes that many); "
+                                         f"read_ceiling_kernel over the same {CALIB_BYTES} B (reads that many)"}))
         return
 
     if args.early_exit_ends:
@@ -248,22 +261,18 @@ def main():
                           "mean_accepted": float(nacc.float().mean().item())}))
         return
 
-    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    wall, per, _ = timed(step, args.steps, args.warmup)
-    # the same steps with an event after each, for the spread only
-    _, per_ev, _ = timed(step, args.steps, 2, per_step=True)
-    ms = float(np.mean(per))
-    value = rows / (ms * 1e-3)
-    # the same steps again with the library's per-kernel events armed (the
-    # event markers add a few microseconds per call, so they stay out of the
-    # headline region)
-    log(f"timing {args.steps} steps with per-kernel events")
-    _, sper, st = timed(step, args.steps, 2, stages=True)
+    # The library's per-kernel events (on the launch stream, around each
+    # kernel of every timed call) for the roofline's kernel duration; the
+    # event markers add a few microseconds per call, so this pass is separate
+    # from the headline region.  It runs first, with the plain-read pass, so
+    # that the headline region runs on a GPU that has left its idle clocks
+    # (after only a few warm-up steps from idle, steps ran 2-5 us slower).
+    log(f"timing {args.steps} steps with per-kernel events after {args.warmup} warm-up steps")
+    _, sper, st = timed(step, args.steps, args.warmup, stages=True)
     st = np.asarray(st, dtype=np.float64)
     stage_ms = st.mean(axis=0)
     rp_ms = float(stage_ms[0])
     achieved = rp_bytes / (rp_ms * 1e-3) / 1e9
-    n_mean = float(nacc.float().mean().item())
     # practical ceiling: a plain read of as many bytes as the row pass reads,
     # alternating two buffers so the 256 MB MALL serves none of it
     log("timing the plain read of the row pass's bytes")
@@ -273,6 +282,13 @@ def main():
     ceil_ms = float(np.mean(cper))
     ceil_gbs = rp_bytes / (ceil_ms * 1e-3) / 1e9
     del rbufs
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps (headline)")
+    wall, per, _ = timed(step, args.steps, args.warmup)
+    # the same steps with an event after each, for the spread only
+    _, per_ev, _ = timed(step, args.steps, 2, per_step=True)
+    ms = float(np.mean(per))
+    value = rows / (ms * 1e-3)
+    n_mean = float(nacc.float().mean().item())
     sha = source_sha256()
     traffic = None
     valu_busy = None
@@ -375,11 +391,36 @@ def main():
                     sv.verify_greedy(ct, ctok, out_tokens=cout, num_accepted=cn, workspace=ws, stream=stream)
             _, cper, _ = timed(cstep, steps2, warm2)
             cms = float(np.mean(cper))
+            _, _, cst = timed(cstep, steps2, 2, stages=True)
+            cstage = np.asarray(cst, dtype=np.float64).mean(axis=0)
+            # the same calls replayed from a HIP graph (20 calls per graph):
+            # GPU time per call without the host's enqueue work in between
+            NG = 20
+
+            def cgraph_body(mode=mode):
+                for _ in range(NG):
+                    if mode == "sample":
+                        sv.verify_sample(ct, cd, ctok, cT, cua, cus, out_tokens=cout, num_accepted=cn,
+                                         want_probs=False, workspace=ws)
+                    else:
+                        sv.verify_greedy(ct, ctok, out_tokens=cout, num_accepted=cn, workspace=ws)
+            cgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(cgraph):
+                cgraph_body()
+            torch.cuda.synchronize()
+            _, gper_c, _ = timed(lambda i: cgraph.replay(), max(steps2 // 4, 5), 3)
+            gms_c = float(np.mean(gper_c)) / NG
+            del cgraph
             cb = synth.algorithmic_bytes(wc, mode)
             crow = synth.rows_verified(wc)
-            sec[f"mtp_chat_B4_K3_{mode}"] = {"rows_per_s": crow / (cms * 1e-3), "ms": cms,
-                                             "GB_s": cb / (cms * 1e-3) / 1e9,
-                                             "pct_hbm_peak": 100 * cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            sec[f"mtp_chat_B4_K3_{mode}"] = {
+                "rows_per_s": crow / (cms * 1e-3), "ms": cms,
+                "GB_s": cb / (cms * 1e-3) / 1e9, "pct_hbm_peak": 100 * cb / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "graph_replay_ms_per_call": gms_c, "graph_replay_rows_per_s": crow / (gms_c * 1e-3),
+                "stage_ms_with_events": {"row_pass": float(cstage[0]), "finish": float(cstage[1]),
+                                         "draw": float(cstage[2])},
+                "note": "ms: eager calls back to back through the binding; graph_replay: 20 calls per HIP "
+                        "graph, replayed; stage_ms: the library's per-kernel events (each adds ~1 us)"}
         # D-cut pipeline: confidence -> dcut_allocate(384) -> ragged sampled verify
         conf = torch.empty((B, K), dtype=torch.float32, device="cuda")
         depth = torch.empty((B,), dtype=torch.int32, device="cuda")
@@ -399,6 +440,34 @@ def main():
             "bytes_per_step": int((B * K + prow + int(dep.sum())) * V * 2),
             "note": "confidence pass reads all 1024 draft rows; ragged verify reads sum(d_b+1) target "
                     "and sum(d_b) draft rows"}
+        # the allocation alone, on the pipeline's last confidences
+        _, aper, _ = timed(lambda i: sv.dcut_allocate(conf, w.budget, depth_out=depth, stream=stream), steps2, warm2)
+        sec["dcut_allocate_B64_K16_budget384"] = {
+            "ms": float(np.mean(aper)), "keys": B * K,
+            "note": "global top-k of fp32 prefix confidence (one workgroup, LDS radix select)"}
+        # the ragged verify alone at the D-cut depths: reads sum(d_b + 1)
+        # target and sum(d_b) draft rows of the padded buffers
+        rsum = int(dep.sum())
+        ralgo = (prow + rsum) * V * 2
+
+        def vstep(i):
+            t, d = copies[i % ncopy]
+            sv.verify_sample(t, d, tok, T, ua, us, depth, out_tokens=out, num_accepted=nacc, p_draft=pd,
+                             q_draft=qd, workspace=ws, stream=stream)
+        _, vper, _ = timed(vstep, steps2, warm2)
+        _, _, vst = timed(vstep, steps2, 2, stages=True)
+        vms = float(np.mean(vper))
+        vstage = np.asarray(vst, dtype=np.float64).mean(axis=0)
+        vrp_bytes = 2 * rsum * V * 2
+        sec["dcut_ragged_verify_B64_K16_budget384"] = {
+            "verified_rows_per_s": prow / (vms * 1e-3), "ms": vms, "rows_per_step": prow,
+            "algorithmic_bytes_per_step": ralgo, "GB_s": ralgo / (vms * 1e-3) / 1e9,
+            "pct_hbm_peak": 100 * ralgo / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "stage_ms_with_events": {"row_pass": float(vstage[0]), "finish": float(vstage[1]),
+                                     "draw": float(vstage[2])},
+            "row_pass_GB_s": vrp_bytes / (float(vstage[0]) * 1e-3) / 1e9,
+            "note": "spec_verify_sample alone at the D-cut depths (budget 384): sum(d_b + 1) target and "
+                    "sum(d_b) draft rows; padded [B,K+1,V] buffers, rotated"}
         # the same pipeline with the confidence pass's row statistics reused:
         # the verify streams target rows only (plus the drawn draft row)
         dstats = torch.empty((B, K, 2), dtype=torch.float64, device="cuda")
@@ -465,7 +534,9 @@ def main():
         del copies
         # mixed fp32 batch: per-request K_b and T_b, dcut_allocate(512), one sampled launch
         wm = synth.mixed(args.seed)
-        mt, md = dev(wm.target), dev(wm.draft)
+        mt0, md0 = dev(wm.target), dev(wm.draft)
+        # two copies of 1.28 GB each: the 256 MB memory-side cache serves none of a step
+        mcopies = [(mt0, md0), (mt0.clone(), md0.clone())]
         mtok, mT, mua, mus = dev(wm.tokens), dev(wm.temperature), dev(wm.u_accept), dev(wm.u_sample)
         mK = dev(wm.max_depth)
         mconf = torch.empty((wm.B, wm.K), dtype=torch.float32, device="cuda")
@@ -474,6 +545,7 @@ def main():
         mn = torch.empty((wm.B,), dtype=torch.int32, device="cuda")
 
         def mstep(i):
+            mt, md = mcopies[i % 2]
             sv.draft_confidence(md, mK, conf=mconf, workspace=ws, stream=stream)
             sv.dcut_allocate(mconf, wm.budget, mK, depth_out=mdep, stream=stream)
             sv.verify_sample(mt, md, mtok, mT, mua, mus, mdep, out_tokens=mout, num_accepted=mn,
@@ -485,7 +557,8 @@ def main():
         sec["mixed_fp32_B64_V152064_budget512"] = {
             "verified_rows_per_s": mrow / (mms * 1e-3), "ms": mms, "rows_per_step": mrow,
             "note": "confidence over all max_depth draft rows + dcut_allocate + one mixed-K/T sampled launch; "
-                    "inputs not rotated (fits the memory-side cache partly)"}
+                    "two input copies rotated"}
+        del mcopies, mt0, md0
         result["secondary"] = sec
 
     # ----------------------------------------------------------- CPU baseline

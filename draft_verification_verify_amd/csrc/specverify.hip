@@ -2320,24 +2320,30 @@ __global__ __launch_bounds__(WG) void read_ceiling_kernel(const uint4 *buf_, int
 
 // ---------------------------------------------------------------------------
 // Cost-aware D-cut: one workgroup of 1024 threads.
-//  1. cost(d) for every depth into LDS: the latency table read as linear
-//     between neighbouring points, constant outside them.
-//  2. one thread per request: the value (P(d) * d) / cost(d) of each depth,
-//     the prefix product P in order in double; the request bids its best
-//     depth (smallest on ties).  Confidence loads go out eight at a time.
-//  3. the bids are sorted in LDS by (value desc, request asc): a bitonic
-//     sort over the next power of two, requests without a bid last.
-//  4. wave 0 offers the budget in that order: lane l holds the cost of bid
-//     64 h + l, and the running total is advanced one bid at a time on
-//     wave-uniform values (the total's rounding is the sequential sum's), a
-//     bid that does not fit being passed over; once even the cheapest depth
-//     cannot fit, the offer stops.
+//  1. the latency table and (small inputs) the confidences into LDS, all
+//     loads in flight together; cost(d) for every depth: the table read as
+//     linear between neighbouring points, constant outside them.
+//  2. the bids.  Small inputs (B * K up to 4096 pairs): one thread per
+//     request forms its prefix products in order (double) into LDS, then one
+//     thread per (request, depth) pair forms the value (P * d) / cost(d), then
+//     one thread per request takes the first largest value.  Larger inputs:
+//     one thread per request does all three in order, its confidence loads
+//     sixteen at a time.  Either way each P is the sequential product.
+//  3. the bids are ordered by (value desc, request asc): rank by counting
+//     for up to 256 requests, a bitonic sort in LDS above that; requests
+//     without a bid go last.
+//  4. wave 0 offers the budget in that order.  Lane l holds the cost of bid
+//     64 h + l, and the running total advances one bid at a time on
+//     wave-uniform values with selects (no branch per bid), so it rounds as
+//     the sequential sum does; a bid that does not fit is passed over.
 // Arithmetic in double without contraction, in the order written.
 // ---------------------------------------------------------------------------
 
 constexpr int COST_TAB_MAX = 32;
 constexpr int COST_WG = 1024;
 constexpr int COST_B_MAX = 4096;
+constexpr int COST_RANK_MAX = 256;   // up to this many requests, ranks by counting
+constexpr int COST_PAIRS = 4096;     // up to this many (request, depth) pairs, values in parallel
 
 struct CostTable {
     double t[COST_TAB_MAX];   // depths, strictly increasing
@@ -2345,129 +2351,208 @@ struct CostTable {
     int n;
 };
 
-__device__ double table_cost(const CostTable &T, double d)
+// cost(d) from the table held in LDS (depths td, costs tc, n points).
+__device__ double table_cost(const double *td, const double *tc, int n, double d)
 {
 #pragma clang fp contract(off)
     int above = 0;   // table points at or below d
-    while (above < T.n && T.t[above] <= d) ++above;
-    if (above == 0) return T.c[0];
-    if (above == T.n) return T.c[T.n - 1];
-    const double w = (d - T.t[above - 1]) / (T.t[above] - T.t[above - 1]);
-    return T.c[above - 1] + w * (T.c[above] - T.c[above - 1]);
+    while (above < n && td[above] <= d) ++above;
+    if (above == 0) return tc[0];
+    if (above == n) return tc[n - 1];
+    const double w = (d - td[above - 1]) / (td[above] - td[above - 1]);
+    return tc[above - 1] + w * (tc[above] - tc[above - 1]);
 }
 
 // Sort key of a bid: the value's bits (values are >= 0, so their bits order
-// like them); 0 for a request without a bid.
+// like them) plus 1; 0 for a request without a bid.
 __device__ __forceinline__ uint64_t bid_key(double v) { return (uint64_t)__double_as_longlong(v) + 1ull; }
 
+// Confidences up to this many are staged through LDS with one coalesced load
+// per element; larger inputs are read in place.
+constexpr int COST_STAGE = 8192;
+
+// Does (a, wa) come before (c, wc): key descending, request ascending?
+__device__ __forceinline__ bool bid_first(uint64_t a, int wa, uint64_t c, int wc)
+{
+    return a > c || (a == c && wa < wc);
+}
+
+__device__ __forceinline__ double wave_max_d(double v)
+{
+    v = fmax(v, xchg_d<0>(v));
+    v = fmax(v, xchg_d<1>(v));
+    v = fmax(v, xchg_d<2>(v));
+    v = fmax(v, xchg_d<3>(v));
+    v = fmax(v, xchg_d<4>(v));
+    return fmax(v, xchg_d<5>(v));
+}
+
+// The window of request b (K_b, or -1 when it is outside [0, K]).
+__device__ __forceinline__ int cost_window(const int32_t *max_depth, int b, int K)
+{
+    const int Kb = max_depth ? max_depth[b] : K;
+    return (Kb >= 0 && Kb <= K) ? Kb : -1;
+}
+
+// flags: bit 0 the confidences are staged in LDS, bit 1 the bids use the
+// pair-parallel values (needs bit 0)
 __global__ __launch_bounds__(COST_WG) void dcut_cost_kernel(const float *conf, const int32_t *max_depth, int B,
-                                                            int K, CostTable T, double max_verify,
+                                                            int K, CostTable T, double max_verify, int flags,
                                                             int32_t *depth_out)
 {
 #pragma clang fp contract(off)
     extern __shared__ double cost_smem[];
+    const bool staged = flags & 1, paired = flags & 2;
     int N = 1;
     while (N < B) N <<= 1;
     double *costd = cost_smem;                          // [K + 1]
-    uint64_t *key = (uint64_t *)(costd + (K + 1));      // [N] sort keys
-    uint16_t *who = (uint16_t *)(key + N);              // [N] request of each key
+    uint64_t *key = (uint64_t *)(costd + (K + 1));      // [N] sort keys (by request, then by rank)
+    uint16_t *who = (uint16_t *)(key + N);              // [N] request of each sorted key
     uint16_t *bid = who + N;                            // [B] bid depth (0: none)
+    double *pv = cost_smem + (K + 1) + N + (N + B + 3) / 4;   // [B * K] products, then values (paired)
+    float *cst = (float *)(pv + (paired ? B * K : 0));        // [B * K] confidences (staged)
     __shared__ int8_t state[COST_B_MAX];                // -1 bad K_b, 0 no grant, 1 granted
+    __shared__ double tab_t[COST_TAB_MAX], tab_c[COST_TAB_MAX];
     __shared__ double sh_min;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
 
-    for (int d = tid; d <= K; d += COST_WG) costd[d] = d == 0 ? 0.0 : table_cost(T, (double)d);
+    if (tid < T.n) {
+        tab_t[tid] = T.t[tid];
+        tab_c[tid] = T.c[tid];
+    }
+    if (staged)
+        for (int i = tid; i < B * K; i += COST_WG) cst[i] = conf[i];
     __syncthreads();
-    if (tid < 64) {
+    for (int d = tid; d <= K; d += COST_WG) costd[d] = d == 0 ? 0.0 : table_cost(tab_t, tab_c, T.n, (double)d);
+    __syncthreads();
+    if (wv == 0) {
         // the cheapest depth's cost: once it cannot fit, nothing can
         double m = INFINITY;
-        for (int d = 1 + tid; d <= K; d += 64) m = fmin(m, costd[d]);
-        m = fmin(m, xchg_d<0>(m));
-        m = fmin(m, xchg_d<1>(m));
-        m = fmin(m, xchg_d<2>(m));
-        m = fmin(m, xchg_d<3>(m));
-        m = fmin(m, xchg_d<4>(m));
-        m = fmin(m, xchg_d<5>(m));
-        if (tid == 0) sh_min = m;
+        for (int d = 1 + lane; d <= K; d += 64) m = fmin(m, costd[d]);
+        m = -wave_max_d(-m);
+        if (lane == 0) sh_min = m;
     }
 
+    // 2. bids
+    if (paired) {
+        for (int b = tid; b < B; b += COST_WG) {
+            const int dn = max(cost_window(max_depth, b, K), 0);
+            double P = 1.0;
+            for (int d = 1; d <= dn; ++d) {
+                P = P * (double)sanitize_conf(cst[b * K + d - 1]);
+                pv[b * K + d - 1] = P;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < B * K; i += COST_WG) {
+            const int d = i % K + 1;   // entries past a request's window are never read
+            pv[i] = (pv[i] * (double)d) / costd[d];
+        }
+        __syncthreads();
+    }
     for (int b = tid; b < N; b += COST_WG) {
         uint64_t kb = 0;
         if (b < B) {
-            const int Kb = max_depth ? max_depth[b] : K;
-            const bool ok = Kb >= 0 && Kb <= K;
-            state[b] = ok ? 0 : -1;
-            double P = 1.0, best = 0.0;
+            const int Kb = cost_window(max_depth, b, K);
+            const int dn = max(Kb, 0);
+            double best = 0.0;
             int dbest = 0;
-            const float *cb = conf + (int64_t)b * K;
-            const int dn = ok ? Kb : 0;
-            for (int d0 = 0; d0 < dn; d0 += 8) {
-                float c8[8];
+            if (paired) {
+                for (int d = 1; d <= dn; ++d) {
+                    const double v = pv[b * K + d - 1];
+                    if (d == 1 || v > best) { best = v; dbest = d; }
+                }
+            } else {
+                double P = 1.0;
+                const float *cb = conf + (int64_t)b * K;
+                for (int d0 = 0; d0 < dn; d0 += 16) {
+                    float c16[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) c8[i] = cb[min(d0 + i, dn - 1)];   // all eight in flight
+                    for (int i = 0; i < 16; ++i) {
+                        const int dd = min(d0 + i, dn - 1);
+                        c16[i] = staged ? cst[(int64_t)b * K + dd] : cb[dd];   // all sixteen in flight
+                    }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int d = d0 + i + 1;
-                    if (d <= dn) {
-                        P = P * (double)sanitize_conf(c8[i]);
-                        const double v = (P * (double)d) / costd[d];
-                        if (d == 1 || v > best) { best = v; dbest = d; }
+                    for (int i = 0; i < 16; ++i) {
+                        const int d = d0 + i + 1;
+                        if (d <= dn) {
+                            P = P * (double)sanitize_conf(c16[i]);
+                            const double v = (P * (double)d) / costd[d];
+                            if (d == 1 || v > best) { best = v; dbest = d; }
+                        }
                     }
                 }
             }
+            state[b] = Kb < 0 ? -1 : 0;
             bid[b] = (uint16_t)dbest;
             if (dbest > 0) kb = bid_key(best);
         }
         key[b] = kb;
-        who[b] = (uint16_t)min(b, B - 1);
     }
     __syncthreads();
 
-    // bitonic sort: descending by key, ascending by request on equal keys
-    for (int size = 2; size <= N; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < N / 2; t += COST_WG) {
-                const int lo = 2 * t - (t & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint64_t a = key[lo], c = key[hi];
-                const int wa = who[lo], wc = who[hi];
-                const bool lo_first = a > c || (a == c && wa < wc);
-                if (lo_first != desc) {
-                    key[lo] = c;
-                    key[hi] = a;
-                    who[lo] = (uint16_t)wc;
-                    who[hi] = (uint16_t)wa;
+    // 3. order of the bids
+    if (N <= COST_RANK_MAX) {
+        // rank of request t = the bids that come before it
+        uint64_t kt = 0;
+        int rank = 0;
+        if (tid < N) {
+            kt = key[tid];
+#pragma unroll 8
+            for (int o = 0; o < N; ++o) rank += bid_first(key[o], o, kt, tid) ? 1 : 0;
+        }
+        __syncthreads();
+        if (tid < N) {   // the ranks are a permutation of 0 .. N-1
+            key[rank] = kt;
+            who[rank] = (uint16_t)min(tid, B - 1);
+        }
+    } else {
+        for (int t = tid; t < N; t += COST_WG) who[t] = (uint16_t)min(t, B - 1);
+        __syncthreads();
+        for (int size = 2; size <= N; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int t = tid; t < N / 2; t += COST_WG) {
+                    const int lo = 2 * t - (t & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool desc = (lo & size) == 0;
+                    const uint64_t a = key[lo], c = key[hi];
+                    const int wa = who[lo], wc = who[hi];
+                    if (bid_first(a, wa, c, wc) != desc) {
+                        key[lo] = c;
+                        key[hi] = a;
+                        who[lo] = (uint16_t)wc;
+                        who[hi] = (uint16_t)wa;
+                    }
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
+    __syncthreads();
 
-    if (tid < 64) {
-        const int lane = tid;
+    // 4. the budget, in bid order
+    if (wv == 0) {
         const double minc = sh_min;
         double spent = 0.0;
-        bool open = true;
-        for (int h0 = 0; h0 < B && open; h0 += 64) {
+        for (int h0 = 0; h0 < B; h0 += 64) {
             const int r = h0 + lane;
             const bool has = r < B && key[r] != 0;
             const int req = has ? who[r] : 0;
-            const double c = has ? costd[bid[req]] : 0.0;
+            const double c = has ? costd[bid[req]] : INFINITY;   // no bid: never fits
             const uint64_t bids = __ballot(has);   // a prefix of the lanes: bids sort first
+            // the chunk's 64 offers, unrolled: the running total is the only
+            // dependence from one offer to the next; a lane without a bid
+            // costs +inf and never fits
             uint64_t granted = 0;
+#pragma unroll
             for (int i = 0; i < 64; ++i) {
-                if (!((bids >> i) & 1ull) || !(spent + minc <= max_verify)) {
-                    open = false;
-                    break;
-                }
-                const double ci = readlane_d(c, i);
-                if (spent + ci <= max_verify) {
-                    spent = spent + ci;
-                    granted |= 1ull << i;
-                }
+                const double s2 = spent + readlane_d(c, i);
+                const bool fit = s2 <= max_verify;
+                spent = fit ? s2 : spent;
+                granted |= (__ballot(fit) != 0 ? 1ull : 0ull) << i;
             }
             if ((granted >> lane) & 1ull) state[req] = 1;
+            if (bids != ~0ull || !(spent + minc <= max_verify)) break;   // no bid left, or none can fit
         }
     }
     __syncthreads();
@@ -2494,7 +2579,8 @@ __global__ __launch_bounds__(STATS_WG) void accept_stats_kernel(const int32_t *n
     for (int i = tid; i < 2 * K + 1; i += STATS_WG) hist[i] = 0u;
     if (tid < 4) tot[tid] = 0ull;
     __syncthreads();
-    unsigned long long req = 0, bad = 0, sn = 0;
+    unsigned long long sn = 0;
+    int req = 0, bad = 0;
     for (int b = tid; b < B; b += STATS_WG) {
         const int n = num_accepted[b];
         if (n < 0) { ++bad; continue; }
@@ -2506,16 +2592,31 @@ __global__ __launch_bounds__(STATS_WG) void accept_stats_kernel(const int32_t *n
         atomicAdd(&hn[nw], 1u);
         if (nw < d) atomicAdd(&hr[nw], 1u);
     }
-    atomicAdd(&tot[0], req);
-    atomicAdd(&tot[1], bad);
-    atomicAdd(&tot[2], sn);
+    // one LDS add per wave for the request totals (sum n < 2^31: B <= 4096, n < 2^30)
+    req = wave_sum_i(req);
+    bad = wave_sum_i(bad);
+    const int snw = wave_sum_i((int)sn);
+    if (lane_id() == 0) {
+        atomicAdd(&tot[0], (unsigned long long)req);
+        atomicAdd(&tot[1], (unsigned long long)bad);
+        atomicAdd(&tot[2], (unsigned long long)snw);
+    }
     __syncthreads();
-    // suffix sums over n (K + 1 bins; K is at most 1024, one pass of the workgroup per 256)
-    if (tid == 0) {
-        unsigned long long above = 0;   // #{n > k}
-        for (int k = K - 1; k >= 0; --k) {
-            above += hn[k + 1];
-            hn[k + 1] = (unsigned int)above;   // now accepted[k], stored one bin up
+    // suffix sums over n: accepted[k] = #{n > k} = sum of bins k+1 .. K, stored
+    // one bin up.  Wave 0: lane l sums a block of bins, a scan over the lanes
+    // gives each block the count above it, then each lane walks its block
+    // from the top.
+    if (tid < 64) {
+        const int per = (K + 63) / 64;
+        const int lo = 1 + tid * per, hi = min(K, lo + per - 1);   // bins lo .. hi
+        unsigned int blk = 0;
+        for (int j = lo; j <= hi; ++j) blk += hn[j];
+        const int incl = wave_incl_scan_i((int)blk);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        unsigned int above = (unsigned int)(total - incl);   // bins past this block
+        for (int j = hi; j >= lo; --j) {
+            above += hn[j];
+            hn[j] = above;
         }
     }
     __syncthreads();
@@ -2619,14 +2720,31 @@ __global__ __launch_bounds__(DCUT_WG) void dcut_kernel(const float *conf, const 
                 if (key != 0 && (key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 255u], 1);
             }
             __syncthreads();
-            if (tid == 0) {
-                int acc = 0, digit = 0;
-                for (int bin = 255; bin >= 0; --bin) {
-                    if (acc + hist[bin] >= kr) { digit = bin; break; }
-                    acc += hist[bin];
+            if (tid < 64) {
+                // the digit: the highest bin whose count, with every bin above
+                // it, reaches kr.  Lane l holds bins 255 - 4l down to 252 - 4l;
+                // a scan over the lanes gives the counts above each lane.
+                int h[4], sum = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    h[j] = hist[255 - 4 * tid - j];
+                    sum += h[j];
                 }
-                sh_kr = kr - acc;
-                sh_prefix = prefix | ((uint32_t)digit << shift);
+                const int incl = wave_incl_scan_i(sum);
+                const uint64_t hit = __ballot(incl >= kr);   // nonempty: kr <= the keys left
+                if (tid == __builtin_ctzll(hit)) {
+                    int acc = incl - sum, digit = 255 - 4 * tid - 3;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (acc + h[j] >= kr) {
+                            digit = 255 - 4 * tid - j;
+                            break;
+                        }
+                        acc += h[j];
+                    }
+                    sh_kr = kr - acc;
+                    sh_prefix = prefix | ((uint32_t)digit << shift);
+                }
             }
             __syncthreads();
             prefix = sh_prefix;
@@ -3321,12 +3439,25 @@ sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth, int32_
     }
     int64_t N = 1;
     while (N < B) N <<= 1;
-    const size_t lds = sizeof(double) * (size_t)(K + 1) + (sizeof(uint64_t) + sizeof(uint16_t)) * (size_t)N +
-                       sizeof(uint16_t) * (size_t)B;
-    if (lds > 58 * 1024) return SV_ERR_UNSUPPORTED;
+    // costs per depth, sort keys and requests, bids (rounded up to whole
+    // doubles), then the staged confidences of small inputs
+    constexpr size_t LDS_DYN_MAX = 60 * 1024;   // with the kernel's 4.6 KiB of static LDS, within 64 KiB
+    size_t lds = sizeof(double) * (size_t)((K + 1) + N + (N + B + 3) / 4);
+    if (lds > LDS_DYN_MAX) return SV_ERR_UNSUPPORTED;
+    // small inputs: confidences staged (4 B per pair), and with room for
+    // them the pair-parallel values (8 B per pair)
+    const size_t pairs = (size_t)B * (size_t)K;
+    int flags = 0;
+    if ((int64_t)pairs <= COST_PAIRS && lds + 12 * pairs <= LDS_DYN_MAX) {
+        flags = 3;
+        lds += 12 * pairs;
+    } else if ((int64_t)pairs <= COST_STAGE && lds + 4 * pairs <= LDS_DYN_MAX) {
+        flags = 1;
+        lds += 4 * pairs;
+    }
     (void)hipGetLastError();
     hipLaunchKernelGGL(dcut_cost_kernel, dim3(1), dim3(COST_WG), lds, stream, conf, max_depth, B, K, T, max_verify,
-                       depth_out);
+                       flags, depth_out);
     return hip_status("dcut_cost_kernel launch");
 }
 

@@ -356,7 +356,7 @@ sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_
  *                strictly increasing, costs finite and > 0 (copied into the
  *                launch; the call keeps no reference)
  *   max_verify   finite, >= 0
- *   B <= 4096 and 8 (K + 1) + 10 P + 2 B <= 58 KiB of LDS, P the power of two
+ *   B <= 4096 and 8 (K + 1) + 10 P + 2 B <= 60 KiB of LDS, P the power of two
  *   at or above B (SV_ERR_UNSUPPORTED). */
 sv_status dcut_allocate_cost(const float *conf, const int32_t *max_depth,
                              int32_t B, int32_t K,
