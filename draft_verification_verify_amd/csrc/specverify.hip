@@ -1485,33 +1485,74 @@ __device__ __forceinline__ Stat merge2(Stat a, Stat b, bool lse, double cs, cons
         a = b;
         b = t;
     }
+    // The rescale factor 2^((b.m - a.m) * cs) <= 1 in fp32 (hardware exp2,
+    // within 2 ulp; an argument below the fp32 range gives 0): it moves S by
+    // at most 2.4e-7 relative, as the row pass's own lane rescales do.
     if (b.m == -INFINITY) a.s += (b.s != b.s) ? b.s : 0.0;   // empty (or NaN-poisoned) partial
-    else a.s += b.s * exp2_tab(((double)b.m - (double)a.m) * cs, tab);
+    else a.s += b.s * (double)__builtin_amdgcn_exp2f((float)(((double)b.m - (double)a.m) * cs));
     return a;
 }
 
 constexpr int MERGE_LOADS = 4;   // row-pass partials loaded at once per merging thread
 
+// Threads per row of the merge: the largest power of two up to 64 (and up
+// to the workspace's column count) with a group of rows_max rows fitting
+// half the workgroup, for a request of at most rows_max rows.  It depends on
+// launch constants only, so the merge's first loads wait on no device value.
+__device__ __forceinline__ int merge_tpr(int rows_max, int cpr_max)
+{
+    int tpr = 1;
+    while (tpr < 64 && tpr < cpr_max && 2 * tpr * rows_max <= WG) tpr <<= 1;
+    return tpr;
+}
+
+// The first MERGE_LOADS partials of every thread of the merge's first row
+// group (row tid / tpr, columns tid % tpr + i * tpr), loaded at kernel start
+// before the chunk count and the request's row count are known: every slot
+// read lies in request b's own slot range (rows_max rows of cpr_max
+// columns); those past the request's rows or the chunk count are read and
+// not folded.
+struct MergePre {
+    Stat v[MERGE_LOADS];
+};
+
+__device__ __forceinline__ MergePre merge_prefetch(const Params &P, int pre, int rows_max, int tpr)
+{
+    MergePre m;
+    const int r = min((int)threadIdx.x / tpr, rows_max - 1), l = threadIdx.x & (tpr - 1);
+    const Stat *pp = P.ws.part + (int64_t)(pre + r) * P.cpr_max;
+#pragma unroll
+    for (int i = 0; i < MERGE_LOADS; ++i) m.v[i] = pp[min(l + i * tpr, P.cpr_max - 1)];
+    return m;
+}
+
 // Merges the row-pass partials of request b's rows into rows_s (all threads;
-// tpr threads per row, each folding every tpr-th partial, then a butterfly
-// over the tpr lanes).  Every workgroup of a request performs the same
-// operations in the same order, so all of them hold identical statistics.
-__device__ void merge_rows(const Params &P, int pre, int rows, int cpr, bool lse, double cs, const double *tab,
-                           Stat *rows_s)
+// tpr threads per row, each folding every tpr-th partial in chunk order, then
+// a butterfly over the tpr lanes; rows in groups of WG / tpr).  The first
+// MERGE_LOADS partials of each thread of the first group come from
+// merge_prefetch.  Every workgroup of a request performs the same operations
+// in the same order, so all of them hold identical statistics.
+__device__ void merge_rows(const Params &P, int pre, int rows, int tpr, int cpr, bool lse, double cs,
+                           const double *tab, const MergePre &first, Stat *rows_s)
 {
     const int tid = threadIdx.x;
-    int tpr = 1;
-    while (tpr < 64 && tpr < cpr && 2 * tpr * rows <= WG) tpr <<= 1;
     const int G = WG / tpr;
     const Stat ident = {-INFINITY, 0x7fffffff, 0.0};
     for (int g0 = 0; g0 < rows; g0 += G) {
         const int r = g0 + tid / tpr, l = tid & (tpr - 1);
         Stat acc = ident;
         if (r < rows) {
+            int j0 = l;
+            if (g0 == 0) {
+#pragma unroll
+                for (int i = 0; i < MERGE_LOADS; ++i)
+                    if (l + i * tpr < cpr) acc = merge2(acc, first.v[i], lse, cs, tab);
+                j0 += MERGE_LOADS * tpr;
+            }
             // MERGE_LOADS partials in flight per thread (clamped index, no
-            // branch), then folded in chunk order j = l, l + tpr, ...
+            // branch), folded in chunk order
             const Stat *pp = P.ws.part + (int64_t)(pre + r) * P.cpr_max;
-            for (int j0 = l; j0 < cpr; j0 += MERGE_LOADS * tpr) {
+            for (; j0 < cpr; j0 += MERGE_LOADS * tpr) {
                 Stat v[MERGE_LOADS];
 #pragma unroll
                 for (int i = 0; i < MERGE_LOADS; ++i) v[i] = pp[min(j0 + i * tpr, cpr - 1)];
@@ -1666,37 +1707,65 @@ __device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int b, cons
     return r;
 }
 
-// Residual sums over a wave's run (loads already issued into rz / ry).
-template <bool BF16, bool ALIGNED, bool EXACT, int NSTEP, int NV>
+// Residual sums over a wave's run of VT vectors per lane (vector i of the
+// run is vu + 64 i + lane), loads one vector ahead of the arithmetic: the
+// unit passes of a whole batch start at once, and if every wave issued its
+// whole run up front, every wave would wait for the whole burst (a row pair
+// per request, tens of MB) before its first term; one vector ahead, the
+// first terms start after a fraction of it and the rest streams under the
+// fp64 work.
+template <bool BF16, bool ALIGNED, bool EXACT, int VT>
 __device__ __forceinline__ void resid_terms(const DrawRows<BF16> &dr, double rho_hat, int vu, const double *tab,
-                                            const uint4 (&rz)[NSTEP][NV], const uint4 (&ry)[NSTEP][NV], int &flag,
-                                            double &dsum, double &bq, double &sz, double &sy)
+                                            int &flag, double &dsum, double &bq, double &sz, double &sy)
 {
     constexpr int EPV = RowView<BF16>::EPV;
     const int lane = lane_id();
+    uint4 zc, yc = make_uint4(0, 0, 0, 0);
+    {
+        uint4 t1[1], t2[1];
+        issue_vecs<BF16, 1>(dr.rz, vu + lane, 64, t1);
+        zc = t1[0];
+        if (ALIGNED) {
+            issue_vecs<BF16, 1>(dr.dc.ry, vu + lane, 64, t2);
+            yc = t2[0];
+        }
+    }
 #pragma unroll
-    for (int u = 0; u < NSTEP; ++u) {
-        const int v0 = vu + u * NV * 64 + lane;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int vi = v0 + j * 64;
-            float f[EPV], g[EPV];
-            // one vector at a time: unbounded interleaving of the fp64
-            // exponentials would cost occupancy
-            __builtin_amdgcn_sched_barrier(0);
-            chunk_vec<BF16, ALIGNED>(dr.rz, vi, rz[u][j], f, flag);
-            draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, ry[u][j], g);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const double p = exp2_512(draw_exp_arg<EXACT>(f[e], dr.mz, dr.mzc5, dr.cd5), tab);
-                const double q = exp2_512(draw_exp_arg<EXACT>(g[e], dr.my, dr.myc5, dr.cd5), tab);
-                sz += p;
-                sy += q;
-                const double t = fma(-rho_hat, q, p);
-                dsum += __builtin_fmax(t, 0.0);
-                bq += (t > 0.0) ? q : 0.0;
+    for (int i = 0; i < VT; ++i) {
+        uint4 zn = zc, yn = yc;
+        if (i + 1 < VT) {
+            uint4 t1[1], t2[1];
+            issue_vecs<BF16, 1>(dr.rz, vu + (i + 1) * 64 + lane, 64, t1);
+            zn = t1[0];
+            if (ALIGNED) {
+                issue_vecs<BF16, 1>(dr.dc.ry, vu + (i + 1) * 64 + lane, 64, t2);
+                yn = t2[0];
             }
         }
+        const int vi = vu + i * 64 + lane;
+        float f[EPV], g[EPV];
+        // one vector at a time: unbounded interleaving of the fp64
+        // exponentials would cost occupancy
+        __builtin_amdgcn_sched_barrier(0);
+        chunk_vec<BF16, ALIGNED>(dr.rz, vi, zc, f, flag);
+        draft_vec<BF16, ALIGNED>(dr.dc, dr.rz, vi, yc, g);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const double p = exp2_512(draw_exp_arg<EXACT>(f[e], dr.mz, dr.mzc5, dr.cd5), tab);
+            const double q = exp2_512(draw_exp_arg<EXACT>(g[e], dr.my, dr.myc5, dr.cd5), tab);
+            sz += p;
+            sy += q;
+            // t > 0: add t to d and q to bq; else add zeros.  One select
+            // builds the 0/1 multiplier (its low word is 0 either way), and
+            // t * 1 = t, t * 0 = +-0 keep the sums bit for bit those of
+            // adding max(t, 0) and (t > 0 ? q : 0).
+            const double t = fma(-rho_hat, q, p);
+            const double one = __longlong_as_double(t > 0.0 ? 0x3ff0000000000000ll : 0ll);
+            dsum = fma(t, one, dsum);
+            bq = fma(q, one, bq);
+        }
+        zc = zn;
+        yc = yn;
     }
 }
 
@@ -1715,16 +1784,8 @@ __device__ ChunkPart unit_sums(const DrawRows<BF16> &dr, bool resid, double rho_
     int flag = 0;
     if (resid) {
         double dsum = 0.0, bq = 0.0, sz = 0.0, sy = 0.0;
-        // every step's loads are issued before the first step's arithmetic, so
-        // the second step's memory latency hides under the first's fp64 work
-        uint4 rz[NSTEP][NV], ry[NSTEP][NV];
-#pragma unroll
-        for (int u = 0; u < NSTEP; ++u) {
-            issue_vecs<BF16, NV>(dr.rz, vu + u * NV * 64 + lane, 64, rz[u]);
-            if (ALIGNED) issue_vecs<BF16, NV>(dr.dc.ry, vu + u * NV * 64 + lane, 64, ry[u]);
-        }
-        if (dr.exact) resid_terms<BF16, ALIGNED, true, NSTEP, NV>(dr, rho_hat, vu, tab, rz, ry, flag, dsum, bq, sz, sy);
-        else resid_terms<BF16, ALIGNED, false, NSTEP, NV>(dr, rho_hat, vu, tab, rz, ry, flag, dsum, bq, sz, sy);
+        if (dr.exact) resid_terms<BF16, ALIGNED, true, NSTEP * NV>(dr, rho_hat, vu, tab, flag, dsum, bq, sz, sy);
+        else resid_terms<BF16, ALIGNED, false, NSTEP * NV>(dr, rho_hat, vu, tab, flag, dsum, bq, sz, sy);
         part.d = wave_sum(dsum);
         part.bq = wave_sum(bq);
         part.sz = wave_sum(sz);
@@ -1873,6 +1934,10 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // the request's plan and the row pass's chunking are read before the
     // table is built, so their loads overlap its arithmetic
     const int cpr = P.ws.meta[0];
+    // request b's partials start at slot row b * (2K + 1)
+    const int pre = b * (2 * P.K + 1);
+    const int tpr = merge_tpr(2 * P.K + 1, P.cpr_max);
+    const MergePre first = merge_prefetch(P, pre, 2 * P.K + 1, tpr);
     // the scan's inputs for positions lo..lo+63, issued with the plan's loads
     // so their latencies overlap each other, the table and the merge; every
     // wave loads them (no branch), from a stand-in where an argument is
@@ -1894,8 +1959,6 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     }
     init_exp2_table(tab);
 
-    // request b's partials start at slot row b * (2K + 1)
-    const int pre = b * (2 * P.K + 1);
     const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF || q.kind == KIND_SAMPLED_R;
     if (q.kind == KIND_SAMPLED_R) {
         // draft rows 0..d-1: the given statistics, with the draft logit at the
@@ -1911,7 +1974,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
             rows_s[q.d + k] = st;
         }
     }
-    merge_rows(P, pre, q.rows, cpr, lse, lse ? scale_d(scale_of(q.kind, q.T)) : 0.0, tab, rows_s);
+    merge_rows(P, pre, q.rows, tpr, cpr, lse, lse ? scale_d(scale_of(q.kind, q.T)) : 0.0, tab, first, rows_s);
 
     if (P.mode == MODE_CONF) {
         for (int k = tid; k < P.K; k += WG) {
