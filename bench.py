@@ -468,6 +468,41 @@ def main():
             "row_pass_GB_s": vrp_bytes / (float(vstage[0]) * 1e-3) / 1e9,
             "note": "spec_verify_sample alone at the D-cut depths (budget 384): sum(d_b + 1) target and "
                     "sum(d_b) draft rows; padded [B,K+1,V] buffers, rotated"}
+        # the same verify on the packed (CSR) layout: the buffers hold only
+        # the sum(d_b + 1) target and sum(d_b) draft rows (gathered here,
+        # outside the timed region; three copies rotated, 640 MB)
+        tgt_idx = torch.tensor([b * (K + 1) + k for b in range(B) for k in range(int(dep[b]) + 1)],
+                               dtype=torch.int64, device="cuda")
+        drf_idx = torch.tensor([b * K + k for b in range(B) for k in range(int(dep[b]))],
+                               dtype=torch.int64, device="cuda")
+        offs = torch.tensor(np.concatenate([[0], np.cumsum(dep)]).astype(np.int32), device="cuda")
+        pcopies = [(copies[i % ncopy][0].view(B * (K + 1), V)[tgt_idx].contiguous(),
+                    copies[i % ncopy][1].view(B * K, V)[drf_idx].contiguous()) for i in range(3)]
+        ptok = tok.view(-1)[drf_idx].contiguous()
+        pua = ua.view(-1)[drf_idx].contiguous()
+        pout = torch.empty(rsum + B, dtype=torch.int32, device="cuda")
+        ppd = torch.empty(rsum, dtype=torch.float32, device="cuda")
+        pqd = torch.empty(rsum, dtype=torch.float32, device="cuda")
+
+        def kstep(i):
+            pt, pdr = pcopies[i % 3]
+            sv.verify_sample_packed(pt, pdr, ptok, offs, T, pua, us, K, out_tokens=pout, num_accepted=nacc,
+                                    p_draft=ppd, q_draft=pqd, workspace=ws, stream=stream)
+        _, kper, _ = timed(kstep, steps2, warm2)
+        _, _, kst = timed(kstep, steps2, 2, stages=True)
+        kms = float(np.mean(kper))
+        kstage = np.asarray(kst, dtype=np.float64).mean(axis=0)
+        sec["dcut_packed_verify_B64_K16_budget384"] = {
+            "verified_rows_per_s": prow / (kms * 1e-3), "ms": kms, "rows_per_step": prow,
+            "algorithmic_bytes_per_step": ralgo, "GB_s": ralgo / (kms * 1e-3) / 1e9,
+            "pct_hbm_peak": 100 * ralgo / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "buffer_bytes": int(pcopies[0][0].nbytes + pcopies[0][1].nbytes),
+            "stage_ms_with_events": {"row_pass": float(kstage[0]), "finish": float(kstage[1]),
+                                     "draw": float(kstage[2])},
+            "row_pass_GB_s": vrp_bytes / (float(kstage[0]) * 1e-3) / 1e9,
+            "note": "spec_verify_sample_packed at the D-cut depths (budget 384): CSR offsets, buffers of "
+                    "sum(d_b + 1) target and sum(d_b) draft rows only; three copies rotated"}
+        del pcopies
         # the same pipeline with the confidence pass's row statistics reused:
         # the verify streams target rows only (plus the drawn draft row)
         dstats = torch.empty((B, K, 2), dtype=torch.float64, device="cuda")

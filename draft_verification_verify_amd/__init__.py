@@ -11,6 +11,9 @@ Calls mirror the C ABI in ``include/specverify.h``:
     verify_greedy(target, tokens, depth=None)            -> (out_tokens, num_accepted)
     verify_sample(target, draft, tokens, temperature,
                   u_accept, u_sample, depth=None)        -> (out_tokens, num_accepted, p_draft, q_draft)
+    verify_greedy_packed(target, tokens, offsets, K_max) -> (out_tokens, num_accepted)
+    verify_sample_packed(target, draft, tokens, offsets, temperature,
+                         u_accept, u_sample, K_max)      -> (out_tokens, num_accepted, p_draft, q_draft)
     draft_confidence(draft, max_depth=None)              -> conf
     dcut_allocate(conf, budget, max_depth=None)          -> depth
 """
@@ -57,6 +60,11 @@ def _load() -> ctypes.CDLL:
     L.spec_verify_sample.restype = ctypes.c_int
     L.spec_verify_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32,
                                      vp, vp, vp, vp, vp, sz, vp]
+    L.spec_verify_greedy_packed.restype = ctypes.c_int
+    L.spec_verify_greedy_packed.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.spec_verify_sample_packed.restype = ctypes.c_int
+    L.spec_verify_sample_packed.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                            vp, vp, vp, vp, vp, sz, vp]
     L.spec_verify_sample_noalloc.restype = ctypes.c_int
     L.spec_verify_sample_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32,
                                              vp, vp, vp, vp, vp]
@@ -103,7 +111,7 @@ EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify
             "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
             "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit",
             "spec_verify_read_ceiling", "spec_early_exit_plan", "spec_verify_sample_noalloc",
-            "spec_accept_stats_summary")
+            "spec_accept_stats_summary", "spec_verify_greedy_packed", "spec_verify_sample_packed")
 
 # Bytes of the static scratch array behind spec_verify_sample_noalloc.
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -314,6 +322,84 @@ def verify_sample(target, draft, tokens, temperature, u_accept, u_sample, depth=
                                 _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft),
                                 _ptr(ws), nbytes, _stream(stream))
     _raise("spec_verify_sample", st)
+    return out_tokens, num_accepted, p_draft, q_draft
+
+
+def _packed_shape(target, tokens, offsets):
+    """(B, N, V) of a packed call: offsets [B + 1], tokens [N], target [N + B, V]."""
+    torch = _torch()
+    for t, name in ((target, "target"), (tokens, "tokens"), (offsets, "offsets")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if offsets.dim() != 1 or offsets.numel() < 2:
+        raise ValueError(f"offsets must be 1-D [B + 1] with B >= 1, got shape {tuple(offsets.shape)}")
+    if tokens.dim() != 1:
+        raise ValueError(f"tokens must be 1-D [N], got shape {tuple(tokens.shape)}")
+    B, N = offsets.numel() - 1, tokens.numel()
+    if target.dim() != 2 or target.shape[0] != N + B:
+        raise ValueError(f"target must be 2-D [N + B, V] = [{N + B}, V], got shape {tuple(target.shape)}")
+    return B, N, int(target.shape[1])
+
+
+def _packed_outputs(dev, B, N, out_tokens, num_accepted, p_draft=None, q_draft=None, want_probs=False):
+    torch = _torch()
+    if out_tokens is None:
+        out_tokens = torch.empty((N + B,), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if want_probs and p_draft is None:
+        p_draft = torch.empty((N,), dtype=torch.float32, device=dev)
+    if want_probs and q_draft is None:
+        q_draft = torch.empty((N,), dtype=torch.float32, device=dev)
+    return out_tokens, num_accepted, p_draft, q_draft
+
+
+def verify_greedy_packed(target, tokens, offsets, K_max: int, *, out_tokens=None, num_accepted=None,
+                         workspace=None, stream=None):
+    """Greedy verification, packed layout: request b's drafted positions are
+    offsets[b] .. offsets[b+1]-1 of tokens [N]; its target rows start at row
+    offsets[b] + b of target [N + B, V].  Returns (out_tokens [N + B],
+    num_accepted [B])."""
+    torch = _torch()
+    B, N, V = _packed_shape(target, tokens, offsets)
+    dt = _dtype_code(target)
+    _validate((target, "target", None, None), (tokens, "tokens", torch.int32, (N,)),
+              (offsets, "offsets", torch.int32, (B + 1,)),
+              (out_tokens, "out_tokens", torch.int32, (N + B,)), (num_accepted, "num_accepted", torch.int32, (B,)))
+    out_tokens, num_accepted, _, _ = _packed_outputs(target.device, B, N, out_tokens, num_accepted)
+    ws, nbytes = _ws(target.device, B, int(K_max), V, workspace)
+    st = lib.spec_verify_greedy_packed(_ptr(target), dt, _ptr(tokens) if N else None, _ptr(offsets), B,
+                                       int(K_max), N, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(ws),
+                                       nbytes, _stream(stream))
+    _raise("spec_verify_greedy_packed", st)
+    return out_tokens, num_accepted
+
+
+def verify_sample_packed(target, draft, tokens, offsets, temperature, u_accept, u_sample, K_max: int, *,
+                         out_tokens=None, num_accepted=None, p_draft=None, q_draft=None,
+                         want_probs: bool = True, workspace=None, stream=None):
+    """Rejection-sampling verification, packed layout: draft [N, V],
+    tokens / u_accept [N], target [N + B, V], offsets [B + 1] (see
+    verify_greedy_packed); temperature and u_sample [B].  Returns
+    (out_tokens [N + B], num_accepted [B], p_draft [N], q_draft [N])."""
+    torch = _torch()
+    B, N, V = _packed_shape(target, tokens, offsets)
+    dt = _dtype_code(target)
+    _validate((target, "target", None, None), (draft, "draft", target.dtype, (N, V)),
+              (tokens, "tokens", torch.int32, (N,)), (offsets, "offsets", torch.int32, (B + 1,)),
+              (temperature, "temperature", torch.float32, (B,)), (u_accept, "u_accept", torch.float32, (N,)),
+              (u_sample, "u_sample", torch.float32, (B,)),
+              (out_tokens, "out_tokens", torch.int32, (N + B,)), (num_accepted, "num_accepted", torch.int32, (B,)),
+              (p_draft, "p_draft", torch.float32, (N,)), (q_draft, "q_draft", torch.float32, (N,)))
+    out_tokens, num_accepted, p_draft, q_draft = _packed_outputs(target.device, B, N, out_tokens, num_accepted,
+                                                                 p_draft, q_draft, want_probs)
+    ws, nbytes = _ws(target.device, B, int(K_max), V, workspace)
+    nz = (lambda t: _ptr(t) if N else None)
+    st = lib.spec_verify_sample_packed(_ptr(target), nz(draft), dt, nz(tokens), _ptr(offsets),
+                                       _ptr(temperature), nz(u_accept), _ptr(u_sample), B, int(K_max), N, V,
+                                       _ptr(out_tokens), _ptr(num_accepted), nz(p_draft), nz(q_draft),
+                                       _ptr(ws), nbytes, _stream(stream))
+    _raise("spec_verify_sample_packed", st)
     return out_tokens, num_accepted, p_draft, q_draft
 
 

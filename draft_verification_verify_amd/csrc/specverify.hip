@@ -134,8 +134,12 @@ struct alignas(16) ChunkPart {
 struct alignas(16) DrawRec {
     int32_t state, n;
     float T, mz;
-    float my, pad;
+    float my;
+    int32_t tb;       // first target row (and output slot) of the request
     double rho_hat;
+    int32_t db;       // first draft row (and drafted-token slot) of the request
+    int32_t nout;     // output slots of the request
+    int32_t pad[2];
 };
 
 struct Ws {
@@ -217,6 +221,11 @@ struct Params {
     float *conf;
     const Stat *dstats_in;   // sampled calls: draft-row statistics [B, K] from a confidence pass, or NULL
     Stat *dstats_out;        // confidence calls: draft-row statistics out [B, K], or NULL
+    // Packed (CSR) layout, or NULL for the padded one: request b's drafted
+    // positions are offs[b] .. offs[b + 1] - 1 of n_rows; K is then the
+    // largest depth the call accepts.
+    const int32_t *offs;
+    int32_t n_rows;
     int32_t B, K, V;
     int32_t bf16;      // logits dtype: 1 bf16, 0 fp32
     int32_t mode;
@@ -581,15 +590,30 @@ __device__ __forceinline__ bool temp_ok(float T)
 // argument's load goes to.
 __device__ int32_t k_stand_in = 0;
 
+// Where request b's rows and slots start.  Padded layout: target row k and
+// output slot k at b(K + 1) + k; draft row k, drafted token k, accept
+// uniform k and p/q slot k at bK + k; K + 1 output slots.  Packed layout
+// (positions o0 = offs[b] .. o1 - 1 = offs[b + 1] - 1): target row and output
+// slot k at o0 + b + k, the others at o0 + k; o1 - o0 + 1 output slots (none
+// when the offsets are unusable).
+struct ReqBase {
+    int64_t tb, db;
+    int nout;
+};
+
 struct ReqPlan {
     int d, kind, rows;
     float T;
     int lo;      // first position of the window (0 outside early-exit calls)
     bool fin;    // the window reaches the depth: the request ends in it
+    bool pair_ok;   // packed layout: 0 <= offs[b] <= offs[b + 1] <= n_rows
+    ReqBase rb;
 };
 
+// offs_bad: packed layout, the offsets are not a valid CSR array (some
+// request's pair is unusable), which makes every request bad.
 template <bool EE>
-__device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
+__device__ __forceinline__ ReqPlan plan_request(const Params &P, int b, bool offs_bad)
 {
     // Every load first and unconditionally: an argument the call does not
     // use is read from a valid stand-in address and its value discarded.
@@ -600,15 +624,30 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b)
                                             : (P.depth ? P.depth + b : stand_in);
     const float *tp = P.mode == MODE_SAMPLE ? P.temperature + b : (const float *)stand_in;
     const int32_t *ap = (EE && P.win_lo > 0) ? P.alive_in + b : stand_in;
-    const int dv = *dp;
+    const int32_t *o0p = P.offs ? P.offs + b : stand_in;
+    const int32_t *o1p = P.offs ? P.offs + b + 1 : stand_in;
+    int dv = *dp;
     const float tv = *tp;
     const int av = *ap;
-    const bool have_depth = P.mode == MODE_CONF ? P.max_depth != nullptr : P.depth != nullptr;
+    const int o0 = *o0p, o1 = *o1p;
+    const bool have_depth = P.offs || (P.mode == MODE_CONF ? P.max_depth != nullptr : P.depth != nullptr);
 
     ReqPlan q;
     q.T = 0.0f;
     q.lo = 0;
     q.fin = true;
+    q.pair_ok = true;
+    if (P.offs) {
+        q.pair_ok = 0 <= o0 && o0 <= o1 && o1 <= P.n_rows;
+        dv = (q.pair_ok && !offs_bad) ? o1 - o0 : -1;
+        q.rb.tb = (int64_t)o0 + b;
+        q.rb.db = o0;
+        q.rb.nout = (q.pair_ok && !offs_bad) ? o1 - o0 + 1 : 0;
+    } else {
+        q.rb.tb = (int64_t)b * (P.K + 1);
+        q.rb.db = (int64_t)b * P.K;
+        q.rb.nout = P.K + 1;
+    }
     if (P.mode == MODE_CONF) {
         q.d = have_depth ? dv : P.K;
         const bool ok = q.d >= 0 && q.d <= P.K;
@@ -647,21 +686,35 @@ struct Plan {
 };
 
 // Whole-workgroup plan: row_off = exclusive prefix of per-request rows.
+// Returns 1 when the packed layout's offsets are not a valid CSR array
+// (then every request is bad and reads no rows), else 0.
 template <bool EE>
-__device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
+__device__ int make_plan(const Params &P, Plan pl, int *scan_tmp)
 {
     const int B = P.B;
     const int per = (int)ceil_div(B, WG);
     const int b0 = threadIdx.x * per;
-    int local = 0;
+    int local = 0, bad_pair = 0;
     for (int j = 0; j < per; ++j) {
         const int b = b0 + j;
         if (b >= B) break;
-        const ReqPlan q = plan_request<EE>(P, b);
+        const ReqPlan q = plan_request<EE>(P, b, false);
         pl.info[b] = q.d | (q.kind << 16);
         pl.T[b] = q.T;
         pl.row_off[b] = q.rows;   // count for now
         local += q.rows;
+        bad_pair |= !q.pair_ok;
+    }
+    int offs_bad = 0;
+    if (P.offs && __syncthreads_or(bad_pair)) {
+        offs_bad = 1;
+        local = 0;
+        for (int j = 0; j < per; ++j) {
+            const int b = b0 + j;
+            if (b >= B) break;
+            pl.info[b] = KIND_BAD << 16;
+            pl.row_off[b] = 0;
+        }
     }
     const int v = wave_incl_scan_i(local);
     const int lane = lane_id();
@@ -679,6 +732,7 @@ __device__ void make_plan(const Params &P, Plan pl, int *scan_tmp)
     }
     if (threadIdx.x == WG - 1) pl.row_off[B] = run;
     __syncthreads();
+    return offs_bad;
 }
 
 // Request containing global active row r (row_off is non-decreasing).  r is
@@ -1037,7 +1091,10 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
         k.sc.c32 = 0.0f;
         k.sc.sh = 0;
     }
-    const int64_t row = is_draft ? ((int64_t)b * P.K + kk) : ((int64_t)b * (P.K + 1) + kk);
+    // the request's first draft row and first target row
+    const int64_t db = P.offs ? (int64_t)ld_scalar_i32(P.offs + b) : (int64_t)b * P.K;
+    const int64_t tb = P.offs ? db + b : (int64_t)b * (P.K + 1);
+    const int64_t row = is_draft ? db + kk : tb + kk;
     const char *row_start = (const char *)(is_draft ? P.draft : P.target) + row * (int64_t)P.V * (BF16 ? 2 : 4);
     const RowView<BF16> rv(row_start, P.V);
     k.vec = rv.vec;
@@ -1050,7 +1107,7 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     // rejected as bad data by the scan.
     k.zx = __int_as_float(0x7fffffff);
     if ((kind == KIND_SAMPLED || kind == KIND_SAMPLED_R) && c == 0) {
-        const int x = min(max(ld_scalar_i32(P.tokens + (int64_t)b * P.K + kk), 0), P.V - 1);
+        const int x = min(max(ld_scalar_i32(P.tokens + db + kk), 0), P.V - 1);
         k.zx = ld_scalar_logit<BF16>(row_start, x);
     }
     const int nbr = (int)ceil_div(k.nvec, WVEC);
@@ -1130,7 +1187,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     pl.row_off = plan_smem;
     pl.info = plan_smem + P.B + 1;
     pl.T = (float *)(plan_smem + 2 * P.B + 1);
-    make_plan<EE>(P, pl, scan_tmp);
+    const int offs_bad = make_plan<EE>(P, pl, scan_tmp);
 
     const int R = __builtin_amdgcn_readfirstlane(pl.row_off[P.B]);
     const uint32_t nwaves = gridDim.x * NWAVE;
@@ -1143,6 +1200,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         P.ws.meta[0] = cpr;
         P.ws.meta[1] = nb;
+        P.ws.meta[2] = offs_bad;
     }
 
     // Static assignment in rounds.  Task t is chunk t % cpr of row t / cpr.
@@ -1275,9 +1333,9 @@ __device__ __forceinline__ bool unif_ok(float u) { return u >= 0.0f && u < 1.0f;
 __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const Stat *rows, float2 *pq,
                                 const double *tab, int x0, float ua0, float us0)
 {
-    const int K = P.K, d = q.d;
+    const int d = q.d;
     const int lane = lane_id();
-    const int64_t tb = (int64_t)b * K;
+    const int64_t tb = q.rb.db;
     ReqDesc desc = {SREQ_BAD, 0, -1, q.T};
     if (q.kind == KIND_BAD) return desc;
 
@@ -1341,18 +1399,20 @@ __device__ ReqDesc scan_request(const Params &P, int b, const ReqPlan &q, const 
 
 // One wave writes request b's outputs: the accepted prefix, the emitted token
 // at position n, -1 after it, num_accepted, and (sampled calls) p/q at the
-// drafted tokens.  A bad request gets -1 everywhere and zero probabilities.
-__device__ void write_outputs(const Params &P, int b, int d, const ReqDesc &desc, const float2 *pq, int token)
+// drafted tokens.  A bad request gets -1 everywhere and zero probabilities
+// (in every slot it has: none when its packed offsets are unusable).
+__device__ void write_outputs(const Params &P, int b, int d, const ReqBase &rb, const ReqDesc &desc,
+                              const float2 *pq, int token)
 {
-    const int K = P.K, lane = lane_id();
-    const int64_t ob = (int64_t)b * (K + 1), tb = (int64_t)b * K;
+    const int lane = lane_id();
+    const int64_t ob = rb.tb, tb = rb.db;
     const bool bad = desc.state == SREQ_BAD;
     const int n = desc.n;
-    for (int k = lane; k <= K; k += 64)
+    for (int k = lane; k < rb.nout; k += 64)
         P.out_tokens[ob + k] = bad ? -1 : (k < n ? P.tokens[tb + k] : (k == n ? token : -1));
     if (P.mode == MODE_SAMPLE) {
         const bool sampled = desc.state == SREQ_RESID || desc.state == SREQ_BONUS;
-        for (int k = lane; k < K; k += 64) {
+        for (int k = lane; k < rb.nout - 1; k += 64) {
             const float2 v = (sampled && k < d) ? pq[k] : make_float2(0.0f, 0.0f);
             if (P.p_draft) P.p_draft[tb + k] = v.x;
             if (P.q_draft) P.q_draft[tb + k] = v.y;
@@ -1375,7 +1435,7 @@ __device__ ReqDesc scan_window(const Params &P, int b, const ReqPlan &q, const S
 {
     const int nd = q.d, lo = q.lo;
     const int lane = lane_id();
-    const int64_t tb = (int64_t)b * P.K + lo;
+    const int64_t tb = q.rb.db + lo;
     ReqDesc desc = {SREQ_BAD, 0, -1, q.T};
     if (q.kind == KIND_BAD) return desc;
     if (q.kind == KIND_DONE) return {SREQ_DONE, 0, -1, q.T};
@@ -1440,8 +1500,9 @@ __device__ ReqDesc scan_window(const Params &P, int b, const ReqPlan &q, const S
 __device__ void write_window(const Params &P, int b, const ReqPlan &q, const ReqDesc &desc, const float2 *pq,
                              int token)
 {
-    const int K = P.K, lane = lane_id();
-    const int64_t ob = (int64_t)b * (K + 1), tb = (int64_t)b * K;
+    const int lane = lane_id();
+    const int64_t ob = q.rb.tb, tb = q.rb.db;
+    const int K = q.rb.nout - 1;
     if (desc.state == SREQ_DONE) return;
     const bool bad = desc.state == SREQ_BAD, cont = desc.state == SREQ_CONT;
     const int n = desc.n, lo = q.lo, hi = q.lo + q.d;
@@ -1690,12 +1751,13 @@ __device__ __forceinline__ double draw_exp_arg(float v, double m, double mc5, do
 }
 
 template <bool BF16>
-__device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int b, const ReqDesc &desc, float Mz, float My)
+__device__ __forceinline__ DrawRows<BF16> draw_rows(const Params &P, int64_t tb, int64_t db, const ReqDesc &desc,
+                                                    float Mz, float My)
 {
     DrawRows<BF16> r;
     const int64_t esz = BF16 ? 2 : 4;
-    r.rz = RowView<BF16>((const char *)P.target + ((int64_t)b * (P.K + 1) + desc.n) * P.V * esz, P.V);
-    r.dc.yrow = (const char *)P.draft + ((int64_t)b * P.K + desc.n) * P.V * esz;
+    r.rz = RowView<BF16>((const char *)P.target + (tb + desc.n) * P.V * esz, P.V);
+    r.dc.yrow = (const char *)P.draft + (db + desc.n) * P.V * esz;
     r.dc.ry = RowView<BF16>(r.dc.yrow, P.V);
     r.cd = LOG2E / (double)desc.T;
     r.mz = (double)Mz;
@@ -1906,7 +1968,7 @@ __device__ void units_from_record(const Params &P, int b, int c, double *tab, Ch
     if (!SPLIT && c * NWAVE + wave_id() >= P.cs) return;
     const bool resid = rec.state == SREQ_RESID;
     const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
-    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
+    const DrawRows<BF16> dr = draw_rows<BF16>(P, rec.tb, rec.db, desc, rec.mz, rec.my);
     unit_sums_store<BF16, ALIGNED, SPLIT>(P, b, c, dr, resid, rec.rho_hat, tab, sh);
 }
 
@@ -1934,6 +1996,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // the request's plan and the row pass's chunking are read before the
     // table is built, so their loads overlap its arithmetic
     const int cpr = P.ws.meta[0];
+    const int offs_bad = P.offs ? P.ws.meta[2] : 0;   // the row pass's verdict on packed offsets
     // request b's partials start at slot row b * (2K + 1)
     const int pre = b * (2 * P.K + 1);
     const int tpr = merge_tpr(2 * P.K + 1, P.cpr_max);
@@ -1941,17 +2004,24 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // the scan's inputs for positions lo..lo+63, issued with the plan's loads
     // so their latencies overlap each other, the table and the merge; every
     // wave loads them (no branch), from a stand-in where an argument is
-    // unused or absent, and only wave 0's are used
+    // unused or absent, and only wave 0's are used.  (The packed layout's
+    // positions depend on the request's offsets: loaded after the plan.)
     const int lo = EE ? P.win_lo : 0;
     const int l = min(lo + lane_id(), max(P.K - 1, 0));
-    const bool has_tok = P.mode != MODE_CONF && P.K > 0;
-    const bool has_u = P.mode == MODE_SAMPLE && P.K > 0;
+    const bool has_tok = P.mode != MODE_CONF && P.K > 0 && !P.offs;
+    const bool has_u = P.mode == MODE_SAMPLE && P.K > 0 && !P.offs;
     const int32_t *tokp = has_tok ? P.tokens + (int64_t)b * P.K + l : &k_stand_in;
     const float *uap = has_u ? P.u_accept + (int64_t)b * P.K + l : (const float *)&k_stand_in;
     const float *usp = P.mode == MODE_SAMPLE ? P.u_sample + b : (const float *)&k_stand_in;
-    const int x0 = *tokp;
-    const float ua0 = *uap, us0 = *usp;
-    const ReqPlan q = plan_request<EE>(P, b);
+    int x0 = *tokp;
+    float ua0 = *uap;
+    const float us0 = *usp;
+    const ReqPlan q = plan_request<EE>(P, b, offs_bad != 0);
+    if (P.offs && q.d > 0) {
+        const int64_t i = q.rb.db + min(lo + lane_id(), lo + q.d - 1);
+        x0 = P.tokens[i];
+        ua0 = P.mode == MODE_SAMPLE ? P.u_accept[i] : 0.0f;
+    }
     if (q.kind == KIND_DONE) {   // early-exit calls: ended in an earlier window
         if (c == 0 && tid == 0) P.alive_out[b] = 0;
         if (EE && P.ee_last && P.mode == MODE_SAMPLE) units_from_record<BF16, ALIGNED, SPLIT>(P, b, c, tab, sh_parts);
@@ -2016,7 +2086,7 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
             write_window(P, b, q, desc, pq_s, token);
             if (lane_id() == 0) P.alive_out[b] = desc.state == SREQ_CONT;
         } else {
-            write_outputs(P, b, d, desc, pq_s, token);
+            write_outputs(P, b, d, q.rb, desc, pq_s, token);
         }
         if (P.mode == MODE_SAMPLE && lane_id() == 0) {
             DrawRec r;
@@ -2025,7 +2095,10 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
             r.T = desc.T;
             r.mz = resid ? sz_row.m : 0.0f;
             r.my = resid ? sy_row.m : 0.0f;
-            r.pad = 0.0f;
+            r.tb = (int32_t)q.rb.tb;
+            r.db = (int32_t)q.rb.db;
+            r.nout = q.rb.nout;
+            r.pad[0] = r.pad[1] = 0;
             r.rho_hat = rho_hat;
             P.ws.rec[b] = r;
         }
@@ -2036,7 +2109,8 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // this wave's unit of the drawn row pair (SPLIT: its part of one)
     if (!SPLIT && c * NWAVE + wave_id() >= P.cs) return;
     __builtin_amdgcn_s_setprio(0);
-    const DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, resid ? sz_row.m : 0.0f, resid ? sy_row.m : 0.0f);
+    const DrawRows<BF16> dr =
+        draw_rows<BF16>(P, q.rb.tb, q.rb.db, desc, resid ? sz_row.m : 0.0f, resid ? sy_row.m : 0.0f);
     unit_sums_store<BF16, ALIGNED, SPLIT>(P, b, c, dr, resid, rho_hat, tab, sh_parts);
 }
 
@@ -2234,12 +2308,12 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
     init_exp2_table_wave(tab);
     const bool resid = rec.state == SREQ_RESID;
     const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
-    DrawRows<BF16> dr = draw_rows<BF16>(P, b, desc, rec.mz, rec.my);
+    DrawRows<BF16> dr = draw_rows<BF16>(P, rec.tb, rec.db, desc, rec.mz, rec.my);
     const UnitPick k = pick_unit<BF16>(P, b, rec, dr, tab, c0, u0);
     if (k.bad || k.cstar < 0) {   // the drawn row holds NaN, +inf or nothing but -inf
         if (w == 0) {
             const ReqDesc bd = {SREQ_BAD, 0, -1, rec.T};
-            write_outputs(P, b, 0, bd, nullptr, -1);
+            write_outputs(P, b, 0, {rec.tb, rec.db, rec.nout}, bd, nullptr, -1);
         }
         return;
     }
@@ -2329,10 +2403,10 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
     }
     const int tok = (!k.over && fi != 0x7fffffff) ? fi : lp;
     if (tok >= 0) {
-        if (lane == 0) P.out_tokens[(int64_t)b * (P.K + 1) + rec.n] = tok;
+        if (lane == 0) P.out_tokens[(int64_t)rec.tb + rec.n] = tok;
     } else {
         const ReqDesc bd = {SREQ_BAD, 0, -1, rec.T};
-        write_outputs(P, b, 0, bd, nullptr, -1);
+        write_outputs(P, b, 0, {rec.tb, rec.db, rec.nout}, bd, nullptr, -1);
     }
 }
 
@@ -2948,6 +3022,17 @@ sv_status check_shape(int32_t B, int32_t K, int32_t V)
     return SV_OK;
 }
 
+// Packed layout: the number of drafted positions the packed arrays hold
+// (row and slot indices stay below 2^31 with B <= B_MAX added).
+constexpr int32_t PACKED_ROWS_MAX = 1 << 30;
+
+sv_status check_packed(int32_t n_rows)
+{
+    if (n_rows < 0) return SV_ERR_INVALID_ARG;
+    if (n_rows > PACKED_ROWS_MAX) return SV_ERR_UNSUPPORTED;
+    return SV_OK;
+}
+
 sv_status check_ws(void *ws, size_t ws_bytes, const Layout &L)
 {
     if (!ws || ws_bytes < L.total || ((uintptr_t)ws & 255u) != 0) return SV_ERR_WORKSPACE;
@@ -3255,6 +3340,65 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
     P.p_draft = p_draft;
     P.q_draft = q_draft;
     return checked(launch(P, stream), num_accepted, B, stream, "spec_verify_sample");
+}
+
+sv_status spec_verify_greedy_packed(const void *target_logits, sv_dtype dt, const int32_t *draft_tokens,
+                                    const int32_t *draft_offsets, int32_t B, int32_t K_max, int32_t n_draft_rows,
+                                    int32_t V, int32_t *out_tokens, int32_t *num_accepted, void *workspace,
+                                    size_t ws_bytes, hipStream_t stream)
+{
+    sv_status st = check_shape(B, K_max, V);
+    if (st != SV_OK) return st;
+    if ((st = check_packed(n_draft_rows)) != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (!target_logits || !draft_offsets || !out_tokens || !num_accepted || (n_draft_rows > 0 && !draft_tokens))
+        return SV_ERR_INVALID_ARG;
+    if (!aligned16(target_logits)) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K_max, V, L);
+    if ((st = check_ws(workspace, ws_bytes, L)) != SV_OK) return st;
+    Params P = base_params(B, K_max, V, dt, MODE_GREEDY, L, workspace);
+    P.target = target_logits;
+    P.tokens = draft_tokens;
+    P.offs = draft_offsets;
+    P.n_rows = n_draft_rows;
+    P.out_tokens = out_tokens;
+    P.num_accepted = num_accepted;
+    return checked(launch(P, stream), num_accepted, B, stream, "spec_verify_greedy_packed");
+}
+
+sv_status spec_verify_sample_packed(const void *target_logits, const void *draft_logits, sv_dtype dt,
+                                    const int32_t *draft_tokens, const int32_t *draft_offsets,
+                                    const float *temperature, const float *u_accept, const float *u_sample,
+                                    int32_t B, int32_t K_max, int32_t n_draft_rows, int32_t V, int32_t *out_tokens,
+                                    int32_t *num_accepted, float *p_draft, float *q_draft, void *workspace,
+                                    size_t ws_bytes, hipStream_t stream)
+{
+    sv_status st = check_shape(B, K_max, V);
+    if (st != SV_OK) return st;
+    if ((st = check_packed(n_draft_rows)) != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (!target_logits || !draft_offsets || !temperature || !u_sample || !out_tokens || !num_accepted)
+        return SV_ERR_INVALID_ARG;
+    if (n_draft_rows > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+    if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits))) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K_max, V, L);
+    if ((st = check_ws(workspace, ws_bytes, L)) != SV_OK) return st;
+    Params P = base_params(B, K_max, V, dt, MODE_SAMPLE, L, workspace);
+    P.target = target_logits;
+    P.draft = draft_logits;
+    P.tokens = draft_tokens;
+    P.offs = draft_offsets;
+    P.n_rows = n_draft_rows;
+    P.temperature = temperature;
+    P.u_accept = u_accept;
+    P.u_sample = u_sample;
+    P.out_tokens = out_tokens;
+    P.num_accepted = num_accepted;
+    P.p_draft = p_draft;
+    P.q_draft = q_draft;
+    return checked(launch(P, stream), num_accepted, B, stream, "spec_verify_sample_packed");
 }
 
 sv_status spec_verify_sample_noalloc(const void *target_logits, const void *draft_logits, sv_dtype dt,

@@ -176,6 +176,56 @@ sv_status spec_verify_sample(const void *target_logits, const void *draft_logits
                              float *p_draft, float *q_draft,
                              void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Packed (CSR) layout of the two verify calls.  D-cut gives every request
+ * its own verification depth ([Stack], section "What problem does it
+ * solve", inference layer; [Remio], section "Come AngelSpec rende DFly più
+ * selettivo"), so a serving engine holds logits only for the positions it
+ * verifies: request b's drafted positions are o_b .. o_{b+1} - 1 of one flat
+ * array, o = draft_offsets, and its depth is d_b = o_{b+1} - o_b.  Same
+ * rules, outputs and kernels as spec_verify_greedy / spec_verify_sample
+ * with depth[b] = d_b; only the addresses differ:
+ *   target_logits  [n_draft_rows + B, V]: target row k of request b at
+ *                  o_b + b + k, k = 0..d_b (d_b + 1 rows per request)
+ *   draft_logits   [n_draft_rows, V]: draft row k of request b at o_b + k
+ *   draft_tokens, u_accept, p_draft, q_draft  [n_draft_rows]: slot o_b + k
+ *   out_tokens     [n_draft_rows + B] int32: slot o_b + b + k, k = 0..d_b
+ *   draft_offsets  [B + 1] int32 device array (read on the device)
+ *   temperature, u_sample, num_accepted  [B] as in the padded calls
+ *   K_max          the largest depth accepted (sizes the workspace:
+ *                  spec_verify_workspace_size(B, K_max, V)); a request with
+ *                  d_b > K_max is bad data
+ *   n_draft_rows   positions the packed arrays hold, 0 <= n <= 2^30
+ * Offsets.  They must form a CSR array: 0 <= o_0 <= o_1 <= ... <= o_B <=
+ *   n_draft_rows (o_0 need not be 0).  If they do not, no request's rows or
+ *   slots are defined: every num_accepted[b] is -1 and nothing else is
+ *   written.  Otherwise bad data is reported per request as in the padded
+ *   calls, with -1 in the request's own d_b + 1 output slots.
+ * Pointers.  draft_tokens, draft_logits and u_accept may be NULL when
+ *   n_draft_rows is 0.  The packed calls do not take draft statistics
+ *   (spec_verify_sample_reuse) or windows (the early-exit calls). */
+sv_status spec_verify_greedy_packed(const void *target_logits, sv_dtype dt,
+                                    const int32_t *draft_tokens,
+                                    const int32_t *draft_offsets,
+                                    int32_t B, int32_t K_max,
+                                    int32_t n_draft_rows, int32_t V,
+                                    int32_t *out_tokens, int32_t *num_accepted,
+                                    void *workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
+sv_status spec_verify_sample_packed(const void *target_logits,
+                                    const void *draft_logits, sv_dtype dt,
+                                    const int32_t *draft_tokens,
+                                    const int32_t *draft_offsets,
+                                    const float *temperature,
+                                    const float *u_accept,
+                                    const float *u_sample,
+                                    int32_t B, int32_t K_max,
+                                    int32_t n_draft_rows, int32_t V,
+                                    int32_t *out_tokens, int32_t *num_accepted,
+                                    float *p_draft, float *q_draft,
+                                    void *workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
 /* Allocation-free variant of spec_verify_sample, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, rules, outputs and

@@ -140,3 +140,85 @@ def run_sample_reuse(w: synth.Workload, depth=None, max_depth=None):
                                           dev(w.u_accept), dev(w.u_sample), st, dev(depth))
     torch.cuda.synchronize()
     return host(out), host(n), host(p), host(q)
+
+
+# ------------------------------------------------------- packed layout ----
+
+def _poison(dtype):
+    """A value no parity case expects to be read: NaN logits (bf16 bits for
+    uint16)."""
+    return np.uint16(0x7FC0) if dtype == np.uint16 else np.float32(np.nan)
+
+
+class Packed:
+    """Packed (CSR) copy of a padded workload's first depth[b] drafted
+    positions per request: offsets o (o_0 = start), target rows (b, 0..d_b)
+    at o_b + b + k, draft rows, tokens and accept uniforms (b, k < d_b) at
+    o_b + k.  `slack` unused positions follow o_B; unused rows hold NaN and
+    unused tokens / uniforms invalid values, so a stray read shows up."""
+
+    def __init__(self, w: synth.Workload, depth, start: int = 0, slack: int = 0, offsets=None):
+        d = np.asarray(depth, np.int64)
+        B, K, V = w.B, w.K, w.V
+        self.depth = d
+        if offsets is None:
+            offsets = start + np.concatenate([[0], np.cumsum(d)])
+        self.offsets = np.asarray(offsets, np.int64).astype(np.int32)
+        self.N = int(start + d.sum() + slack)
+        N = self.N
+        self.target = np.full((N + B, V), _poison(w.target.dtype), w.target.dtype)
+        self.draft = np.full((N, V), _poison(w.draft.dtype), w.draft.dtype)
+        self.tokens = np.full(N, -7, np.int32)
+        self.u_accept = np.full(N, 2.0, np.float32)
+        for b in range(B):
+            o = int(self.offsets[b])
+            db = int(d[b])
+            if db < 0 or db > K:
+                continue
+            self.target[o + b:o + b + db + 1] = w.target[b, :db + 1]
+            self.draft[o:o + db] = w.draft[b, :db]
+            self.tokens[o:o + db] = w.tokens[b, :db]
+            self.u_accept[o:o + db] = w.u_accept[b, :db]
+
+    def unpack(self, w: synth.Workload, out, p=None, q=None):
+        """Padded [B, K+1] / [B, K] views of packed outputs (-1 / 0 past each
+        request's slots), and the mask of packed output slots no request owns."""
+        B, K = w.B, w.K
+        out_pad = np.full((B, K + 1), -1, np.int32)
+        p_pad = np.zeros((B, K), np.float32)
+        q_pad = np.zeros((B, K), np.float32)
+        owned = np.zeros(self.N + B, bool)
+        for b in range(B):
+            o, db = int(self.offsets[b]), int(self.depth[b])
+            if db < 0 or db > K:
+                continue
+            out_pad[b, :db + 1] = out[o + b:o + b + db + 1]
+            owned[o + b:o + b + db + 1] = True
+            if p is not None:
+                p_pad[b, :db] = p[o:o + db]
+                q_pad[b, :db] = q[o:o + db]
+        return out_pad, p_pad, q_pad, ~owned
+
+
+def run_greedy_packed(pk: Packed, K_max: int, sentinel: int = -99):
+    import draft_verification_verify_amd as sv
+    B = pk.offsets.size - 1
+    out = torch.full((pk.N + B,), sentinel, dtype=torch.int32, device="cuda")
+    num = torch.full((B,), sentinel, dtype=torch.int32, device="cuda")
+    sv.verify_greedy_packed(dev(pk.target), dev(pk.tokens), dev(pk.offsets), K_max, out_tokens=out, num_accepted=num)
+    torch.cuda.synchronize()
+    return host(out), host(num)
+
+
+def run_sample_packed(pk: Packed, w: synth.Workload, K_max: int, sentinel: int = -99):
+    import draft_verification_verify_amd as sv
+    B = pk.offsets.size - 1
+    out = torch.full((pk.N + B,), sentinel, dtype=torch.int32, device="cuda")
+    num = torch.full((B,), sentinel, dtype=torch.int32, device="cuda")
+    p = torch.full((pk.N,), -3.0, dtype=torch.float32, device="cuda")
+    q = torch.full((pk.N,), -3.0, dtype=torch.float32, device="cuda")
+    sv.verify_sample_packed(dev(pk.target), dev(pk.draft), dev(pk.tokens), dev(pk.offsets), dev(w.temperature),
+                            dev(pk.u_accept), dev(w.u_sample), K_max, out_tokens=out, num_accepted=num,
+                            p_draft=p, q_draft=q)
+    torch.cuda.synchronize()
+    return host(out), host(num), host(p), host(q)

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -115,6 +115,29 @@ def test_sample_host_errors():
     assert sample(dt=2) == 1
     assert sample(B=0) == 1
     assert sample(wsb=10) == 3
+
+
+def test_packed_host_errors():
+    wsb = sv.workspace_size(4, 3, 1000)
+
+    def g(target=FAKE, dt=1, tokens=FAKE, offs=FAKE, B=4, K=3, N=8, V=1000, out=FAKE, num=FAKE, ws=FAKE, n=wsb):
+        return L.spec_verify_greedy_packed(target, dt, tokens, offs, B, K, N, V, out, num, ws, n, NULL)
+
+    def s(target=FAKE, draft=FAKE, tokens=FAKE, offs=FAKE, T=FAKE, ua=FAKE, us=FAKE, B=4, K=3, N=8, out=FAKE,
+          num=FAKE, ws=FAKE, n=wsb):
+        return L.spec_verify_sample_packed(target, draft, 1, tokens, offs, T, ua, us, B, K, N, 1000, out, num,
+                                           NULL, NULL, ws, n, NULL)
+
+    assert g(offs=NULL) == 1 and g(target=NULL) == 1 and g(tokens=NULL) == 1 and g(out=NULL) == 1
+    assert g(num=NULL) == 1 and g(dt=3) == 1 and g(target=FAKE_MIS) == 1
+    assert g(N=-1) == 1 and g(N=(1 << 30) + 1) == 2 and g(B=0) == 1 and g(K=2000) == 2
+    assert g(ws=NULL) == 3 and g(n=64) == 3
+    # no drafted positions: the tokens may be NULL (the workspace check is then reached)
+    assert g(tokens=NULL, N=0, ws=NULL) == 3
+    assert s(offs=NULL) == 1 and s(target=NULL) == 1 and s(T=NULL) == 1 and s(us=NULL) == 1
+    assert s(draft=NULL) == 1 and s(tokens=NULL) == 1 and s(ua=NULL) == 1 and s(draft=FAKE_MIS) == 1
+    assert s(N=-5) == 1 and s(N=(1 << 30) + 1) == 2 and s(n=10) == 3
+    assert s(draft=NULL, tokens=NULL, ua=NULL, N=0, ws=NULL) == 3
 
 
 def test_early_exit_host_errors():
