@@ -75,6 +75,7 @@ constexpr int DCUT_MAX = 32768;   // B*K for dcut_allocate (keys held in LDS)
 constexpr int DCUT_WG = 1024;
 constexpr int EXP2_TAB = 512;     // table entries of the fp64 exp2
 constexpr int SLOT_MAX = 4;       // dispatch slots of the row pass told apart
+constexpr uint32_t ROUND_SHIFT = 5;   // row pass: rotation of the task order per round
 // Task-count slope across dispatch slots, measured on MI355X on the dense
 // B=64, K=16, V=128000 bf16 batch (greedy and sampled).  Per-slot task counts
 // round to whole tasks, so nearby slopes can give the same schedule or
@@ -1209,9 +1210,14 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     // and win more issue cycles, so slot group s gets n_s tasks per wave,
     // n_s = ceil(avg * (1 + skew * ((nslot - 1) / 2 - s))), non-increasing in
     // s.  Round k is run by the slot groups with n_s > k -- a prefix of the
-    // waves, of size A_k -- and wave gw's round-k task is pre_k + gw, with
-    // pre_k the tasks of the earlier rounds.  Skew 0 is the plain round robin
-    // w, w + nwaves, ...  All loop state is wave-uniform (scalar).
+    // waves, of size A_k -- and wave gw's round-k task is
+    // pre_k + (gw + ROUND_SHIFT * k) mod A_k, with pre_k the tasks of the
+    // earlier rounds (a rotation: each round's tasks go to its waves one to
+    // one).  Without the rotation a wave would meet the same chunk position
+    // in every round whenever A_k is a multiple of the chunks per row, and
+    // chunk positions differ in work: the first chunk of a sampled row also
+    // loads the logit at the drafted token, the last is usually short.  All
+    // loop state is wave-uniform (scalar).
     const uint32_t ntask = (uint32_t)R * (uint32_t)cpr;
     const uint32_t gw = blockIdx.x * NWAVE + (uint32_t)__builtin_amdgcn_readfirstlane(wave_id());
     if (gw >= ntask) return;
@@ -1262,7 +1268,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
         const int k1 = k.k + 1;
         if (k1 >= mytasks) return false;
         const uint32_t pre1 = k.pre + active(k.k);
-        const uint32_t t = pre1 + gw;
+        const uint32_t t = pre1 + (gw + ROUND_SHIFT * (uint32_t)k1) % active(k1);
         if (t >= ntask) return false;
         const int r = __builtin_amdgcn_readfirstlane((int)(t / (uint32_t)cpr));
         const int c = (int)t - r * cpr;
