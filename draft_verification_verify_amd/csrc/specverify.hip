@@ -518,12 +518,16 @@ __device__ double wg_excl_scan(double v, double *sm4, double &total)
     return wb + excl;
 }
 
-// fp64 2^(s/512) for s <= 0, within 1e-14 relative (the sampler needs
-// per-term accuracy far below 1e-10, not correct rounding).  s = k + r with
+// fp64 2^(s/512) for s <= 0, within 6e-11 relative, not correctly rounded.
+// The sampler's sums compare a uniform with a residual CDF to within 1e-6
+// of the residual's mass R; a per-term relative error e moves that CDF by at
+// most about 2e/R (R as a fraction of the row's mass), so 6e-11 holds the
+// band for every R above 1e-4, and a rejection whose residual holds less
+// than that happens with probability below 1e-4.  s = k + r with
 // k = round(s) taken from the low word of s + 1.5*2^52, |r| <= 1/2;
 // 2^(k/512) = 2^(k >> 9) * T[k & 511] with T[j] = 2^(j/512) tabulated in LDS
-// at kernel start, and 2^(r/512) by its Taylor polynomial of degree 3
-// (truncation below 1e-14 relative).  Taking the argument pre-scaled by 512
+// at kernel start, and 2^(r/512) = e^x, |x| <= ln2/1024, by its Taylor
+// polynomial of degree 2 (truncation x^3/6 < 5.2e-11).  Taking the argument pre-scaled by 512
 // lets callers fold the scale into their own constants.  s is clamped at
 // -2000*512, so -inf (a masked logit) and anything below 2^-2000 give exactly
 // 0 through ldexp's underflow; a NaN argument also gives 0 (rows holding NaN
@@ -554,13 +558,12 @@ __device__ void init_exp2_table(double *tab)
 __device__ __forceinline__ double exp2_512(double s, const double *tab)
 {
     constexpr double SHIFT = 6755399441055744.0;   // 1.5 * 2^52
-    constexpr double D1 = LN2 / EXP2_TAB, D2 = D1 * D1 / 2.0, D3 = D1 * D1 * D1 / 6.0;
+    constexpr double D1 = LN2 / EXP2_TAB, D2 = D1 * D1 / 2.0;
     s = __builtin_fmax(s, -2000.0 * EXP2_TAB);
     const double kb = s + SHIFT;
     const int k = (int)(uint32_t)(uint64_t)__double_as_longlong(kb);
     const double r = s - (kb - SHIFT);
-    double p = fma(r, D3, D2);
-    p = fma(r, p, D1);
+    double p = fma(r, D2, D1);
     p = fma(r, p, 1.0);
     return ldexp(tab[k & (EXP2_TAB - 1)] * p, k >> 9);
 }
