@@ -23,6 +23,10 @@ Profiling helpers (run under rocprofv3; see the summaries under profiles/):
     python bench.py --early-exit-ends 4,16
                                           times only early-exit calls with those
                                           window ends (for kernel traces)
+    python bench.py --trace-shape k3      times only the K=3 chat calls (B=4,
+                                          sampled, then greedy), for traces
+    python bench.py --trace-shape greedy  times only greedy calls on the
+                                          headline batch, for traces
     python bench.py --pmc-pass            a few headline steps, then a plain
                                           device copy of 512 MiB (counter
                                           calibration); prints the kernel names
@@ -56,11 +60,11 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "96edfd8588940e326dfc2c77409a8fb1355e2a68fd2410b720e87db61bf02c50",
-                    "fetch_bytes": 525251139, "write_bytes": 536401,
+ROW_PASS_TRAFFIC = {"source_sha256": "aa8c3c8a370f40e53db525c7ea88bdd850c28c9899bcacad9ca6feb6f125da31",
+                    "fetch_bytes": 525405182, "write_bytes": 658261,
                     # SQ counters of the same source (one --pmc run of eight SQ counters):
                     # VALU instructions and busy cycles per dispatch, summed over the device
-                    "sq_insts_valu": 30573955, "sq_busy_cycles": 5662837}
+                    "sq_insts_valu": 31931139, "sq_busy_cycles": 5769815}
 
 
 def parse():
@@ -78,6 +82,9 @@ def parse():
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR")
     ap.add_argument("--early-exit-ends", default="", metavar="E1,E2,...",
                     help="time only early-exit calls with these window ends (for kernel traces)")
+    ap.add_argument("--trace-shape", choices=("k3", "greedy"), default="",
+                    help="time only the K=3 chat shape (B=4, sampled then greedy) or the greedy headline "
+                         "batch, eager calls (for kernel traces)")
     return ap.parse_args()
 
 
@@ -259,6 +266,36 @@ def main():
         _, eper, _ = timed(estep, args.steps, args.warmup)
         print(json.dumps({"early_exit_ends": ends, "ms_per_call": float(np.mean(eper)), "steps": args.steps,
                           "mean_accepted": float(nacc.float().mean().item())}))
+        return
+
+    if args.trace_shape:
+        report = {"trace_shape": args.trace_shape, "steps": args.steps, "warmup": args.warmup}
+        if args.trace_shape == "greedy":
+            wg = synth.dcut_ragged(args.seed, T=0.0)
+            gt = dev(wg.target)
+            gcopies = [gt] + [gt.clone() for _ in range(max(2, -(-512 * 2**20 // wg.target.nbytes) + 1) - 1)]
+            gtok = dev(wg.tokens)
+            _, gper, _ = timed(lambda i: sv.verify_greedy(gcopies[i % len(gcopies)], gtok, out_tokens=out,
+                                                          num_accepted=nacc, workspace=ws, stream=stream),
+                               args.steps, args.warmup)
+            report["greedy_ms_per_call"] = float(np.mean(gper))
+        else:
+            for mode in ("sample", "greedy"):
+                wc = synth.mtp_chat(args.seed, T=1.0 if mode == "sample" else 0.0)
+                ct, cd = dev(wc.target), dev(wc.draft)
+                ctok, cT, cua, cus = dev(wc.tokens), dev(wc.temperature), dev(wc.u_accept), dev(wc.u_sample)
+                cout = torch.empty((wc.B, wc.K + 1), dtype=torch.int32, device="cuda")
+                cn = torch.empty((wc.B,), dtype=torch.int32, device="cuda")
+
+                def cstep(i, mode=mode):
+                    if mode == "sample":
+                        sv.verify_sample(ct, cd, ctok, cT, cua, cus, out_tokens=cout, num_accepted=cn,
+                                         want_probs=False, workspace=ws, stream=stream)
+                    else:
+                        sv.verify_greedy(ct, ctok, out_tokens=cout, num_accepted=cn, workspace=ws, stream=stream)
+                _, cper, _ = timed(cstep, args.steps, args.warmup)
+                report[f"k3_{mode}_ms_per_call"] = float(np.mean(cper))
+        print(json.dumps(report))
         return
 
     # The library's per-kernel events (on the launch stream, around each
