@@ -631,28 +631,34 @@ def main():
             "note": "confidence over all max_depth draft rows + dcut_allocate + one mixed-K/T sampled launch; "
                     "two input copies rotated"}
         # the same pipeline with the confidence pass's draft-row statistics
-        # reused: only requests at T = 1 skip their draft rows in the verify
+        # reused, taken at T = 1 (only requests at T = 1 skip their draft rows
+        # in the verify) and at each request's own temperature (every sampled
+        # request skips them)
         mst = torch.empty((wm.B, wm.K, 2), dtype=torch.float64, device="cuda")
-
-        def mrstep(i):
-            mt, md = mcopies[i % 2]
-            sv.draft_confidence_stats(md, mK, conf=mconf, stats=mst, workspace=ws, stream=stream)
-            sv.dcut_allocate(mconf, wm.budget, mK, depth_out=mdep, stream=stream)
-            sv.verify_sample_reuse(mt, md, mtok, mT, mua, mus, mst, mdep, out_tokens=mout, num_accepted=mn,
-                                   want_probs=False, workspace=ws, stream=stream)
-        _, mrper, _ = timed(mrstep, steps2, warm2)
-        mrms = float(np.mean(mrper))
         Tm = wm.temperature
         row_b = wm.V * 4
         d_t1 = int(np.sum(mdv[Tm == 1.0]))
         d_tx = int(np.sum(mdv[(Tm > 0) & (Tm != 1.0)]))
-        sec["mixed_fp32_reuse_B64_V152064_budget512"] = {
-            "verified_rows_per_s": mrow / (mrms * 1e-3), "ms": mrms, "vs_no_reuse_ms": mms / mrms,
-            "draft_rows_reused_T1": d_t1, "draft_rows_streamed_other_T": d_tx,
-            "bytes_saved_per_step": d_t1 * row_b, "bytes_reuse_at_every_T_would_save": (d_t1 + d_tx) * row_b,
-            "note": "confidence pass with row statistics + dcut_allocate + spec_verify_sample_reuse; the "
-                    "statistics are taken at T = 1, so a request at T = 0.7 still streams its d_b draft rows "
-                    "(T = 0 requests read none)"}
+        for tag, temps in (("T1", None), ("any_T", mT)):
+            def mrstep(i, temps=temps):
+                mt, md = mcopies[i % 2]
+                sv.draft_confidence_stats(md, mK, temperature=temps, conf=mconf, stats=mst, workspace=ws,
+                                          stream=stream)
+                sv.dcut_allocate(mconf, wm.budget, mK, depth_out=mdep, stream=stream)
+                sv.verify_sample_reuse(mt, md, mtok, mT, mua, mus, mst, mdep, out_tokens=mout, num_accepted=mn,
+                                       want_probs=False, workspace=ws, stream=stream)
+            _, mrper, _ = timed(mrstep, steps2, warm2)
+            mrms = float(np.mean(mrper))
+            reused = d_t1 if temps is None else d_t1 + d_tx
+            sec[f"mixed_fp32_reuse_{tag}_B64_V152064_budget512"] = {
+                "verified_rows_per_s": mrow / (mrms * 1e-3), "ms": mrms, "vs_no_reuse_ms": mms / mrms,
+                "draft_rows_reused": reused, "draft_rows_streamed": d_t1 + d_tx - reused,
+                "bytes_saved_per_step": reused * row_b,
+                "note": ("spec_draft_confidence_stats (statistics at T = 1: requests at T = 0.7 still stream "
+                         "their d_b draft rows)" if temps is None else
+                         "spec_draft_confidence_stats_t (statistics at each request's temperature, two sums "
+                         "per row at T != 1)") + " + dcut_allocate + spec_verify_sample_reuse; T = 0 requests "
+                         "read no draft rows"}
         del mcopies, mt0, md0
         result["secondary"] = sec
 

@@ -76,6 +76,8 @@ def _load() -> ctypes.CDLL:
                                                 vp, vp, vp, vp, vp, sz, vp]
     L.spec_draft_confidence.restype = ctypes.c_int
     L.spec_draft_confidence.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, sz, vp]
+    L.spec_draft_confidence_stats_t.restype = ctypes.c_int
+    L.spec_draft_confidence_stats_t.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     L.spec_draft_confidence_stats.restype = ctypes.c_int
     L.spec_draft_confidence_stats.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     L.spec_verify_sample_reuse.restype = ctypes.c_int
@@ -111,7 +113,8 @@ EXPORTED = ("spec_verify_abi_version", "spec_verify_status_string", "spec_verify
             "spec_draft_confidence_stats", "spec_verify_sample_reuse", "spec_accept_stats_update",
             "dcut_allocate_cost", "spec_verify_greedy_early_exit", "spec_verify_sample_early_exit",
             "spec_verify_read_ceiling", "spec_early_exit_plan", "spec_verify_sample_noalloc",
-            "spec_accept_stats_summary", "spec_verify_greedy_packed", "spec_verify_sample_packed")
+            "spec_accept_stats_summary", "spec_verify_greedy_packed", "spec_verify_sample_packed",
+            "spec_draft_confidence_stats_t")
 
 # Bytes of the static scratch array behind spec_verify_sample_noalloc.
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -518,37 +521,49 @@ def draft_confidence(draft, max_depth=None, *, conf=None, workspace=None, stream
     return conf
 
 
-def draft_confidence_stats(draft, max_depth=None, *, conf=None, want_conf: bool = True, stats=None,
-                           workspace=None, stream=None):
+def draft_confidence_stats(draft, max_depth=None, *, temperature=None, conf=None, want_conf: bool = True,
+                           stats=None, workspace=None, stream=None):
     """Draft confidence plus every read draft row's statistics (sv_row_stat
-    records, returned as a float64 tensor [B, K, 2]: see row_stat_fields).
-    Returns (conf or None, stats)."""
+    records, returned as a float64 tensor [B, K, 2]: see row_stat_fields),
+    taken at T = 1, or with `temperature` [B] at each request's own
+    temperature (spec_draft_confidence_stats_t).  Returns (conf or None,
+    stats)."""
     torch = _torch()
     B, K, V = _shape3(draft, "draft")
     dt = _dtype_code(draft)
     _validate((draft, "draft", None, None), (max_depth, "max_depth", torch.int32, (B,)),
+              (temperature, "temperature", torch.float32, (B,)),
               (conf, "conf", torch.float32, (B, K)), (stats, "stats", torch.float64, (B, K, 2)))
     if want_conf and conf is None:
         conf = torch.empty((B, K), dtype=torch.float32, device=draft.device)
     if stats is None:
         stats = torch.empty((B, K, 2), dtype=torch.float64, device=draft.device)
     ws, nbytes = _ws(draft.device, B, K, V, workspace)
-    st = lib.spec_draft_confidence_stats(_ptr(draft), dt, _ptr(max_depth), B, K, V,
-                                         _ptr(conf), _ptr(stats), _ptr(ws), nbytes, _stream(stream))
-    _raise("spec_draft_confidence_stats", st)
+    if temperature is None:
+        st = lib.spec_draft_confidence_stats(_ptr(draft), dt, _ptr(max_depth), B, K, V,
+                                             _ptr(conf), _ptr(stats), _ptr(ws), nbytes, _stream(stream))
+        _raise("spec_draft_confidence_stats", st)
+    else:
+        st = lib.spec_draft_confidence_stats_t(_ptr(draft), dt, _ptr(max_depth), _ptr(temperature), B, K, V,
+                                               _ptr(conf), _ptr(stats), _ptr(ws), nbytes, _stream(stream))
+        _raise("spec_draft_confidence_stats_t", st)
     return conf, stats
 
 
 def row_stat_fields(stats):
-    """(max float32 [B, K], sum float64 [B, K]) of sv_row_stat records."""
-    return stats.view(_torch().float32)[..., 0].contiguous(), stats[..., 1].contiguous()
+    """(max float32 [B, K], sum float64 [B, K], temp float32 [B, K]) of
+    sv_row_stat records (temp: the temperature they were taken at)."""
+    torch = _torch()
+    f = stats.view(torch.float32)
+    return f[..., 0].contiguous(), stats[..., 1].contiguous(), f[..., 1].contiguous()
 
 
 def verify_sample_reuse(target, draft, tokens, temperature, u_accept, u_sample, draft_stats, depth=None, *,
                         out_tokens=None, num_accepted=None, p_draft=None, q_draft=None,
                         want_probs: bool = True, workspace=None, stream=None):
     """verify_sample with the draft rows' statistics from draft_confidence_stats
-    (used for requests at temperature 1)."""
+    (used for every sampled request whose statistics were taken at its own
+    temperature)."""
     torch = _torch()
     B, K1, V = _shape3(target, "target")
     K = K1 - 1

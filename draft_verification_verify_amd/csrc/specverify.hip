@@ -87,7 +87,10 @@ enum : int { MODE_GREEDY = 0, MODE_SAMPLE = 1, MODE_CONF = 2 };
 // KIND_SAMPLED_R: a sampled request at T = 1 whose draft-row statistics come
 // from a confidence pass (the row pass reads its target rows only).
 // KIND_DONE: early-exit calls, a request that ended in an earlier window.
-enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3, KIND_SAMPLED_R = 4, KIND_DONE = 5 };
+// KIND_CONF2: a confidence row whose statistics are also wanted at the
+// request's own temperature T != 1 (two sums over one read of the row).
+enum : int { KIND_GREEDY = 0, KIND_SAMPLED = 1, KIND_CONF = 2, KIND_BAD = 3, KIND_SAMPLED_R = 4, KIND_DONE = 5,
+             KIND_CONF2 = 6 };
 // outcome of a request's accept scan; SREQ_CONT (early-exit calls): every
 // position of the window accepted and the depth lies beyond it; SREQ_DONE:
 // nothing to do in this window
@@ -222,6 +225,7 @@ struct Params {
     float *conf;
     const Stat *dstats_in;   // sampled calls: draft-row statistics [B, K] from a confidence pass, or NULL
     Stat *dstats_out;        // confidence calls: draft-row statistics out [B, K], or NULL
+    const float *conf_temp;  // confidence calls: temperature [B] of the statistics, or NULL (all at T = 1)
     // Packed (CSR) layout, or NULL for the padded one: request b's drafted
     // positions are offs[b] .. offs[b + 1] - 1 of n_rows; K is then the
     // largest depth the call accepts.
@@ -630,8 +634,15 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b, bool off
     const int32_t *ap = (EE && P.win_lo > 0) ? P.alive_in + b : stand_in;
     const int32_t *o0p = P.offs ? P.offs + b : stand_in;
     const int32_t *o1p = P.offs ? P.offs + b + 1 : stand_in;
+    // the temperature the given draft statistics were taken at (the first
+    // record's temp field), and a confidence call's statistics temperature
+    const int32_t *rtp = (P.mode == MODE_SAMPLE && P.dstats_in && P.K > 0)
+                             ? (const int32_t *)(P.dstats_in + (int64_t)b * P.K) + 1 : stand_in;
+    const float *ctp = (P.mode == MODE_CONF && P.conf_temp) ? P.conf_temp + b : (const float *)stand_in;
     int dv = *dp;
     const float tv = *tp;
+    const int rtv = *rtp;
+    const float ctv = *ctp;
     const int av = *ap;
     const int o0 = *o0p, o1 = *o1p;
     const bool have_depth = P.offs || (P.mode == MODE_CONF ? P.max_depth != nullptr : P.depth != nullptr);
@@ -655,14 +666,20 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b, bool off
     if (P.mode == MODE_CONF) {
         q.d = have_depth ? dv : P.K;
         const bool ok = q.d >= 0 && q.d <= P.K;
-        q.kind = ok ? KIND_CONF : KIND_BAD;
+        // statistics at the request's own temperature when one is given and
+        // is a finite T > 0 other than 1; at T = 1 otherwise
+        const bool dual = P.conf_temp && ctv > 0.0f && ctv <= 3.40282347e38f && ctv != 1.0f;
+        q.kind = ok ? (dual ? KIND_CONF2 : KIND_CONF) : KIND_BAD;
+        q.T = dual ? ctv : 1.0f;
         q.rows = ok ? q.d : 0;
     } else {
         q.d = have_depth ? dv : P.K;
         q.T = (P.mode == MODE_SAMPLE) ? tv : 0.0f;
         const bool ok = q.d >= 0 && q.d <= P.K && temp_ok(q.T);
         q.kind = !ok ? KIND_BAD : (q.T > 0.0f ? KIND_SAMPLED : KIND_GREEDY);
-        if (q.kind == KIND_SAMPLED && P.dstats_in && q.T == 1.0f) q.kind = KIND_SAMPLED_R;
+        // reuse the draft rows' statistics when they were taken at this
+        // request's temperature
+        if (q.kind == KIND_SAMPLED && P.dstats_in && rtv == __float_as_int(q.T)) q.kind = KIND_SAMPLED_R;
         q.rows = !ok ? 0 : (q.kind == KIND_SAMPLED ? 2 * q.d : q.kind == KIND_SAMPLED_R ? q.d : q.d + 1);
         if constexpr (EE) {
             q.lo = P.win_lo;
@@ -884,7 +901,7 @@ constexpr double SCALE_SHIFT_AT = 0x1p100;
 
 __device__ __forceinline__ LseScale scale_of(int kind, float T)
 {
-    const double c = LOG2E / (double)(kind == KIND_CONF ? 1.0f : T);
+    const double c = LOG2E / (double)((kind == KIND_CONF || kind == KIND_CONF2) ? 1.0f : T);
     LseScale sc;
     sc.sh = c > SCALE_SHIFT_AT ? 64 : 0;
     sc.c32 = (float)(sc.sh ? c * 0x1p-64 : c);
@@ -1020,6 +1037,89 @@ __device__ __forceinline__ void process_batch(const RowView<BF16> &rv, int vbeg,
 }
 
 
+// Two log-sum-exp statistics of the same row over one read: lane states a
+// (scale sa, T = 1) and b (scale sb, a request's own temperature) share the
+// running max M.  State a takes exactly lse_batch's arithmetic (so the
+// confidence is the same bits as the single-statistic pass); state b's terms
+// use the difference form, (v - M) * c, valid for every finite M and scale.
+// A confidence row whose statistics are also wanted at another temperature.
+template <bool BF16, bool EDGE>
+__device__ __forceinline__ void lse_batch2(const RowView<BF16> &rv, int vbeg, const uint4 (&raw)[UW],
+                                           const LseScale &sa, const LseScale &sb, LseLane &a, LseLane &b)
+{
+    constexpr int EPV = RowView<BF16>::EPV;
+    const int lane = lane_id();
+    float bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < UW; ++j) {
+        float f[EPV];
+        widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) bm = fmaxf(bm, f[e]);
+    }
+    if (bm > a.M) {
+        if (a.M != -INFINITY) {
+            a.s *= (double)__builtin_amdgcn_exp2f(scaled_exp(a.M - bm, sa));
+            b.s *= (double)__builtin_amdgcn_exp2f(scaled_exp(a.M - bm, sb));
+        }
+        a.M = b.M = bm;
+        a.mc = bm * sa.c32;
+        a.corr = offset_factor(__builtin_fmaf(bm, sa.c32, -a.mc));
+    }
+    if (a.M == -INFINITY) {
+        int un = 0;
+#pragma unroll
+        for (int j = 0; j < UW; ++j) {
+            float f[EPV];
+            widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
+#pragma unroll
+            for (int e = 0; e < EPV; e += 2) un |= __builtin_isunordered(f[e], f[e + 1]);
+        }
+        if (un) a.s = b.s = NAN;
+        return;
+    }
+    const bool diff_a = sa.sh != 0 || __ballot(!(__builtin_fabsf(a.mc) < 0x1p31f)) != 0;
+    float va[UW], vb[UW];
+    // state a: the single-statistic pass's forms and pairwise tree (same
+    // bits); state b: difference-form terms added in order (fewer live
+    // registers).  The form of a is wave-uniform: one loop per form.
+    auto terms = [&](auto fma_form) {
+        constexpr bool FMA = decltype(fma_form)::value;
+#pragma unroll
+        for (int j = 0; j < UW; ++j) {
+            float f[EPV];
+            widen<BF16, EDGE>(rv, vbeg + j * 64 + lane, raw[j], f);
+            float ta[EPV];
+            float sbv = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                ta[e] = __builtin_amdgcn_exp2f(FMA ? __builtin_fmaf(f[e], sa.c32, -a.mc) : scaled_exp(f[e] - a.M, sa));
+                sbv += __builtin_amdgcn_exp2f(scaled_exp(f[e] - a.M, sb));
+            }
+#pragma unroll
+            for (int w = EPV / 2; w > 0; w >>= 1)
+#pragma unroll
+                for (int e = 0; e < w; ++e) ta[e] += ta[e + w];
+            va[j] = ta[0];
+            vb[j] = sbv;
+            // one vector's terms at a time: interleaving all UW vectors'
+            // temporaries would need more registers than the kernel has
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (diff_a) terms(std::false_type());
+    else terms(std::true_type());
+#pragma unroll
+    for (int w = UW / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int j = 0; j < w; ++j) {
+            va[j] += va[j + w];
+            vb[j] += vb[j + w];
+        }
+    a.s += diff_a ? (double)va[0] : (double)va[0] * a.corr;
+    b.s += (double)vb[0];
+}
+
 // One chunk of one row: its row view and the end b1 of the batches
 // [c * nb, b1) it covers.  A chunk past the end of a short row (rows whose
 // start is not 16-byte aligned cover one vector more) gets one fully masked
@@ -1034,6 +1134,8 @@ struct Task {
     uint32_t pre;  // first task index of round k
     LseScale sc;   // log-sum-exp scale; c32 = 0 marks a greedy (argmax) row
     float zx;      // sampled rows: the row's logit at the drafted token
+    LseScale sc2;  // confidence rows with temperatures: the second statistic's scale
+    int slot2;     // confidence rows with temperatures: the second statistic's partial slot row
     __device__ __forceinline__ bool lse() const { return sc.c32 != 0.0f; }
     __device__ __forceinline__ RowView<BF16> view(int V) const
     {
@@ -1085,7 +1187,16 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     if (kind == KIND_GREEDY) { is_draft = false; kk = local; lse = false; }
     else if (kind == KIND_SAMPLED) { is_draft = local >= d; kk = is_draft ? local - d : local; lse = true; }
     else if (kind == KIND_SAMPLED_R) { is_draft = false; kk = local; lse = true; }
-    else { is_draft = true; kk = local; lse = true; }   // KIND_CONF
+    else { is_draft = true; kk = local; lse = true; }   // KIND_CONF, KIND_CONF2
+    // KIND_CONF2: the statistics at the request's temperature go to slot row
+    // d + local of the request (the confidence's own in row local)
+    k.sc2 = k.sc;
+    k.slot2 = k.slot + d;
+    if (kind == KIND_CONF2) {
+        k.sc2 = scale_of(KIND_SAMPLED, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b]))));
+        k.sc2.c32 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(k.sc2.c32)));
+        k.sc2.sh = __builtin_amdgcn_readfirstlane(k.sc2.sh);
+    }
     if constexpr (EE) kk += P.win_lo;   // the window's first position
     if (lse) {
         k.sc = scale_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b]))));
@@ -1161,29 +1272,53 @@ __device__ __forceinline__ Stat finish_task(const Task<BF16> &k, const ArgmaxLan
 // per batch on every path, so the compiler's load-wait counts stay exact and
 // no wait ever covers a store.  The partial is wave-uniform (butterfly
 // reductions), so every lane stores the same 16 bytes: one write.
-template <bool BF16>
+// DUAL (confidence calls with temperatures; their rows are all log-sum-exp
+// rows): every task keeps two statistics, ls at T = 1 and ls2 at scale sc2
+// (its request's temperature for KIND_CONF2, else T = 1 again), and stores
+// both, the second into slot row slot2 (for a KIND_CONF request a row the
+// finish kernel does not read).  One path for every task keeps the
+// compiler's wait counts exact, as in the single-statistic kernel.
+template <bool BF16, bool DUAL>
 __device__ __forceinline__ void consume(const Params &P, const Task<BF16> &k, int i, const uint4 (&raw)[UW],
-                                        ArgmaxLane &am, LseLane &ls)
+                                        ArgmaxLane &am, LseLane &ls, LseLane &ls2)
 {
-    if (k.lse()) process_batch<BF16, true>(k.view(P.V), i * WVEC, raw, k.sc, ls);
-    else process_batch<BF16, false>(k.view(P.V), i * WVEC, raw, k.sc, am);
-    Stat st;
+    Stat st, st2;
+    if constexpr (DUAL) {
+        const RowView<BF16> rv = k.view(P.V);
+        if (rv.batch_edge(i * WVEC, WVEC)) lse_batch2<BF16, true>(rv, i * WVEC, raw, k.sc, k.sc2, ls, ls2);
+        else lse_batch2<BF16, false>(rv, i * WVEC, raw, k.sc, k.sc2, ls, ls2);
+    } else if (k.lse()) {
+        process_batch<BF16, true>(k.view(P.V), i * WVEC, raw, k.sc, ls);
+    } else {
+        process_batch<BF16, false>(k.view(P.V), i * WVEC, raw, k.sc, am);
+    }
     if (i + 1 >= k.b1) {
         st = finish_task<BF16>(k, am, ls);
+        if constexpr (DUAL) st2 = finish_task(true, am, ls2, k.sc2);
         am = ArgmaxLane();
         ls = LseLane();
+        if constexpr (DUAL) ls2 = LseLane();
     } else {
         st.m = 0.0f;
         st.idx = 0;
         st.s = 0.0;
+        st2 = st;
     }
+    if constexpr (DUAL) P.ws.part[(int64_t)k.slot2 * P.cpr_max + k.c] = st2;
     P.ws.part[(int64_t)k.slot * P.cpr_max + k.c] = st;
 }
 
 // Four waves per SIMD (128 VGPRs) keep enough 16-byte loads in flight per CU
-// to cover HBM latency; the register budget fits without spills.
-template <bool BF16, bool EE>
-__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void row_pass_kernel(Params P)
+// to cover HBM latency; the register budget fits without spills.  DUAL: the
+// instantiation for confidence calls with temperatures (two sums per row);
+// with bf16's eight logits per vector its two sums need more than 128
+// registers: at three waves per SIMD it spills least and ran fastest of
+// two, three and four (measured on MI355X, B=64, K=16, V=128000).
+constexpr int row_waves_per_eu(bool bf16, bool dual) { return bf16 && dual ? 3 : 4; }
+
+template <bool BF16, bool EE, bool DUAL>
+__global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(row_waves_per_eu(BF16, DUAL), 8)))
+void row_pass_kernel(Params P)
 {
     extern __shared__ int plan_smem[];
     __shared__ int scan_tmp[NWAVE];
@@ -1300,18 +1435,23 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     kA.pre = 0;
     Task<BF16> kB = kA;
     int iA = c0 * nb, iB = iA;
+    // stands in for a reduction's stores (one, or two in the DUAL kernel)
+    auto stand_in = [&]() {
+        *spare = zero;
+        if constexpr (DUAL) *spare = zero;
+    };
     bool vB = next_batch(kA, iA, kB, iB);
     issue_batch(kA.vec, kA.nvec, iA * WVEC, A);
-    *spare = zero;
+    stand_in();
     issue_batch(kB.vec, kB.nvec, vB ? iB * WVEC : kB.nvec, Bv);
     ArgmaxLane am;
-    LseLane ls;
+    LseLane ls, ls2;
     for (;;) {
-        consume<BF16>(P, kA, iA, A, am, ls);
+        consume<BF16, DUAL>(P, kA, iA, A, am, ls, ls2);
         const bool vA = vB && next_batch(kB, iB, kA, iA);
         issue_batch(kA.vec, kA.nvec, vA ? iA * WVEC : kA.nvec, A);
-        if (vB) consume<BF16>(P, kB, iB, Bv, am, ls);
-        else *spare = zero;
+        if (vB) consume<BF16, DUAL>(P, kB, iB, Bv, am, ls, ls2);
+        else stand_in();
         vB = vA && next_batch(kA, iA, kB, iB);
         issue_batch(kB.vec, kB.nvec, vB ? iB * WVEC : kB.nvec, Bv);
         if (!vA) break;
@@ -1602,21 +1742,24 @@ __device__ __forceinline__ MergePre merge_prefetch(const Params &P, int pre, int
 // MERGE_LOADS partials of each thread of the first group come from
 // merge_prefetch.  Every workgroup of a request performs the same operations
 // in the same order, so all of them hold identical statistics.
+// Rows from `split` on use the scale cs2 (a confidence call's statistics at
+// a request's own temperature, KIND_CONF2); the others use cs.
 __device__ void merge_rows(const Params &P, int pre, int rows, int tpr, int cpr, bool lse, double cs,
-                           const double *tab, const MergePre &first, Stat *rows_s)
+                           double cs2, int split, const double *tab, const MergePre &first, Stat *rows_s)
 {
     const int tid = threadIdx.x;
     const int G = WG / tpr;
     const Stat ident = {-INFINITY, 0x7fffffff, 0.0};
     for (int g0 = 0; g0 < rows; g0 += G) {
         const int r = g0 + tid / tpr, l = tid & (tpr - 1);
+        const double csr = r < split ? cs : cs2;
         Stat acc = ident;
         if (r < rows) {
             int j0 = l;
             if (g0 == 0) {
 #pragma unroll
                 for (int i = 0; i < MERGE_LOADS; ++i)
-                    if (l + i * tpr < cpr) acc = merge2(acc, first.v[i], lse, cs, tab);
+                    if (l + i * tpr < cpr) acc = merge2(acc, first.v[i], lse, csr, tab);
                 j0 += MERGE_LOADS * tpr;
             }
             // MERGE_LOADS partials in flight per thread (clamped index, no
@@ -1628,7 +1771,7 @@ __device__ void merge_rows(const Params &P, int pre, int rows, int tpr, int cpr,
                 for (int i = 0; i < MERGE_LOADS; ++i) v[i] = pp[min(j0 + i * tpr, cpr - 1)];
 #pragma unroll
                 for (int i = 0; i < MERGE_LOADS; ++i)
-                    if (j0 + i * tpr < cpr) acc = merge2(acc, v[i], lse, cs, tab);
+                    if (j0 + i * tpr < cpr) acc = merge2(acc, v[i], lse, csr, tab);
             }
         }
         // butterfly over the tpr lanes of the row (levels with 2^L < tpr;
@@ -1640,7 +1783,7 @@ __device__ void merge_rows(const Params &P, int pre, int rows, int tpr, int cpr,
                 other.m = xchg_f<L>(acc.m);
                 other.idx = xchg_i<L>(acc.idx);
                 other.s = xchg_d<L>(acc.s);
-                acc = merge2(acc, other, lse, cs, tab);
+                acc = merge2(acc, other, lse, csr, tab);
             }
         };
         level(std::integral_constant<int, 0>());
@@ -2038,22 +2181,32 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     }
     init_exp2_table(tab);
 
-    const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF || q.kind == KIND_SAMPLED_R;
+    const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF || q.kind == KIND_SAMPLED_R ||
+                     q.kind == KIND_CONF2;
     if (q.kind == KIND_SAMPLED_R) {
         // draft rows 0..d-1: the given statistics, with the draft logit at the
         // drafted token in idx (the row pass's convention; a token outside
         // [0, V) is clamped here and rejected by the scan); merge_rows' barrier
-        // publishes them with the merged target rows
+        // publishes them with the merged target rows.  A record taken at
+        // another temperature than the request's (the plan checked the first)
+        // counts as a NaN statistic: the request is bad.
         const int64_t esz = P.bf16 ? 2 : 4;
         for (int k = tid; k < q.d; k += WG) {
             Stat st = P.dstats_in[(int64_t)b * P.K + k];
+            if (st.idx != __float_as_int(q.T)) st.m = NAN;
             const int x = min(max(P.tokens[(int64_t)b * P.K + k], 0), P.V - 1);
             const char *yrow = (const char *)P.draft + ((int64_t)b * P.K + k) * P.V * esz;
             st.idx = __float_as_int(load_logit_dt(yrow, P.bf16 != 0, x));
             rows_s[q.d + k] = st;
         }
     }
-    merge_rows(P, pre, q.rows, tpr, cpr, lse, lse ? scale_d(scale_of(q.kind, q.T)) : 0.0, tab, first, rows_s);
+    // a KIND_CONF2 request also merges its statistics at its temperature,
+    // slot rows d .. 2d - 1
+    const bool conf2 = q.kind == KIND_CONF2;
+    const double cs = lse ? scale_d(scale_of(q.kind, q.T)) : 0.0;
+    const double cs2 = conf2 ? scale_d(scale_of(KIND_SAMPLED, q.T)) : cs;
+    merge_rows(P, pre, conf2 ? 2 * q.d : q.rows, tpr, cpr, lse, cs, cs2, conf2 ? q.d : 0x7fffffff, tab, first,
+               rows_s);
 
     if (P.mode == MODE_CONF) {
         for (int k = tid; k < P.K; k += WG) {
@@ -2066,10 +2219,14 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
                 P.conf[(int64_t)b * P.K + k] = v;
             }
             if (P.dstats_out) {
+                // the statistics at the request's temperature (KIND_CONF2:
+                // merged rows d..2d-1), else at T = 1; the record carries the
+                // temperature it was taken at
+                const int r = q.kind == KIND_CONF2 ? q.d + k : k;
                 Stat st;
-                st.m = have ? rows_s[k].m : NAN;
-                st.idx = 0;
-                st.s = have ? rows_s[k].s : NAN;
+                st.m = have ? rows_s[r].m : NAN;
+                st.idx = __float_as_int(q.kind == KIND_CONF2 ? q.T : 1.0f);
+                st.s = have ? rows_s[r].s : NAN;
                 P.dstats_out[(int64_t)b * P.K + k] = st;
             }
         }
@@ -2980,17 +3137,22 @@ sv_status checked(sv_status st, const int32_t *vals, int32_t n, hipStream_t stre
 // Resident workgroups of the persistent row pass per compute unit (from the
 // occupancy calculator; the grid never exceeds what can run at once, so the
 // static task assignment stays balanced).
-int row_wgs_per_cu(bool bf16, bool ee, size_t lds)
+int row_wgs_per_cu(bool bf16, bool ee, bool dual, size_t lds)
 {
-    static std::atomic<int> cache[2][2][64];
+    static std::atomic<int> cache[2][3][64];
     const int bucket = (int)std::min<size_t>(63, lds / 1024);
-    int n = cache[bf16][ee][bucket].load(std::memory_order_relaxed);
+    const int v = dual ? 2 : ee ? 1 : 0;
+    int n = cache[bf16][v][bucket].load(std::memory_order_relaxed);
     if (n <= 0) {
-        const void *fn = bf16 ? (ee ? (const void *)row_pass_kernel<true, true> : (const void *)row_pass_kernel<true, false>)
-                              : (ee ? (const void *)row_pass_kernel<false, true> : (const void *)row_pass_kernel<false, false>);
+        const void *fn = bf16 ? (dual ? (const void *)row_pass_kernel<true, false, true>
+                                      : ee ? (const void *)row_pass_kernel<true, true, false>
+                                           : (const void *)row_pass_kernel<true, false, false>)
+                              : (dual ? (const void *)row_pass_kernel<false, false, true>
+                                      : ee ? (const void *)row_pass_kernel<false, true, false>
+                                           : (const void *)row_pass_kernel<false, false, false>);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, WG, (bucket + 1) * 1024) != hipSuccess || n <= 0)
             n = 2;
-        cache[bf16][ee][bucket].store(n, std::memory_order_relaxed);
+        cache[bf16][v][bucket].store(n, std::memory_order_relaxed);
     }
     return n;
 }
@@ -3072,7 +3234,8 @@ sv_status launch(Params &P, hipStream_t stream)
     const int64_t rows_max = (P.mode == MODE_SAMPLE) ? (int64_t)P.B * (2 * kw + 1)
                            : (P.mode == MODE_GREEDY) ? (int64_t)P.B * (kw + 1) : (int64_t)P.B * P.K;
     const size_t lds_a = sizeof(int) * (size_t)(3 * P.B + 1);
-    int64_t grid = (int64_t)cu_count() * row_wgs_per_cu(P.bf16, P.ee, lds_a);
+    const bool dual = P.mode == MODE_CONF && P.conf_temp != nullptr;
+    int64_t grid = (int64_t)cu_count() * row_wgs_per_cu(P.bf16, P.ee, dual, lds_a);
     grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div(rows_max * ceil_div(nv, WVEC), NWAVE)));
     const size_t lds_b = sizeof(Stat) * (size_t)(2 * P.K + 1) + sizeof(float2) * (size_t)P.K;
     const bool sample = P.mode == MODE_SAMPLE;
@@ -3089,11 +3252,12 @@ sv_status launch(Params &P, hipStream_t stream)
     do {                                                                                                    \
         SV_MARK(0);                                                                                         \
         if (P.ee) {                                                                                         \
-            hipLaunchKernelGGL((row_pass_kernel<BF, true>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
+            hipLaunchKernelGGL((row_pass_kernel<BF, true, false>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
             if (split) hipLaunchKernelGGL((finish_kernel<BF, AL, true, true>), grid_b, dim3(WG), lds_b, stream, P); \
             else hipLaunchKernelGGL((finish_kernel<BF, AL, true, false>), grid_b, dim3(WG), lds_b, stream, P); \
         } else {                                                                                            \
-            hipLaunchKernelGGL((row_pass_kernel<BF, false>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
+            if (dual) hipLaunchKernelGGL((row_pass_kernel<BF, false, true>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
+            else hipLaunchKernelGGL((row_pass_kernel<BF, false, false>), dim3((unsigned)grid), dim3(WG), lds_a, stream, P); \
             SV_MARK(1);                                                                                     \
             if (split) hipLaunchKernelGGL((finish_kernel<BF, AL, false, true>), grid_b, dim3(WG), lds_b, stream, P); \
             else hipLaunchKernelGGL((finish_kernel<BF, AL, false, false>), grid_b, dim3(WG), lds_b, stream, P); \
@@ -3557,6 +3721,29 @@ sv_status spec_draft_confidence_stats(const void *draft_logits, sv_dtype dt, con
     Params P = base_params(B, K, V, dt, MODE_CONF, L, workspace);
     P.draft = draft_logits;
     P.max_depth = max_depth;
+    P.conf = conf;
+    P.dstats_out = (Stat *)draft_stats;
+    return launch(P, stream);
+}
+
+sv_status spec_draft_confidence_stats_t(const void *draft_logits, sv_dtype dt, const int32_t *max_depth,
+                                        const float *temperature, int32_t B, int32_t K, int32_t V, float *conf,
+                                        void *draft_stats, void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    sv_status st = check_shape(B, K, V);
+    if (st != SV_OK) return st;
+    if (dt != SV_F32 && dt != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (K == 0) return SV_OK;
+    if (!draft_logits || !draft_stats || !temperature || ((uintptr_t)draft_stats & 15u) != 0)
+        return SV_ERR_INVALID_ARG;
+    if (!aligned16(draft_logits)) return SV_ERR_INVALID_ARG;
+    Layout L;
+    make_layout(B, K, V, L);
+    if ((st = check_ws(workspace, ws_bytes, L)) != SV_OK) return st;
+    Params P = base_params(B, K, V, dt, MODE_CONF, L, workspace);
+    P.draft = draft_logits;
+    P.max_depth = max_depth;
+    P.conf_temp = temperature;
     P.conf = conf;
     P.dstats_out = (Stat *)draft_stats;
     return launch(P, stream);

@@ -333,14 +333,16 @@ sv_status spec_draft_confidence(const void *draft_logits, sv_dtype dt,
                                 void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Draft-row statistics, for reuse by spec_verify_sample_reuse.  Per draft
- * row (b, k): max = the row's largest logit, sum = the sum over the row of
- * 2^((v - max) * c) with c = (float)log2(e) (that is, T = 1), so that
- * softmax(y)_v = 2^((v - max) * c) / sum.  A row the confidence pass did not
- * read (k >= max_depth[b]) or could not use (NaN, +inf, all -inf) gets NaN
- * in both fields.  16 bytes, 16-byte aligned. */
+ * row (b, k) and temperature T: max = the row's largest logit, sum = the sum
+ * over the row of 2^((v - max) * c) with c = (float)(log2(e) / T), so that
+ * softmax(y / T)_v = 2^((v - max) * c) / sum; temp = the bits of the fp32 T
+ * they were taken at (1.0 from spec_draft_confidence_stats; the request's
+ * temperature from spec_draft_confidence_stats_t).  A row the confidence pass
+ * did not read (k >= max_depth[b]) or could not use (NaN, +inf, all -inf)
+ * gets NaN in max and sum.  16 bytes, 16-byte aligned. */
 typedef struct {
     float max;
-    int32_t reserved;
+    int32_t temp;
     double sum;
 } sv_row_stat;
 
@@ -360,16 +362,35 @@ sv_status spec_draft_confidence_stats(const void *draft_logits, sv_dtype dt,
                                       void *draft_stats,
                                       void *workspace, size_t ws_bytes, hipStream_t stream);
 
-/* spec_verify_sample with the draft rows' statistics given: for a request
- * with temperature exactly 1 the draft rows 0..d-1 are not streamed; their
- * (max, sum) come from draft_stats[b, 0..d-1] (as written by
- * spec_draft_confidence_stats on the same draft logits) and the draft logit
- * at each drafted token is read singly.  Requests with another temperature
- * are verified exactly as by spec_verify_sample.  The rule and every output
- * are those of spec_verify_sample; a NaN statistic (a row the confidence
- * pass did not read, depth[b] > its max_depth[b]) makes the request bad
+/* spec_draft_confidence_stats with the statistics of request b's rows taken
+ * at its own temperature: temperature[b] when that is a finite T > 0 (and
+ * not 1), at T = 1 otherwise (T = 0, the greedy rule, reads no draft
+ * statistics).  The confidence stays the T = 1 value D-cut ranks by; a row
+ * at another temperature gets both from one read (two sums, sharing the
+ * row's max).  So a later spec_verify_sample_reuse skips the draft rows of
+ * every sampled request, whatever its temperature.
+ *   temperature  [B] float (device), the verify call's temperatures
+ *   Other arguments as in spec_draft_confidence_stats. */
+sv_status spec_draft_confidence_stats_t(const void *draft_logits, sv_dtype dt,
+                                        const int32_t *max_depth,
+                                        const float *temperature,
+                                        int32_t B, int32_t K, int32_t V, float *conf,
+                                        void *draft_stats,
+                                        void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* spec_verify_sample with the draft rows' statistics given: for a sampled
+ * request whose statistics were taken at its temperature (draft_stats[b, 0]
+ * .temp holds the bits of temperature[b]) the draft rows 0..d-1 are not
+ * streamed; their (max, sum) come from draft_stats[b, 0..d-1] (as written by
+ * spec_draft_confidence_stats or spec_draft_confidence_stats_t on the same
+ * draft logits) and the draft logit at each drafted token is read singly.
+ * Other requests are verified exactly as by spec_verify_sample.  The rule
+ * and every output are those of spec_verify_sample; a NaN statistic (a row
+ * the confidence pass did not read, depth[b] > its max_depth[b]) or a later
+ * row's record taken at another temperature makes the request bad
  * (num_accepted = -1).  The draft row a residual draw needs is still read.
- *   draft_stats  [B, K] sv_row_stat (read: rows 0..d-1 of T = 1 requests)
+ *   draft_stats  [B, K] sv_row_stat (read: the first record of every
+ *                request, rows 0..d-1 of the requests that reuse them)
  *   Other arguments as in spec_verify_sample. */
 sv_status spec_verify_sample_reuse(const void *target_logits, const void *draft_logits,
                                    sv_dtype dt, const int32_t *draft_tokens,

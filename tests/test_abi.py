@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(sv.EXPORTED)
@@ -195,6 +195,14 @@ def test_reuse_entry_points_host_errors():
     assert cs(FAKE, 1, NULL, 4, 3, 1000, FAKE, stats_mis, FAKE, wsb, NULL) == 1
     assert cs(FAKE, 1, NULL, 4, 3, 1000, NULL, stats, FAKE, 16, NULL) == 3
     assert cs(FAKE, 9, NULL, 4, 3, 1000, NULL, stats, FAKE, wsb, NULL) == 1
+    # spec_draft_confidence_stats_t: the temperatures are required too
+    ct = L.spec_draft_confidence_stats_t
+    assert ct(FAKE, 1, NULL, NULL, 4, 3, 1000, FAKE, stats, FAKE, wsb, NULL) == 1
+    assert ct(NULL, 1, NULL, FAKE, 4, 3, 1000, FAKE, stats, FAKE, wsb, NULL) == 1
+    assert ct(FAKE, 1, NULL, FAKE, 4, 3, 1000, FAKE, NULL, FAKE, wsb, NULL) == 1
+    assert ct(FAKE, 1, NULL, FAKE, 4, 3, 1000, FAKE, stats_mis, FAKE, wsb, NULL) == 1
+    assert ct(FAKE, 1, NULL, FAKE, 4, 3, 1000, NULL, stats, FAKE, 16, NULL) == 3
+    assert ct(FAKE, 1, NULL, FAKE, 0, 3, 1000, NULL, stats, FAKE, wsb, NULL) == 1
     # spec_verify_sample_reuse: the statistics are required when K > 0
     def reuse(draft_stats=stats, **kw):
         a = dict(target=FAKE, draft=FAKE, dt=1, tokens=FAKE, depth=NULL, T=FAKE, ua=FAKE, us=FAKE,

@@ -240,7 +240,8 @@ def test_reuse_pipeline_full_size():
     conf_g, st = sv.draft_confidence_stats(dev(w.draft))
     conf_o = oracle.draft_confidence(w.draft)
     assert np.max(np.abs(host(conf_g) - conf_o) / conf_o) < 2e-6
-    mx, sm = (host(t) for t in sv.row_stat_fields(st))
+    mx, sm, tt = (host(t) for t in sv.row_stat_fields(st))
+    assert np.all(tt == 1.0)
     # the statistics are the rows' maxima and softmax normalisers at T = 1
     assert np.array_equal(mx, synth.as_f64(w.draft).max(axis=2).astype(np.float32))
     assert np.max(np.abs(1.0 / sm - conf_o) / conf_o) < 2e-6
