@@ -2151,8 +2151,10 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     const int offs_bad = P.offs ? P.ws.meta[2] : 0;   // the row pass's verdict on packed offsets
     // request b's partials start at slot row b * (2K + 1)
     const int pre = b * (2 * P.K + 1);
-    const int tpr = merge_tpr(2 * P.K + 1, P.cpr_max);
-    const MergePre first = merge_prefetch(P, pre, 2 * P.K + 1, tpr);
+    // rows a request merges: at most K + 1 in greedy calls, 2K + 1 otherwise
+    const int rows_max = P.mode == MODE_GREEDY ? P.K + 1 : 2 * P.K + 1;
+    const int tpr = merge_tpr(rows_max, P.cpr_max);
+    const MergePre first = merge_prefetch(P, pre, rows_max, tpr);
     // the scan's inputs for positions lo..lo+63, issued with the plan's loads
     // so their latencies overlap each other, the table and the merge; every
     // wave loads them (no branch), from a stand-in where an argument is
@@ -2179,7 +2181,11 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
         if (EE && P.ee_last && P.mode == MODE_SAMPLE) units_from_record<BF16, ALIGNED, SPLIT>(P, b, c, tab, sh_parts);
         return;
     }
-    init_exp2_table(tab);
+    // the fp64 exp2 table serves the accept test and the sampler: sampled
+    // requests only (the merge rescales with the fp32 exp2).  Wave 0 fills
+    // it before its share of the merge; the merge's closing barrier publishes
+    // it with the merged rows.
+    if ((q.kind == KIND_SAMPLED || q.kind == KIND_SAMPLED_R) && wave_id() == 0) fill_exp2_table(tab);
 
     const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF || q.kind == KIND_SAMPLED_R ||
                      q.kind == KIND_CONF2;
