@@ -618,15 +618,25 @@ struct ReqPlan {
     ReqBase rb;
 };
 
-// offs_bad: packed layout, the offsets are not a valid CSR array (some
-// request's pair is unusable), which makes every request bad.
+// The per-request arguments a plan reads.  Every load is issued, and
+// unconditionally: an argument the call does not use is read from a valid
+// stand-in address and its value discarded.  (Loads issued under branches
+// were each waited for at the branch's join, one after another.)  Kept
+// apart from the arithmetic so a caller can issue these loads ahead of its
+// others and wait for them alone: waits on vector loads retire in issue
+// order.
+struct PlanArgs {
+    int dv;      // depth (or max_depth) of request b
+    float tv;    // temperature
+    int rtv;     // the first given draft record's temperature bits
+    float ctv;   // confidence call: the statistics temperature
+    int av;      // early exit: still verifying
+    int o0, o1;  // packed layout: the request's offsets
+};
+
 template <bool EE>
-__device__ __forceinline__ ReqPlan plan_request(const Params &P, int b, bool offs_bad)
+__device__ __forceinline__ PlanArgs plan_loads(const Params &P, int b)
 {
-    // Every load first and unconditionally: an argument the call does not
-    // use is read from a valid stand-in address and its value discarded.
-    // (Loads issued under branches were each waited for at the branch's
-    // join, one after another.)
     const int32_t *stand_in = &k_stand_in;
     const int32_t *dp = P.mode == MODE_CONF ? (P.max_depth ? P.max_depth + b : stand_in)
                                             : (P.depth ? P.depth + b : stand_in);
@@ -639,12 +649,31 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b, bool off
     const int32_t *rtp = (P.mode == MODE_SAMPLE && P.dstats_in && P.K > 0)
                              ? (const int32_t *)(P.dstats_in + (int64_t)b * P.K) + 1 : stand_in;
     const float *ctp = (P.mode == MODE_CONF && P.conf_temp) ? P.conf_temp + b : (const float *)stand_in;
-    int dv = *dp;
-    const float tv = *tp;
-    const int rtv = *rtp;
-    const float ctv = *ctp;
-    const int av = *ap;
-    const int o0 = *o0p, o1 = *o1p;
+    // through the scalar cache where b is wave-uniform (the finish kernel):
+    // counted apart from the vector loads issued after these
+    typedef const __attribute__((address_space(4))) int32_t *CI;
+    PlanArgs a;
+    a.dv = *(CI)dp;
+    a.tv = __int_as_float(*(CI)tp);
+    a.rtv = *(CI)rtp;
+    a.ctv = __int_as_float(*(CI)ctp);
+    a.av = *(CI)ap;
+    a.o0 = *(CI)o0p;
+    a.o1 = *(CI)o1p;
+    return a;
+}
+
+// offs_bad: packed layout, the offsets are not a valid CSR array (some
+// request's pair is unusable), which makes every request bad.
+template <bool EE>
+__device__ __forceinline__ ReqPlan plan_request(const Params &P, int b, bool offs_bad, const PlanArgs &a)
+{
+    int dv = a.dv;
+    const float tv = a.tv;
+    const int rtv = a.rtv;
+    const float ctv = a.ctv;
+    const int av = a.av;
+    const int o0 = a.o0, o1 = a.o1;
     const bool have_depth = P.offs || (P.mode == MODE_CONF ? P.max_depth != nullptr : P.depth != nullptr);
 
     ReqPlan q;
@@ -719,7 +748,7 @@ __device__ int make_plan(const Params &P, Plan pl, int *scan_tmp)
     for (int j = 0; j < per; ++j) {
         const int b = b0 + j;
         if (b >= B) break;
-        const ReqPlan q = plan_request<EE>(P, b, false);
+        const ReqPlan q = plan_request<EE>(P, b, false, plan_loads<EE>(P, b));
         pl.info[b] = q.d | (q.kind << 16);
         pl.T[b] = q.T;
         pl.row_off[b] = q.rows;   // count for now
@@ -2145,8 +2174,11 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     // request waits on; fp64 unit work of other workgroups on the same SIMD
     // would otherwise delay it.  Raised issue priority until the units start.
     __builtin_amdgcn_s_setprio(3);
-    // the request's plan and the row pass's chunking are read before the
-    // table is built, so their loads overlap its arithmetic
+    // The request's plan arguments are the first loads issued, so the wait
+    // for them covers nothing else; the row pass's chunking, the merge's
+    // first partials and the scan's inputs are issued after them and return
+    // while the plan and the table are computed.
+    const PlanArgs pa = plan_loads<EE>(P, b);
     const int cpr = P.ws.meta[0];
     const int offs_bad = P.offs ? P.ws.meta[2] : 0;   // the row pass's verdict on packed offsets
     // request b's partials start at slot row b * (2K + 1)
@@ -2170,7 +2202,12 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
     int x0 = *tokp;
     float ua0 = *uap;
     const float us0 = *usp;
-    const ReqPlan q = plan_request<EE>(P, b, offs_bad != 0);
+    // the fp64 exp2 table serves the accept test and the sampler of sampled
+    // calls (the merge rescales with the fp32 exp2).  Wave 0 fills it while
+    // the loads above are in flight; the merge's closing barrier publishes
+    // it with the merged rows.
+    if (P.mode == MODE_SAMPLE && wave_id() == 0) fill_exp2_table(tab);
+    const ReqPlan q = plan_request<EE>(P, b, offs_bad != 0, pa);
     if (P.offs && q.d > 0) {
         const int64_t i = q.rb.db + min(lo + lane_id(), lo + q.d - 1);
         x0 = P.tokens[i];
@@ -2181,12 +2218,6 @@ __global__ __launch_bounds__(WG) void finish_kernel(Params P)
         if (EE && P.ee_last && P.mode == MODE_SAMPLE) units_from_record<BF16, ALIGNED, SPLIT>(P, b, c, tab, sh_parts);
         return;
     }
-    // the fp64 exp2 table serves the accept test and the sampler: sampled
-    // requests only (the merge rescales with the fp32 exp2).  Wave 0 fills
-    // it before its share of the merge; the merge's closing barrier publishes
-    // it with the merged rows.
-    if ((q.kind == KIND_SAMPLED || q.kind == KIND_SAMPLED_R) && wave_id() == 0) fill_exp2_table(tab);
-
     const bool lse = q.kind == KIND_SAMPLED || q.kind == KIND_CONF || q.kind == KIND_SAMPLED_R ||
                      q.kind == KIND_CONF2;
     if (q.kind == KIND_SAMPLED_R) {
