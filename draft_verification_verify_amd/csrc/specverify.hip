@@ -2502,13 +2502,17 @@ __global__ __launch_bounds__(WG) void draw_kernel(Params P)
     const int b = blockIdx.x, w = wave_id(), lane = lane_id();
     // the first 64 unit sums and the draw uniform are loaded with the record,
     // so the three latencies overlap instead of following one another
-    // (clamped index, no branch: lanes past the units are never used)
+    // (clamped index, no branch: lanes past the units are never used).  The
+    // compiler-only barrier keeps the first two above the record's test (the
+    // compiler would otherwise sink them below it, into a second round trip);
+    // the exp2 table is built while all three are in flight.
     const ChunkPart c0 = P.ws.cp[(int64_t)b * P.cs + min(lane, P.cs - 1)];
     const float u0 = P.u_sample[b];
     const DrawRec rec = P.ws.rec[b];
-    if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
+    __asm__ volatile("" ::: "memory");
     double *tab = tabs[w];
     init_exp2_table_wave(tab);
+    if (rec.state != SREQ_RESID && rec.state != SREQ_BONUS) return;
     const bool resid = rec.state == SREQ_RESID;
     const ReqDesc desc = {rec.state, rec.n, -1, rec.T};
     DrawRows<BF16> dr = draw_rows<BF16>(P, rec.tb, rec.db, desc, rec.mz, rec.my);
