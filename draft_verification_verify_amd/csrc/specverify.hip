@@ -729,11 +729,38 @@ __device__ __forceinline__ ReqPlan plan_request(const Params &P, int b, bool off
     return q;
 }
 
+// Exponent scale of a row's log-sum-exp statistics.  Every exponent of the
+// row statistics and of the accept test is (v - M) * c with c = c32 * 2^sh:
+// c32 = fl(log2(e)/T), which differs from log2(e)/T by at most 6e-8
+// relative, and sh = 0; only when log2(e)/T exceeds 2^100 (T below about
+// 1.1e-30, down to the smallest positive fp32 value) is c32 the rounded
+// quotient times 2^-64 and sh = 64, so that c32 stays a finite fp32 number
+// for every finite T > 0.
+struct LseScale {
+    float c32;
+    int sh;   // 0 or 64
+};
+
+constexpr double SCALE_SHIFT_AT = 0x1p100;
+
+__device__ __forceinline__ LseScale scale_of(int kind, float T)
+{
+    const double c = LOG2E / (double)((kind == KIND_CONF || kind == KIND_CONF2) ? 1.0f : T);
+    LseScale sc;
+    sc.sh = c > SCALE_SHIFT_AT ? 64 : 0;
+    sc.c32 = (float)(sc.sh ? c * 0x1p-64 : c);
+    return sc;
+}
+
 struct Plan {
     int *row_off;   // [B + 1] in LDS
     int *info;      // [B] in LDS: d | kind << 16
-    float *T;       // [B] in LDS
+    float *c32;     // [B] in LDS: the request's own-temperature scale (scale_of at its T)
 };
+
+// Plan info word: d in bits 0-15, the kind in bits 16-23, and PLAN_SH when
+// the request's own-temperature scale carries the 2^64 shift.
+constexpr int PLAN_SH = 1 << 24;
 
 // Whole-workgroup plan: row_off = exclusive prefix of per-request rows.
 // Returns 1 when the packed layout's offsets are not a valid CSR array
@@ -749,8 +776,11 @@ __device__ int make_plan(const Params &P, Plan pl, int *scan_tmp)
         const int b = b0 + j;
         if (b >= B) break;
         const ReqPlan q = plan_request<EE>(P, b, false, plan_loads<EE>(P, b));
-        pl.info[b] = q.d | (q.kind << 16);
-        pl.T[b] = q.T;
+        // the scale's division once per request here, not once per task;
+        // meaningless (unused) for requests without a temperature
+        const LseScale sc = scale_of(KIND_SAMPLED, q.T);
+        pl.info[b] = q.d | (q.kind << 16) | (sc.sh ? PLAN_SH : 0);
+        pl.c32[b] = sc.c32;
         pl.row_off[b] = q.rows;   // count for now
         local += q.rows;
         bad_pair |= !q.pair_ok;
@@ -785,17 +815,28 @@ __device__ int make_plan(const Params &P, Plan pl, int *scan_tmp)
     return offs_bad;
 }
 
-// Request containing global active row r (row_off is non-decreasing).  r is
-// wave-uniform; the LDS values are made scalar so the search runs on the
-// scalar unit.
+// Request containing global active row r, for a wave-uniform r: the b with
+// row_off[b] <= r < row_off[b + 1] (row_off non-decreasing, row_off[0] = 0,
+// so an empty request is never the answer).  That b is the number of
+// j in [1, B - 1] with row_off[j] <= r, and those j form a prefix, so the
+// wave counts them with ballots instead of a serial binary search: the lanes
+// first test every S-th entry (S = ceil((B - 1) / 64)), which bounds b to S
+// consecutive values, then test those.  One LDS read per lane for B <= 65,
+// two up to B = 4097, whatever the batch.
 __device__ __forceinline__ int find_request(const int *row_off, int B, int r)
 {
-    int lo = 0, hi = B;   // row_off[lo] <= r < row_off[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (__builtin_amdgcn_readfirstlane(row_off[mid]) <= r) lo = mid; else hi = mid;
-    }
-    return lo;
+    const int n = B - 1;
+    if (n <= 0) return 0;
+    const int lane = lane_id();
+    const int S = (n + 63) >> 6;
+    const int j1 = 1 + lane * S;
+    const bool t1 = j1 <= n && row_off[j1] <= r;
+    const int c1 = __builtin_popcountll(__ballot(t1));
+    if (S == 1 || c1 == 0) return c1;
+    const int base = 1 + (c1 - 1) * S;   // row_off[base] <= r, so b >= base
+    const int j2 = base + 1 + lane;
+    const bool t2 = lane < S - 1 && j2 <= n && row_off[j2] <= r;
+    return base + __builtin_popcountll(__ballot(t2));
 }
 
 // Chunking of the row pass: cpr chunks per row of nb batches each, with cpr
@@ -912,29 +953,6 @@ __device__ __forceinline__ void argmax_batch(const RowView<BF16> &rv, int vbeg, 
             st.bidx = rv.elem(vi, found);
         }
     }
-}
-
-// Exponent scale of a row's log-sum-exp statistics.  Every exponent of the
-// row statistics and of the accept test is (v - M) * c with c = c32 * 2^sh:
-// c32 = fl(log2(e)/T), which differs from log2(e)/T by at most 6e-8
-// relative, and sh = 0; only when log2(e)/T exceeds 2^100 (T below about
-// 1.1e-30, down to the smallest positive fp32 value) is c32 the rounded
-// quotient times 2^-64 and sh = 64, so that c32 stays a finite fp32 number
-// for every finite T > 0.
-struct LseScale {
-    float c32;
-    int sh;   // 0 or 64
-};
-
-constexpr double SCALE_SHIFT_AT = 0x1p100;
-
-__device__ __forceinline__ LseScale scale_of(int kind, float T)
-{
-    const double c = LOG2E / (double)((kind == KIND_CONF || kind == KIND_CONF2) ? 1.0f : T);
-    LseScale sc;
-    sc.sh = c > SCALE_SHIFT_AT ? 64 : 0;
-    sc.c32 = (float)(sc.sh ? c * 0x1p-64 : c);
-    return sc;
 }
 
 // The scale as a double, exactly c32 * 2^sh.
@@ -1209,7 +1227,9 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     const int b = find_request(pl.row_off, P.B, r);
     const int local = r - __builtin_amdgcn_readfirstlane(pl.row_off[b]);
     const int info = __builtin_amdgcn_readfirstlane(pl.info[b]);
-    const int d = info & 0xffff, kind = info >> 16;
+    const float cT = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.c32[b])));
+    const int d = info & 0xffff, kind = (info >> 16) & 0xff;
+    const int shT = (info & PLAN_SH) ? 64 : 0;
     k.slot = b * (2 * P.K + 1) + local;
     bool is_draft;
     int kk;
@@ -1222,15 +1242,15 @@ __device__ __forceinline__ Task<BF16> make_task(const Params &P, const Plan &pl,
     k.sc2 = k.sc;
     k.slot2 = k.slot + d;
     if (kind == KIND_CONF2) {
-        k.sc2 = scale_of(KIND_SAMPLED, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b]))));
-        k.sc2.c32 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(k.sc2.c32)));
-        k.sc2.sh = __builtin_amdgcn_readfirstlane(k.sc2.sh);
+        k.sc2.c32 = cT;
+        k.sc2.sh = shT;
     }
     if constexpr (EE) kk += P.win_lo;   // the window's first position
     if (lse) {
-        k.sc = scale_of(kind, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(pl.T[b]))));
-        k.sc.c32 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(k.sc.c32)));
-        k.sc.sh = __builtin_amdgcn_readfirstlane(k.sc.sh);
+        // confidence statistics are at T = 1 (scale_of's rule for those kinds)
+        const bool conf = kind == KIND_CONF || kind == KIND_CONF2;
+        k.sc.c32 = conf ? (float)LOG2E : cT;
+        k.sc.sh = conf ? 0 : shT;
     } else {
         k.sc.c32 = 0.0f;
         k.sc.sh = 0;
@@ -1354,7 +1374,7 @@ void row_pass_kernel(Params P)
     Plan pl;
     pl.row_off = plan_smem;
     pl.info = plan_smem + P.B + 1;
-    pl.T = (float *)(plan_smem + 2 * P.B + 1);
+    pl.c32 = (float *)(plan_smem + 2 * P.B + 1);
     const int offs_bad = make_plan<EE>(P, pl, scan_tmp);
 
     const int R = __builtin_amdgcn_readfirstlane(pl.row_off[P.B]);
