@@ -295,6 +295,26 @@ def test_reuse_depth_beyond_statistics_is_bad():
     tal.assert_ok("reuse partial")
 
 
+@pytest.mark.parametrize("B", [65, 66, 129, 300, 4096])
+def test_ragged_large_batches_with_empty_requests(B):
+    # Each row-pass task finds its request among the plan's row offsets: one
+    # ballot round over 64 offsets up to B = 65, two beyond.  Requests with no
+    # rows (depth 0 on greedy rows aside, bad temperatures, NaN) leave runs of
+    # equal offsets that must never be chosen.
+    note(f"ragged batch B={B}: depths in [0, K] with many zeros, bad temperatures, greedy and sampled")
+    K, V = 4, 37
+    g = np.random.default_rng(B)
+    temps = g.choice(np.array([0.0, 0.7, 1.0, 1.0, np.nan], np.float32), B).astype(np.float32)
+    w = synth.random_case(B + 17, B=B, K=K, V=V, dtype="f32" if B % 2 else "bf16", temperature=temps, sigma=0.6)
+    depth = g.integers(0, K + 1, B).astype(np.int32)
+    depth[g.random(B) < 0.3] = 0
+    depth[g.random(B) < 0.05] = -1   # bad depth: no rows either
+    out, n, p, q = run_sample(w, depth)
+    compare_sample(w, out, n, p, q, depth).assert_ok(f"ragged B={B}")
+    og, ng = run_greedy(w, depth)
+    assert compare_greedy(w, og, ng, depth).size == 0
+
+
 def test_determinism_and_workspace_reuse():
     note("determinism: repeated calls, shared workspace across shapes")
     import draft_verification_verify_amd as sv
