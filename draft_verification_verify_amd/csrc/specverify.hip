@@ -840,18 +840,25 @@ __device__ __forceinline__ int find_request(const int *row_off, int B, int r)
 }
 
 // Chunking of the row pass: cpr chunks per row of nb batches each, with cpr
-// chosen so that every wave gets about eight tasks (bounded tail imbalance)
-// but a task covers at least two batches where the row has them: a wave
-// sets up its next task while its other buffer's batch is in flight, and a
-// run of one-batch tasks leaves that set-up exposed between loads (passes
-// over a few hundred rows ran about 12 % slower on MI355X).
+// chosen so that every wave gets about `tpw` tasks, but a task covers at
+// least two batches where the row has them: a wave sets up its next task
+// while its other buffer's batch is in flight, and a run of one-batch tasks
+// leaves that set-up exposed between loads (passes over a few hundred rows
+// ran about 12 % slower on MI355X).  Calls with log-sum-exp rows take about
+// twelve tasks per wave: finer tasks round the per-slot task counts more
+// evenly, and the dense B=64, K=16, V=128000 sampled batch ran 1.3 us faster
+// at 21 chunks of three batches than at 16 of four.  Greedy calls take about
+// eight: their rows cost less per batch, so a task's set-up weighs more, and
+// the same batch ran about 0.4 us slower at 32 chunks of two batches than at
+// 21 of three (measured on MI355X).
 // A positive `forced` (SPECVERIFY_CHUNK, a test and tuning override) asks for
 // that many chunks per row instead, within [1, min(batches, 256)].
-__device__ __forceinline__ void row_chunking(int R, int V, bool bf16, int64_t nwaves, int forced, int &cpr, int &nb)
+__device__ __forceinline__ void row_chunking(int R, int V, bool bf16, int64_t nwaves, int tpw, int forced, int &cpr,
+                                             int &nb)
 {
     const int64_t nv = nvec_max(V, bf16 ? 8 : 4);
     const int nbt = (int)ceil_div(nv, WVEC);
-    const int64_t want = ceil_div(8 * nwaves, (int64_t)(R > 0 ? R : 1));
+    const int64_t want = ceil_div((int64_t)tpw * nwaves, (int64_t)(R > 0 ? R : 1));
     cpr = (int)std::min<int64_t>(std::max<int64_t>(want, 1),
                                  std::min<int64_t>(std::min(nbt, CPR_CAP), ceil_div(nbt, 2)));
     if (forced > 0) cpr = std::min(forced, std::min(nbt, CPR_CAP));
@@ -1380,7 +1387,7 @@ void row_pass_kernel(Params P)
     const int R = __builtin_amdgcn_readfirstlane(pl.row_off[P.B]);
     const uint32_t nwaves = gridDim.x * NWAVE;
     int cpr, nb;
-    row_chunking(R, P.V, BF16, nwaves, P.chunks, cpr, nb);
+    row_chunking(R, P.V, BF16, nwaves, P.mode == MODE_GREEDY ? 8 : 12, P.chunks, cpr, nb);
     // The divisions above run on the vector unit; their (uniform) results
     // are moved to scalar registers so everything derived stays scalar.
     cpr = __builtin_amdgcn_readfirstlane(cpr);
@@ -1752,7 +1759,7 @@ __device__ __forceinline__ Stat merge2(Stat a, Stat b, bool lse, double cs, cons
     return a;
 }
 
-constexpr int MERGE_LOADS = 4;   // row-pass partials loaded at once per merging thread
+constexpr int MERGE_LOADS = 8;   // row-pass partials loaded at once per merging thread
 
 // Threads per row of the merge: the largest power of two up to 64 (and up
 // to the workspace's column count) with a group of rows_max rows fitting
