@@ -25,22 +25,23 @@
 //     batches and across consecutive tasks, and reduced to (max, lowest
 //     argmax) for greedy rows or (max, sum of exp) for sampled rows.  Each
 //     task stores its partial with plain stores: no atomics, no waits.
-//  B. finish_kernel -- one workgroup per (request, sampler chunk).  It
-//     gathers the request's chunk partials into LDS, merges them per row, and
-//     runs the accept test and first-rejection scan (every chunk's workgroup
-//     does this cheap step itself, so none waits on another).  For a request
-//     that draws a token it then reduces its chunk of the row pair in fp64:
-//     the softmax normalisers.
-//  C. draw_kernel -- per (request, chunk): fp64 residual max(0, p - q) (or p
-//     for the bonus token) chunk totals; the last chunk of a request to
-//     finish locates u*R among the totals and scans that chunk.
-// The kernel boundaries order all data between phases.  Inside B and C the
-// last workgroup of a request is found with a device-scope counter and reads
-// the others' partials back with device-scope loads (no cache flushes).
+//  B. finish_kernel -- workgroups (c, b) for request b.  Every workgroup of
+//     a request merges the request's chunk partials per row and runs the
+//     accept test and first-rejection scan itself (a short chain, so none
+//     waits on another); workgroup 0 writes the outputs and a draw record.
+//     For a request that draws a token, each wave then sums one 2048-logit
+//     unit of the drawn row pair in fp64: the row normalisers and the
+//     unit's residual max(0, p - q) mass (or, for a bonus draw, the unit's
+//     maximum and sum of p).
+//  C. draw_kernel -- one workgroup per drawing request: combines the unit
+//     sums, locates u*R among the unit masses and rescans that unit in
+//     token order.
+// The kernel boundaries order all data between phases: no kernel of a call
+// uses atomics, fences or flags to hand data to another workgroup.
 // dcut_allocate is one workgroup: fp32 running products and an LDS radix
 // select.  Nothing here is a dense contraction, so there is no MFMA: A is
-// bound by HBM bandwidth, B and C by fp64 arithmetic on one row pair per
-// request.
+// bound by HBM bandwidth, B by fp64 arithmetic on one row pair per request,
+// C by latency.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
