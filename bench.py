@@ -60,11 +60,11 @@ CALIB_KERNEL = "neg_kernel"
 # WRITE_SIZE), each scaled by what the same counter reads for the calibration
 # copy in that run.  It describes the kernel source with this SHA-256 only;
 # for any other source it is reported as null.
-ROW_PASS_TRAFFIC = {"source_sha256": "3cd95f8e7624a134bc3c67b1f412cb61e88197e0dd66cbd15969dcda66b75a3e",
-                    "fetch_bytes": 525453214, "write_bytes": 660509,
+ROW_PASS_TRAFFIC = {"source_sha256": "c301634da640cb2650df714ccfc883a87e560943efe3e7042756aa82fa0a3537",
+                    "fetch_bytes": 525406560, "write_bytes": 897576,
                     # SQ counters of the same source (one --pmc run of eight SQ counters):
                     # VALU instructions and busy cycles per dispatch, summed over the device
-                    "sq_insts_valu": 31325955, "sq_busy_cycles": 5735244}
+                    "sq_insts_valu": 32479039, "sq_busy_cycles": 5713611}
 
 
 # Untimed steps before the first timed pass (less any --warmup steps).
