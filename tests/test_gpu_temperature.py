@@ -5,8 +5,9 @@ The contract accepts every finite T > 0.  The row statistics form each
 exponent as (v - M) / T on a scale of about log2(e)/T, so small T and large
 |M| stress the same arithmetic: the rounding offset of M * log2(e)/T grows
 with both.  These cases check the one-pass, early-exit and draft-statistics
-reuse calls at T from 1e-45 (an fp32 denormal) to 3.4e38 on bf16 V=128000
-and fp32 V=152064 rows, and rows shifted by a constant of 1e5 to 1e6 (the
+reuse calls (statistics at T = 1 and at each request's temperature) at T
+from 1e-45 (an fp32 denormal) to 3.4e38 on bf16 V=128000 and fp32 V=152064
+rows, and rows shifted by a constant of 1e5 to 1e6 (the
 softmax is shift invariant; the stored logits are rounded after the shift,
 and the oracle sees the same bytes)."""
 import sys
@@ -80,11 +81,12 @@ def test_early_exit_temperature_sweep(dtype, V):
     compare_early_exit(w, out, n, p, q).assert_ok(f"early exit sweep {dtype}")
 
 
-def test_reuse_temperature_sweep():
-    note("draft-statistics reuse with T from 1e-45 to 3.4e38 (only T = 1 requests reuse) bf16 V=128000")
-    w = sweep_case("bf16", 128000, 300, temps=SWEEP + [1.0])
+@pytest.mark.parametrize("dtype,V", [("bf16", 128000), ("f32", 152064)])
+def test_reuse_temperature_sweep(dtype, V):
+    note(f"draft-statistics reuse with T from 1e-45 to 3.4e38 (only T = 1 requests reuse) {dtype} V={V}")
+    w = sweep_case(dtype, V, 300, temps=SWEEP + [1.0])
     out, n, p, q = run_sample_reuse(w)
-    compare_sample(w, out, n, p, q).assert_ok("reuse sweep")
+    compare_sample(w, out, n, p, q).assert_ok(f"reuse sweep {dtype}")
 
 
 @pytest.mark.parametrize("shift", [1e5, 1e6, -1e6])
@@ -110,3 +112,18 @@ def test_confidence_shifted_rows_fp32(shift):
     conf_g = host(sv.draft_confidence(dev(w.draft)))
     conf_o = oracle.draft_confidence(w.draft)
     assert np.max(np.abs(conf_g - conf_o) / conf_o) < 2e-6
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 128000), ("f32", 152064)])
+def test_reuse_any_temperature_sweep(dtype, V):
+    note(f"draft-statistics reuse taken at each request's temperature, T from 1e-45 to 3.4e38, {dtype} V={V}")
+    import draft_verification_verify_amd as sv
+    w = sweep_case(dtype, V, 310, temps=SWEEP + [1.0])
+    T = dev(w.temperature)
+    _, st = sv.draft_confidence_stats(dev(w.draft), None, temperature=T, want_conf=False)
+    out, n, p, q = sv.verify_sample_reuse(dev(w.target), dev(w.draft), dev(w.tokens), T, dev(w.u_accept),
+                                          dev(w.u_sample), st)
+    torch.cuda.synchronize()
+    out, n, p, q = host(out), host(n), host(p), host(q)
+    compare_sample(w, out, n, p, q).assert_ok(f"reuse at each temperature {dtype}")
+    assert np.all(n >= 0), n
